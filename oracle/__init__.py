@@ -1,0 +1,124 @@
+"""CPU oracle for the Mamba-3 SSM recurrence -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, `__graft_entry__.smoke()` and the benchmark's `cpu_baseline` leg
+may import this package.  It shares no code with the HIP library.
+
+`scan` wraps the float64 C library (`m3ref.c`: the plain sequential recurrence
+in the physical frame).  `matrix_form` holds two independent NumPy derivations
+(the decay x two-band matrix form with data-dependent RoPE, and the rotating-
+frame loop) that pin the C loop.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("M3REF_LIB") or os.path.join(_HERE, "libm3ref.so")
+_lib = None
+
+ERRORS = {
+    1: "bad dimensions",
+    2: "non-finite input",
+    3: "dt < 0",
+    4: "A > 0",
+    5: "lambda outside [0, 1]",
+    6: "dstate must be even when angles are given",
+    7: "missing required input",
+    8: "out of memory",
+}
+
+
+class OracleError(ValueError):
+    pass
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.m3ref_scan.restype = ctypes.c_int
+    lib.m3ref_scan.argtypes = [ctypes.c_int] * 6 + [dp] * 6 + [dp] * 4 + [dp, dp, ctypes.c_int]
+    lib.m3ref_validate.restype = ctypes.c_int
+    lib.m3ref_validate.argtypes = [ctypes.c_int] * 6 + [dp] * 10
+    lib.m3ref_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _as64(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return int(_load().m3ref_max_threads())
+
+
+def scan(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
+         nthreads: int = 0):
+    """Runs the float64 recurrence.
+
+    Shapes: x [b,L,H,R,P], B/C [b,L,H,R,N], dt/lam [b,L,H], A [H],
+    theta [b,L,H,N/2] or None, h0 [b,H,N,P] or None, B_prev [b,H,R,N] and
+    x_prev [b,H,R,P] or both None.  Returns (y [b,L,H,R,P], h_out [b,H,N,P]) as
+    float64 arrays.  Raises OracleError on a violated precondition.
+    """
+    x, B, C, dt, A, lam = map(_as64, (x, B, C, dt, A, lam))
+    theta, h0, B_prev, x_prev = map(_as64, (theta, h0, B_prev, x_prev))
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    if B.shape != (b, L, H, R, N) or C.shape != B.shape:
+        raise OracleError("B/C shape mismatch")
+    if dt.shape != (b, L, H) or lam.shape != (b, L, H) or A.shape != (H,):
+        raise OracleError("dt/lam/A shape mismatch")
+    if theta is not None and theta.shape != (b, L, H, N // 2):
+        raise OracleError("theta shape mismatch")
+    if h0 is not None and h0.shape != (b, H, N, P):
+        raise OracleError("h0 shape mismatch")
+    if (B_prev is None) != (x_prev is None):
+        raise OracleError("B_prev and x_prev must be given together")
+    if B_prev is not None and (B_prev.shape != (b, H, R, N) or x_prev.shape != (b, H, R, P)):
+        raise OracleError("B_prev/x_prev shape mismatch")
+    y = np.zeros((b, L, H, R, P), dtype=np.float64)
+    h_out = np.zeros((b, H, N, P), dtype=np.float64)
+    rc = _load().m3ref_scan(b, L, H, P, N, R, _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
+                            _ptr(lam), _ptr(theta), _ptr(h0), _ptr(B_prev), _ptr(x_prev),
+                            _ptr(y), _ptr(h_out), int(nthreads))
+    if rc:
+        raise OracleError(ERRORS.get(rc, f"error {rc}"))
+    return y, h_out
+
+
+def decode_steps(h0, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None,
+                 nthreads: int = 0):
+    """Successive single-token steps: x [S,b,H,R,P] etc. (step axis first).
+
+    The same recurrence as `scan` with the steps as the time axis.  Returns
+    (y [S,b,H,R,P], h_final [b,H,N,P]).
+    """
+    def tok_major(a):
+        if a is None:
+            return None
+        a = _as64(a)
+        return np.ascontiguousarray(np.moveaxis(a, 0, 1))  # [b,S,H,...]
+    y, h = scan(tok_major(x), tok_major(B), tok_major(C), tok_major(dt), A, tok_major(lam),
+                tok_major(theta), h0, B_prev, x_prev, nthreads=nthreads)
+    return np.ascontiguousarray(np.moveaxis(y, 1, 0)), h
