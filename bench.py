@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X Mamba-3 recurrence: prefill tokens/s/layer and decode
+state-updates/s, with roofline fractions and the CPU oracle timed alongside.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload siso|mimo|long|decode]
+
+One "step" is one call of the hot path over one batch of synthetic input: a
+whole-layer prefill (all heads) for the prefill workloads, or one single-token
+decode step over all (sequence, head) pairs for the decode workload.  Inputs are
+generated on the device from a fixed seed and are resident in HBM before timing.
+Prints ONE JSON line.  The headline `value` is the requested workload (default:
+SISO prefill at the 1.5B-layer shape); the MIMO prefill and the MIMO decode are
+measured in the same run and reported under "secondary".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+import state_space_sequence_02_amd as m3
+from state_space_sequence_02_amd import inputs
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+METRIC = "prefill tokens/s/layer + decode state-updates/s; % of HBM / MFMA roofline"
+
+
+def esize(w):
+    return 2 if w.dtype == "bf16" else 4
+
+
+def prefill_bytes_per_token_head(w) -> int:
+    """Algorithmic bytes: every input read once, y written once."""
+    es, R, N, P = esize(w), w.rank, w.dstate, w.headdim
+    return R * P * es + 2 * R * N * es + 8 + (N // 2) * 4 * (1 if w.rotation else 0) + R * P * es
+
+
+def prefill_flops_per_token_head(w, q) -> float:
+    """Algorithmic flops of the chunked form with q tokens/chunk (causal blocks only)."""
+    R, N, P = w.rank, w.dstate, w.headdim
+    return (q + 1) * R * R * (N + P) + 4 * N * P * R
+
+
+def decode_bytes_per_update(w) -> int:
+    es, R, N, P = esize(w), w.rank, w.dstate, w.headdim
+    return 2 * N * P * 4 + R * P * es + 2 * R * N * es + R * N * es + R * P * es + 8 + (N // 2) * 4 + R * P * es
+
+
+def table2_intensity(n, p, r):
+    """The paper's 2-byte decode arithmetic-intensity model (Table 2)."""
+    return (4 * n * p * r + n * p - p * r) / (2 * (1 + 2 * n * r + p * r + n * p))
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self):
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.s.record(torch.cuda.current_stream())
+
+    def stop(self) -> float:
+        self.e.record(torch.cuda.current_stream())
+        self.e.synchronize()
+        return self.s.elapsed_time(self.e)
+
+
+def bench_prefill(w, steps, warmup, chunk=None, nsets=2):
+    dev = torch.device("cuda")
+    sets = [inputs.make_prefill_inputs(w, seed=s, device=dev) for s in range(nsets)]
+    q = chunk if chunk is not None else w.chunk
+    dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, q, dcode)
+    ws = torch.empty(m3.prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    q_used = m3.prefill_chunk_used(shape)
+    ys = [torch.empty_like(s["x"]) for s in sets]
+    hs = [torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+          for _ in sets]
+
+    def step(i):
+        d = sets[i % nsets]
+        m3.scan_prefill(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"],
+                        y=ys[i % nsets], h_out=hs[i % nsets], chunk=q, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t = Timer()
+    t.start()
+    for i in range(steps):
+        step(i)
+    ms = t.stop() / steps
+    torch.cuda.synchronize()
+    tok = w.batch * w.seqlen
+    bpt = prefill_bytes_per_token_head(w)
+    nbytes = tok * w.nheads * bpt + w.batch * w.nheads * w.dstate * w.headdim * 4
+    flops = tok * w.nheads * prefill_flops_per_token_head(w, q_used)
+    return dict(ms=ms, tokens_per_s=tok / (ms * 1e-3), chunk=q_used, bytes=nbytes, flops=flops,
+                gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12)
+
+
+def bench_decode(w, steps, warmup, nstate=3):
+    dev = torch.device("cuda")
+    S = w.steps
+    d = inputs.make_decode_inputs(w, seed=0, device=dev)
+    # >= 3 state buffers (384 MiB at the 128-seq shape) so a step cannot be served
+    # from the 256 MB last-level cache left warm by the previous step
+    hs = [torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+          for _ in range(nstate)]
+    y = torch.empty_like(d["x"][0])
+
+    def step(i):
+        s = i % S
+        kw = dict(B_prev=d["B"][s - 1], x_prev=d["x"][s - 1]) if s else {}
+        m3.decode_step(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
+                       d["lam"][s], d["theta"][s], y=y, **kw)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t = Timer()
+    t.start()
+    for i in range(steps):
+        step(i)
+    ms = t.stop() / steps
+    upd = w.batch * w.nheads
+    nbytes = upd * decode_bytes_per_update(w)
+    return dict(ms=ms, updates_per_s=upd / (ms * 1e-3), tokens_per_s=w.batch / (ms * 1e-3),
+                bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The float64 CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    nthreads = oracle.max_threads()
+    if w.steps:   # decode: a subset of (sequence, head) pairs over all steps
+        d = inputs.make_decode_inputs(w, seed=0, device="cpu", steps=16)
+        def run(npairs):
+            seqs = list(range(min(npairs, w.batch)))
+            sub = {k: (v[:, seqs] if (v is not None and k != "A") else v) for k, v in d.items()}
+            t0 = time.perf_counter()
+            oracle.decode_steps(np.zeros((len(seqs), w.nheads, w.dstate, w.headdim)), sub["x"], sub["B"],
+                                sub["C"], sub["dt"], sub["A"], sub["lam"], sub["theta"], nthreads=nthreads)
+            return time.perf_counter() - t0, len(seqs) * w.nheads * 16
+        dt1, u1 = run(1)
+        n = max(1, min(w.batch, int(target_s / max(dt1, 1e-3))))
+        el, upd = run(n)
+        return dict(value=upd / el, unit="state-updates/s", cores=nthreads, kind="oracle",
+                    sample=f"{n} sequences x {w.nheads} heads x 16 steps of the decode workload")
+    d = inputs.make_prefill_inputs(w, seed=0, device="cpu", batch=1)
+    def run(nheads):
+        heads = list(range(nheads))
+        o = {k: (None if v is None else (v[heads] if k == "A" else v[:, :, heads]))
+             for k, v in d.items()}
+        t0 = time.perf_counter()
+        oracle.scan(**o, nthreads=nthreads)
+        return time.perf_counter() - t0
+    nh0 = min(nthreads, w.nheads)
+    t1 = run(nh0)
+    nh = max(nh0, min(w.nheads, int(nh0 * target_s / max(t1, 1e-3))))
+    el = run(nh)
+    tokens_per_s = (w.seqlen * nh / w.nheads) / el
+    return dict(value=tokens_per_s, unit="tokens/s/layer", cores=nthreads, kind="oracle",
+                sample=f"1 sequence x {nh} of {w.nheads} heads x L={w.seqlen}, scaled to a full layer")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="siso", choices=["siso", "mimo", "long", "decode", "tiny"])
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and sequences shard with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    m3.load_library()
+    torch.cuda.synchronize()
+
+    w = inputs.WORKLOADS[args.workload]
+    if w.steps:
+        r = bench_decode(w, args.steps * 10, args.warmup * 10)
+        value, unit, ms = r["updates_per_s"], "state-updates/s", r["ms"]
+        roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=None, kernel="decode_kernel")
+        config = dict(workload="decode: 128 seq x 32 heads, N=128, P=64, R=4, bf16 in, fp32 state",
+                      batch=w.batch, nheads=w.nheads, dstate=w.dstate, headdim=w.headdim, rank=w.rank,
+                      state_buffers=3)
+    else:
+        r = bench_prefill(w, args.steps, args.warmup, chunk=args.chunk)
+        value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
+        roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="prefill step (chunk_state + state_pass + chunk_output)",
+                    mfma_tflops=round(r["tflops"], 2),
+                    mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+        config = dict(workload=f"{w.name} prefill: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
+                               f"N={w.dstate}, R={w.rank}, {w.dtype} in, fp32 state",
+                      batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, dstate=w.dstate,
+                      headdim=w.headdim, rank=w.rank, chunk=r["chunk"])
+    out = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="bf16" if w.dtype == "bf16" else "f32", data="synthetic (seeded, on device)",
+               config=config, roofline=roof)
+    if not args.no_secondary and args.workload == "siso":
+        sec = {}
+        rm = bench_prefill(inputs.WORKLOADS["mimo"], max(5, args.steps // 2), args.warmup)
+        sec["mimo_prefill"] = dict(tokens_per_s_layer=rm["tokens_per_s"], ms=rm["ms"], chunk=rm["chunk"],
+                                   hbm_frac=round(rm["gbs"] / HBM_PEAK_GBS, 4),
+                                   mfma_frac=round(rm["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+        wd = inputs.WORKLOADS["decode"]
+        rd = bench_decode(wd, 200, 30)
+        sec["mimo_decode"] = dict(state_updates_per_s=rd["updates_per_s"], us_per_step=rd["ms"] * 1e3,
+                                  hbm_gbs=round(rd["gbs"], 1), hbm_frac=round(rd["gbs"] / HBM_PEAK_GBS, 4),
+                                  table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
+        out["secondary"] = sec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 SSM recurrence library (libm3.so).
+ *
+ * The library computes the per-head Mamba-3 state-space recurrence described on
+ * the Mamba-3 pages ("Mamba-3: Improved Sequence Modeling using State Space
+ * Principles", explainer page sections 3.1-3.3 and panels 1-4; paper page
+ * Table 1 caption):
+ *
+ *   alpha_t = exp(dt_t A), beta_t = (1 - lam_t) dt_t alpha_t, gamma_t = lam_t dt_t
+ *   H_t = alpha_t R(phi_t) H_{t-1} + beta_t R(phi_t) B_{t-1} X_{t-1}^T + gamma_t B_t X_t^T
+ *   Y_t = H_t^T C_t
+ *
+ * per (batch, head), with H an N x P fp32 state whose adjacent row pairs
+ * (2k, 2k+1) rotate by the per-step angle phi_t[k] (the real form of the complex
+ * state, Prop. 2), B_t, C_t N x R and X_t P x R (rank-R MIMO, Eqs. 12-14).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers into memory the caller owns; the
+ *    library allocates nothing and keeps no state between calls.
+ *  - Tensors are dense and row-major in the layouts given below.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *    call returns without waiting.  Shape, pointer and dtype checks run on the
+ *    host before anything is enqueued; on failure nothing is launched and a
+ *    nonzero status is returned.  A launch failure returns M3_ERR_DEVICE.  No C++
+ *    exception crosses this boundary.
+ *  - Value preconditions are NOT checked on the device (as the pages' helper
+ *    states them: finite values, dt >= 0, A <= 0, lam in [0, 1]); violating them
+ *    gives unspecified (but memory-safe) results.
+ *  - The state is exported in the physical frame, so no absolute phase crosses
+ *    the boundary between calls.
+ *  - Calls on different streams touching disjoint buffers may run concurrently.
+ */
+#ifndef M3_H
+#define M3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    M3_OK = 0,
+    M3_ERR_NULL = 1,        /* a required pointer is NULL */
+    M3_ERR_SHAPE = 2,       /* a size is negative, inconsistent or not supported */
+    M3_ERR_DTYPE = 3,       /* unknown dtype code */
+    M3_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than m3_prefill_workspace_bytes */
+    M3_ERR_DEVICE = 5,      /* a HIP call or kernel launch failed */
+    M3_ERR_ALIAS = 6        /* an output aliases an input it must not alias */
+} m3_status;
+
+/* Element type of x, B, C, B_prev, x_prev and y.  dt, A, lam, theta and the state
+ * are always fp32. */
+typedef enum { M3_FP32 = 0, M3_BF16 = 1 } m3_dtype;
+
+/* Problem geometry.
+ *   batch   b  >= 0   independent sequences
+ *   seqlen  L  >= 0   tokens per sequence (ignored by m3_decode_step)
+ *   nheads  H  >= 0   heads; A and all per-token tensors carry a head axis
+ *   headdim P         columns of the state, rows of X_t: one of 16, 32, 64, 128
+ *   dstate  N         rows of the state, rows of B_t / C_t: one of 16, 32, 64, 128, 256
+ *                     (always even: it holds N/2 rotation pairs)
+ *   rank    R         MIMO rank: 1, 2, 4 or 8
+ *   chunk             prefill tokens per chunk; 0 picks the library default.  The
+ *                     result does not depend on it (the chunked form is an exact
+ *                     rearrangement); m3_prefill_chunk_used reports the value used.
+ *   dtype             an m3_dtype code */
+typedef struct {
+    int32_t batch, seqlen, nheads, headdim, dstate, rank, chunk;
+    int32_t dtype;
+} m3_shape;
+
+/* Bytes of device workspace m3_scan_prefill needs for this shape (0 on an
+ * invalid or unsupported shape).  The buffer holds per-chunk states and needs
+ * no initialisation; it may be reused across calls on the same stream. */
+size_t m3_prefill_workspace_bytes(const m3_shape* s);
+
+/* Tokens per chunk m3_scan_prefill will actually use for this shape (the
+ * requested value rounded to a supported power of two and capped so that one
+ * chunk's tiles fit on a compute unit), or 0 on an invalid shape. */
+int32_t m3_prefill_chunk_used(const m3_shape* s);
+
+/* Chunked prefill over a whole sequence (the recurrence above for t = 0..L-1).
+ * Defined by: explainer panels 1 (coefficients, Eq. 6), 2 (causal operator as a
+ * decay x two-band product, Eq. 7), 3 (rotations as data-dependent RoPE,
+ * Prop. 3/4, Eq. 11) and 4 (MIMO write/readout, Eqs. 12-14); the chunked
+ * evaluation follows the explainer's section 3.3 remark on the chunked
+ * algorithm (an exact rearrangement).
+ *
+ *   x      [b, L, H, R, P]   dtype   X_t stored rank-major: x[b,t,h,r,p] = X_t[p, r]
+ *   B, C   [b, L, H, R, N]   dtype   B[b,t,h,r,n] = B_t[n, r]
+ *   dt     [b, L, H]         fp32    step size dt_t (>= 0)
+ *   A      [H]               fp32    per-head decay generator (<= 0)
+ *   lam    [b, L, H]         fp32    current-endpoint weight in [0, 1]
+ *   theta  [b, L, H, N/2]    fp32    per-step angle phi_t[k] of pair k (already
+ *                                    scaled by dt), or NULL = no rotation
+ *   h0     [b, H, N, P]      fp32    incoming state, or NULL = zeros
+ *   B_prev [b, H, R, N]      dtype   B and x of the token before t = 0 (the
+ *   x_prev [b, H, R, P]      dtype   delayed endpoint of the first step), both
+ *                                    NULL = zero previous write.  Give both or none.
+ *   y      [b, L, H, R, P]   dtype   out: y[b,t,h,r,p] = Y_t[p, r]
+ *   h_out  [b, H, N, P]      fp32    out: H_{L-1} (physical frame), or NULL
+ *   workspace, workspace_bytes       device scratch of at least
+ *                                    m3_prefill_workspace_bytes(s)
+ * Aliasing: h_out may equal h0.  y must not alias any input (M3_ERR_ALIAS).
+ * With L = 0 nothing is computed and h_out (if given) receives h0 (or zeros). */
+m3_status m3_scan_prefill(const m3_shape* s,
+                          const void* x, const void* B, const void* C,
+                          const float* dt, const float* A, const float* lam,
+                          const float* theta,
+                          const float* h0, const void* B_prev, const void* x_prev,
+                          void* y, float* h_out,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* One single-token decode step for b sequences x H heads, updating the state in
+ * place: h <- R(phi)[alpha h + beta B_prev x_prev^T] + gamma B x^T, y = h^T C.
+ * Defined by the same passages as the prefill, one token at a time (explainer
+ * panel 3's physical-frame loop; the decode arithmetic-intensity discussion of
+ * section 3.3 and Table 2 is why the state is streamed exactly once).
+ *
+ *   h      [b, H, N, P]      fp32    state, read and written in place
+ *   B_prev [b, H, R, N]      dtype   previous token's B and x (the caller passes
+ *   x_prev [b, H, R, P]      dtype   the previous step's B and x pointers), both
+ *                                    NULL = zero previous write
+ *   x      [b, H, R, P]      dtype   this token's X (rank-major as in the prefill)
+ *   B, C   [b, H, R, N]      dtype
+ *   dt     [b, H]            fp32
+ *   A      [H]               fp32
+ *   lam    [b, H]            fp32
+ *   theta  [b, H, N/2]       fp32 or NULL
+ *   y      [b, H, R, P]      dtype   out
+ * s->seqlen and s->chunk are ignored.  y must not alias any input; B_prev/x_prev
+ * must not alias B/x of the same step (M3_ERR_ALIAS). */
+m3_status m3_decode_step(const m3_shape* s,
+                         float* h,
+                         const void* B_prev, const void* x_prev,
+                         const void* x, const void* B, const void* C,
+                         const float* dt, const float* A, const float* lam,
+                         const float* theta,
+                         void* y, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* m3_status_str(m3_status st);
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int32_t m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3_H */

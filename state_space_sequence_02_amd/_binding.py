@@ -1,0 +1,163 @@
+"""ctypes binding of libm3.so (include/m3.h).  Argument marshalling only.
+
+Every call passes raw device pointers and the current HIP stream of the tensors'
+device; all arithmetic runs in the library's HIP kernels.  There is no fallback:
+if the library is missing or the tensors are not on a GPU the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libm3.so")
+
+M3_FP32, M3_BF16 = 0, 1
+STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
+          4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS"}
+EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_scan_prefill",
+           "m3_decode_step", "m3_status_str", "m3_version")
+
+
+class M3Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libm3.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m state_space_sequence_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, fp, sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
+    sp = ctypes.POINTER(M3Shape)
+    lib.m3_prefill_workspace_bytes.restype = sz
+    lib.m3_prefill_workspace_bytes.argtypes = [sp]
+    lib.m3_prefill_chunk_used.restype = ctypes.c_int32
+    lib.m3_prefill_chunk_used.argtypes = [sp]
+    lib.m3_scan_prefill.restype = ctypes.c_int
+    lib.m3_scan_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.m3_decode_step.restype = ctypes.c_int
+    lib.m3_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.m3_status_str.restype = ctypes.c_char_p
+    lib.m3_status_str.argtypes = [ctypes.c_int]
+    lib.m3_version.restype = ctypes.c_int32
+    lib.m3_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return M3_BF16
+    if t.dtype == torch.float32:
+        return M3_FP32
+    raise TypeError(f"x/B/C must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, device=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"tensor on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _check(code: int):
+    if code != 0:
+        raise M3Error(code, load_library().m3_status_str(code).decode())
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_shape(batch, seqlen, nheads, headdim, dstate, rank, chunk=0, dtype=M3_BF16) -> M3Shape:
+    return M3Shape(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(rank),
+                   int(chunk), int(dtype))
+
+
+def prefill_workspace_bytes(shape: M3Shape) -> int:
+    return int(load_library().m3_prefill_workspace_bytes(ctypes.byref(shape)))
+
+
+def prefill_chunk_used(shape: M3Shape) -> int:
+    return int(load_library().m3_prefill_chunk_used(ctypes.byref(shape)))
+
+
+def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
+                 y=None, h_out=None, chunk: int = 0, workspace=None,
+                 want_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill (m3_scan_prefill).
+
+    x [b,L,H,R,P], B/C [b,L,H,R,N] (fp32 or bf16, same dtype); dt/lam [b,L,H],
+    A [H], theta [b,L,H,N/2] fp32 or None; h0 [b,H,N,P] fp32 or None; B_prev
+    [b,H,R,N] / x_prev [b,H,R,P] or None.  Returns (y, h_out).  Output and
+    workspace tensors are allocated with torch when not given.
+    """
+    lib = load_library()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    dcode = _dtype_code(x)
+    shape = make_shape(b, L, H, P, N, R, chunk, dcode)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_out is None and want_state:
+        h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    need = int(lib.m3_prefill_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    code = lib.m3_scan_prefill(
+        ctypes.byref(shape), _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
+        _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
+        _ptr(h0, f32, dev), _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(y, x.dtype, dev), _ptr(h_out, f32, dev),
+        _ptr(workspace, None, dev), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code)
+    return y, h_out
+
+
+def decode_step(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=None):
+    """One decode step (m3_decode_step); updates h [b,H,N,P] in place, returns y."""
+    lib = load_library()
+    b, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    dcode = _dtype_code(x)
+    shape = make_shape(b, 1, H, P, N, R, 0, dcode)
+    if y is None:
+        y = torch.empty_like(x)
+    f32 = torch.float32
+    code = lib.m3_decode_step(
+        ctypes.byref(shape), _ptr(h, f32, dev), _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
+        _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
+        _ptr(y, x.dtype, dev), _stream(dev))
+    _check(code)
+    return y

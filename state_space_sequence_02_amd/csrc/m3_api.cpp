@@ -1,0 +1,202 @@
+// m3_api.cpp -- the extern "C" boundary of libm3.so (declared in include/m3.h).
+//
+// Host-side only: validates shapes, pointers, dtype, workspace size and
+// aliasing before anything is enqueued, plans the chunking and workspace, and
+// hands off to the launchers.  No allocation, no synchronisation, no exceptions.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "m3_internal.h"
+
+namespace m3 {
+namespace {
+
+size_t esize(int dtype) { return dtype == M3_BF16 ? 2 : 4; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+m3_status check_common(const m3_shape* s, bool need_seq) {
+  if (!s) return M3_ERR_NULL;
+  if (s->dtype != M3_FP32 && s->dtype != M3_BF16) return M3_ERR_DTYPE;
+  if (s->batch < 0 || s->nheads < 0 || (need_seq && s->seqlen < 0) || s->chunk < 0) return M3_ERR_SHAPE;
+  if (!supported_head(s->headdim) || !supported_state(s->dstate) || !supported_rank(s->rank))
+    return M3_ERR_SHAPE;
+  return M3_OK;
+}
+
+// Tokens per chunk: the requested value (or a default of 128 / R rows-worth),
+// rounded down to a power of two in [16, 256], then halved until one chunk's
+// LDS tiles fit on a compute unit.
+int choose_chunk(const m3_shape& s) {
+  int q = s.chunk > 0 ? s.chunk : std::max(16, 128 / s.rank);
+  int p2 = 16;
+  while (p2 * 2 <= q && p2 < 256) p2 *= 2;
+  q = std::max(16, std::min(p2, 256));
+  const int es = (int)esize(s.dtype);
+  while (q > 16 && (chunk_output_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget ||
+                    chunk_state_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget))
+    q /= 2;
+  if (chunk_output_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget ||
+      chunk_state_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget)
+    return 0;
+  return q;
+}
+
+}  // namespace
+
+bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
+  const int q = choose_chunk(s);
+  if (q == 0) return false;
+  const int es = (int)esize(s.dtype);
+  plan->Q = q;
+  plan->nc = s.seqlen > 0 ? (s.seqlen + q - 1) / q : 0;
+  const size_t bhc = (size_t)s.batch * s.nheads * plan->nc;
+  plan->off_state = 0;
+  plan->off_decay = align256(plan->off_state + bhc * s.headdim * s.dstate * sizeof(float));
+  plan->off_rot = align256(plan->off_decay + bhc * sizeof(float));
+  plan->bytes = align256(plan->off_rot + bhc * (s.dstate / 2) * sizeof(float2));
+  plan->lds_state = chunk_state_lds_bytes(q, s.rank, s.dstate, s.headdim, es);
+  plan->lds_output = chunk_output_lds_bytes(q, s.rank, s.dstate, s.headdim, es);
+  return true;
+}
+
+}  // namespace m3
+
+using namespace m3;
+
+extern "C" {
+
+size_t m3_prefill_workspace_bytes(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan)) return 0;
+  return plan.bytes;
+}
+
+int32_t m3_prefill_chunk_used(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan)) return 0;
+  return plan.Q;
+}
+
+m3_status m3_scan_prefill(const m3_shape* s,
+                          const void* x, const void* B, const void* C,
+                          const float* dt, const float* A, const float* lam,
+                          const float* theta,
+                          const float* h0, const void* B_prev, const void* x_prev,
+                          void* y, float* h_out,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  m3_status st = check_common(s, true);
+  if (st != M3_OK) return st;
+  const int b = s->batch, L = s->seqlen, H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
+  const size_t es = esize(s->dtype);
+  const size_t tok = (size_t)b * L * H;
+  const size_t bh = (size_t)b * H;
+  if ((B_prev == nullptr) != (x_prev == nullptr)) return M3_ERR_NULL;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (bh == 0) return M3_OK;
+  if (L == 0) {
+    if (h_out && launch_copy_or_zero(h_out, h0, bh * N * P, hs) != hipSuccess) return M3_ERR_DEVICE;
+    return M3_OK;
+  }
+  if (!x || !B || !C || !dt || !A || !lam || !y) return M3_ERR_NULL;
+
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan)) return M3_ERR_SHAPE;
+  if (!workspace || workspace_bytes < plan.bytes) return M3_ERR_WORKSPACE;
+
+  // y must not alias any input, the final state or the workspace; h_out may be
+  // exactly h0 but must not overlap anything else.
+  const size_t ybytes = tok * R * P * es;
+  const size_t sbytes = bh * N * P * sizeof(float);
+  struct { const void* p; size_t n; } ins[] = {
+      {x, tok * R * P * es}, {B, tok * R * N * es}, {C, tok * R * N * es},
+      {dt, tok * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, tok * sizeof(float)},
+      {theta, theta ? tok * (N / 2) * sizeof(float) : 0}, {h0, h0 ? sbytes : 0},
+      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es}, {workspace, plan.bytes}};
+  for (const auto& in : ins) {
+    if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
+    if (h_out && in.p != h0 && overlaps(h_out, sbytes, in.p, in.n)) return M3_ERR_ALIAS;
+  }
+  if (h_out && overlaps(h_out, sbytes, y, ybytes)) return M3_ERR_ALIAS;
+  if (h_out && h0 && h_out != h0 && overlaps(h_out, sbytes, h0, sbytes)) return M3_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  PrefillParams p;
+  p.x = x; p.B = B; p.C = C; p.dt = dt; p.A = A; p.lam = lam; p.theta = theta;
+  p.h0 = h0; p.Bp = B_prev; p.xp = x_prev; p.y = y; p.h_out = h_out;
+  p.ws_state = reinterpret_cast<float*>(ws + plan.off_state);
+  p.ws_decay = reinterpret_cast<float*>(ws + plan.off_decay);
+  p.ws_rot = reinterpret_cast<float2*>(ws + plan.off_rot);
+  p.batch = b; p.L = L; p.H = H; p.N = N; p.P = P; p.R = R; p.logR = ilog2(R);
+  p.Q = plan.Q; p.nc = plan.nc;
+  if (launch_prefill(p, plan, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
+  return M3_OK;
+}
+
+m3_status m3_decode_step(const m3_shape* s,
+                         float* h,
+                         const void* B_prev, const void* x_prev,
+                         const void* x, const void* B, const void* C,
+                         const float* dt, const float* A, const float* lam,
+                         const float* theta,
+                         void* y, void* stream) {
+  m3_status st = check_common(s, false);
+  if (st != M3_OK) return st;
+  const int b = s->batch, H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
+  const size_t es = esize(s->dtype);
+  const size_t bh = (size_t)b * H;
+  if ((B_prev == nullptr) != (x_prev == nullptr)) return M3_ERR_NULL;
+  if (bh == 0) return M3_OK;
+  if (!h || !x || !B || !C || !dt || !A || !lam || !y) return M3_ERR_NULL;
+
+  const size_t ybytes = bh * R * P * es;
+  const size_t hbytes = bh * N * P * sizeof(float);
+  struct { const void* p; size_t n; } ins[] = {
+      {x, bh * R * P * es}, {B, bh * R * N * es}, {C, bh * R * N * es},
+      {dt, bh * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, bh * sizeof(float)},
+      {theta, theta ? bh * (N / 2) * sizeof(float) : 0},
+      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es}};
+  for (const auto& in : ins) {
+    if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
+    if (overlaps(h, hbytes, in.p, in.n)) return M3_ERR_ALIAS;
+  }
+  if (overlaps(y, ybytes, h, hbytes)) return M3_ERR_ALIAS;
+  if (overlaps(B_prev, bh * R * N * es, B, bh * R * N * es) ||
+      overlaps(x_prev, bh * R * P * es, x, bh * R * P * es))
+    return M3_ERR_ALIAS;
+
+  DecodeParams p;
+  p.h = h; p.Bp = B_prev; p.xp = x_prev; p.x = x; p.B = B; p.C = C;
+  p.dt = dt; p.A = A; p.lam = lam; p.theta = theta; p.y = y;
+  p.batch = b; p.H = H; p.N = N; p.P = P; p.R = R;
+  if (launch_decode(p, s->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return M3_ERR_DEVICE;
+  return M3_OK;
+}
+
+const char* m3_status_str(m3_status st) {
+  switch (st) {
+    case M3_OK: return "ok";
+    case M3_ERR_NULL: return "a required pointer is NULL";
+    case M3_ERR_SHAPE: return "invalid or unsupported shape";
+    case M3_ERR_DTYPE: return "unknown dtype";
+    case M3_ERR_WORKSPACE: return "workspace missing or too small";
+    case M3_ERR_DEVICE: return "HIP launch failed";
+    case M3_ERR_ALIAS: return "an output aliases an input";
+  }
+  return "unknown status";
+}
+
+int32_t m3_version(void) { return 100; }
+
+}  // extern "C"

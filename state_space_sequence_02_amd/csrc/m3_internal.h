@@ -1,0 +1,80 @@
+// m3_internal.h -- internal declarations of the gfx950 Mamba-3 recurrence library.
+// Not installed; the public surface is include/m3.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/m3.h"
+
+namespace m3 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Supported geometry.  Everything the kernels index is a power of two.
+constexpr int kMaxRank = 8;
+constexpr int kLdsBudget = 160 * 1024;   // LDS per compute unit on gfx950
+
+inline bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
+
+inline bool supported_state(int N) { return N == 16 || N == 32 || N == 64 || N == 128 || N == 256; }
+inline bool supported_head(int P) { return P == 16 || P == 32 || P == 64 || P == 128; }
+inline bool supported_rank(int R) { return R == 1 || R == 2 || R == 4 || R == 8; }
+
+// ---------------------------------------------------------------------------
+// Prefill: three launches per call.
+//   chunk_state : per (b, h, chunk) the chunk's own contribution u_c to the state
+//                 at its last token (physical frame), its decay a_c and rotation.
+//   state_pass  : per (b, h, pair, column) the scan G_c = a_c R(Psi_c) G_{c-1} + u_c
+//                 over chunks; leaves in slot c the state entering chunk c.
+//   chunk_output: per (b, h, chunk) the outputs = intra-chunk quadratic part +
+//                 the entering state read out through the rotated C.
+// Workspace layout (each region 256-byte aligned):
+//   state [b*H][nc][P][N] fp32, decay [b*H][nc] fp32, rot [b*H][nc][N/2] float2.
+struct PrefillParams {
+  const void* x; const void* B; const void* C;
+  const float* dt; const float* A; const float* lam; const float* theta;
+  const float* h0; const void* Bp; const void* xp;
+  void* y; float* h_out;
+  float* ws_state; float* ws_decay; float2* ws_rot;
+  int batch, L, H, N, P, R, logR, Q, nc;
+};
+
+struct PrefillPlan {
+  int Q;              // tokens per chunk
+  int nc;             // chunks per sequence
+  size_t off_state, off_decay, off_rot, bytes;
+  size_t lds_state, lds_output;
+};
+
+// Fills `plan` for a validated shape; returns false if no chunk size fits.
+bool plan_prefill(const m3_shape& s, PrefillPlan* plan);
+size_t chunk_state_lds_bytes(int Q, int R, int N, int P, int esize);
+size_t chunk_output_lds_bytes(int Q, int R, int N, int P, int esize);
+
+hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, int dtype,
+                          hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Decode: one workgroup per (sequence, head).
+struct DecodeParams {
+  float* h;
+  const void* Bp; const void* xp;
+  const void* x; const void* B; const void* C;
+  const float* dt; const float* A; const float* lam; const float* theta;
+  void* y;
+  int batch, H, N, P, R;
+};
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
+
+// Copies (or zero-fills when src is NULL) `n` floats on the stream with a kernel
+// (no memset/memcpy nodes, so the call stays safe under graph capture).
+hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t stream);
+
+}  // namespace m3

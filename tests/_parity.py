@@ -1,0 +1,88 @@
+"""Shared helpers for GPU-vs-oracle parity tests.
+
+Tolerances: relative 2e-2 for bf16 inputs/outputs and 1e-4 for fp32, as a
+Frobenius norm per (batch, head) block (and per decode step), plus an
+elementwise check |err| <= ELEM_FACTOR * tol * (|ref| + scale).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+# The stated tolerance gates the relative Frobenius error of every (batch, head)
+# block.  Single elements are additionally held to ELEM_FACTOR x the tolerance:
+# a localized slip (a wrong token, a missing term) is off by ~100% of the
+# output scale, while the rounding tail of bf16 MFMA operands (rotated B and C,
+# the masked score tile and the entering state are rounded to bf16) reaches
+# ~2x the tolerance on a few elements out of millions.
+ELEM_FACTOR = 4.0
+
+
+def note(msg: str):
+    """Names the case about to run on the GPU (unbuffered, bypasses capture)."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def to64(t) -> np.ndarray:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu").double().numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def check_blocks(got: np.ndarray, ref: np.ndarray, tol: float, block_axes, what: str,
+                 elem_axes=None):
+    """Relative Frobenius error over each block (block_axes = axes reduced), then
+    an elementwise bound ELEM_FACTOR * tol * (|ref| + scale).  The scale is the larger of the
+    block's rms and, when elem_axes is given, the rms over elem_axes (one
+    token's rank x column outputs for y): a token whose outputs are far larger
+    than the block average (an incoming state that decays away) is judged at
+    its own magnitude, and a token whose outputs nearly cancel (C_t . B_t ~ 0
+    after the state has decayed) at the block's."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
+    err = got - ref
+    num = np.sqrt((err ** 2).sum(axis=block_axes))
+    den = np.sqrt((ref ** 2).sum(axis=block_axes))
+    rel = num / np.maximum(den, 1e-30)
+    small = den < 1e-20
+    assert (num[small] < 1e-12).all(), f"{what}: nonzero output where reference is zero"
+    worst = float(rel[~small].max()) if (~small).any() else 0.0
+    assert worst <= tol, f"{what}: worst block relative error {worst:.3e} > {tol:g}"
+    scale = np.sqrt((ref ** 2).mean(axis=tuple(block_axes), keepdims=True))
+    if elem_axes is not None:
+        scale = np.maximum(scale, np.sqrt((ref ** 2).mean(axis=tuple(elem_axes), keepdims=True)))
+    bound = ELEM_FACTOR * tol * (np.abs(ref) + scale) + 1e-30
+    ratio = np.abs(err) / bound
+    assert ratio.max() <= 1.0, f"{what}: elementwise error {ratio.max():.2f}x the bound"
+    return worst
+
+
+def dev_inputs(d: dict, device="cuda") -> dict:
+    return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def oracle_inputs(d: dict, heads=None) -> dict:
+    """Float64 copies of a prefill input dict, optionally restricted to heads."""
+    out = {}
+    for k, v in d.items():
+        if v is None:
+            out[k] = None
+            continue
+        t = v.detach().to("cpu")
+        if heads is not None:
+            if k == "A":
+                t = t[heads]
+            elif k in ("h0", "B_prev", "x_prev"):
+                t = t[:, heads]
+            else:
+                t = t[:, :, heads]
+        out[k] = t.double().numpy().copy()
+    return out

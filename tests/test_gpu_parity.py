@@ -1,0 +1,265 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Small cases span several chunks and MFMA tiles with ragged tails; the workload
+cases run at full size in the bench's launch configuration and compare sampled
+heads (the oracle computes each (batch, head) independently).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import state_space_sequence_02_amd as m3
+from state_space_sequence_02_amd import inputs
+
+from _parity import TOL, check_blocks, dev_inputs, note, oracle_inputs, to64
+
+pytestmark = pytest.mark.gpu
+
+PREFILL_KEYS = ("x", "B", "C", "dt", "A", "lam", "theta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m3.load_library()
+
+
+def _run_prefill(d, carry=None, chunk=0, h_out=None, want_state=True):
+    kw = {k: d[k] for k in PREFILL_KEYS}
+    if carry:
+        kw.update(carry)
+    y, h = m3.scan_prefill(**kw, chunk=chunk, h_out=h_out, want_state=want_state)
+    torch.cuda.synchronize()
+    return y, h
+
+
+def _prefill_case(w, seed, carry, chunk, heads=None, seqlen=None):
+    d = inputs.make_prefill_inputs(w, seed=seed, seqlen=seqlen)
+    c = inputs.random_carry(w, seed=seed + 100) if carry else None
+    dg = dev_inputs(d)
+    cg = dev_inputs(c) if c else None
+    note(f"prefill {w.name} b={w.batch} L={seqlen or w.seqlen} H={w.nheads} P={w.headdim} "
+         f"N={w.dstate} R={w.rank} {w.dtype} chunk={chunk} carry={carry} seed={seed}")
+    y, h = _run_prefill(dg, cg, chunk)
+    o = oracle_inputs({**d, **(c or {})}, heads)
+    yr, hr = oracle.scan(**o)
+    yg, hg = to64(y), to64(h)
+    if heads is not None:
+        yg, hg = yg[:, :, heads], hg[:, heads]
+    tol = TOL[w.dtype]
+    e1 = check_blocks(yg, yr, tol, (1, 3, 4), "y", elem_axes=(3, 4))
+    e2 = check_blocks(hg, hr, tol, (2, 3), "h_out")
+    return e1, e2
+
+
+SMALL = [
+    dict(name="tiny", kw={}, chunk=64),
+    dict(name="tiny", kw={}, chunk=16),
+    dict(name="tiny", kw=dict(batch=2, seqlen=150, nheads=3, headdim=32, dstate=64, rank=2), chunk=32),
+    dict(name="siso", kw=dict(batch=2, seqlen=200, nheads=3), chunk=64),
+    dict(name="siso", kw=dict(batch=1, seqlen=333, nheads=2, headdim=32, dstate=32), chunk=128),
+    dict(name="mimo", kw=dict(batch=1, seqlen=130, nheads=2), chunk=32),
+    dict(name="mimo", kw=dict(batch=2, seqlen=97, nheads=2), chunk=64),
+    dict(name="mimo", kw=dict(batch=1, seqlen=70, nheads=2, headdim=16, dstate=16, rank=8), chunk=16),
+    dict(name="mimo", kw=dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=128, rank=2), chunk=32),
+    dict(name="mimo", kw=dict(batch=1, seqlen=64, nheads=1, headdim=64, dstate=256, rank=1), chunk=32),
+    dict(name="long", kw=dict(seqlen=515, nheads=2), chunk=128),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['name']}-{c['kw']}-q{c['chunk']}")
+@pytest.mark.parametrize("carry", [False, True])
+def test_prefill_small(case, carry):
+    w = inputs.workload(case["name"], **case["kw"])
+    _prefill_case(w, seed=3, carry=carry, chunk=case["chunk"])
+
+
+def test_prefill_without_rotation():
+    w = inputs.workload("mimo", batch=1, seqlen=150, nheads=2, rotation=False)
+    _prefill_case(w, seed=4, carry=True, chunk=32)
+    w = inputs.workload("tiny", seqlen=100, rotation=False)
+    _prefill_case(w, seed=4, carry=True, chunk=32)
+
+
+def test_zero_angles_match_no_rotation_bitwise():
+    w = inputs.workload("mimo", batch=1, seqlen=100, nheads=2)
+    d = dev_inputs(inputs.make_prefill_inputs(w, seed=5))
+    note("prefill theta=0 vs theta=NULL")
+    y0, h0 = _run_prefill(dict(d, theta=torch.zeros_like(d["theta"])), chunk=32)
+    yn, hn = _run_prefill(dict(d, theta=None), chunk=32)
+    assert torch.equal(y0, yn) and torch.equal(h0, hn)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_chunk_size_invariance(dtype):
+    w = inputs.workload("mimo", batch=1, seqlen=300, nheads=2, rank=2, dstate=64, dtype=dtype)
+    d = inputs.make_prefill_inputs(w, seed=6)
+    c = inputs.random_carry(w, seed=7)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
+    outs = []
+    for q in (16, 32, 64, 128):
+        note(f"chunk invariance {dtype} q={q}")
+        y, h = _run_prefill(dg, cg, chunk=q)
+        check_blocks(to64(y), yr, TOL[dtype], (1, 3, 4), f"y q={q}", elem_axes=(3, 4))
+        check_blocks(to64(h), hr, TOL[dtype], (2, 3), f"h q={q}")
+        outs.append((to64(y), to64(h)))
+    for y, h in outs[1:]:
+        check_blocks(y, outs[0][0], TOL[dtype], (1, 3, 4), "y vs q=16", elem_axes=(3, 4))
+
+
+def test_run_twice_bit_exact():
+    w = inputs.workload("mimo", batch=2, seqlen=257, nheads=2)
+    dg = dev_inputs(inputs.make_prefill_inputs(w, seed=8))
+    note("prefill run twice")
+    y1, h1 = _run_prefill(dg, chunk=32)
+    y2, h2 = _run_prefill(dg, chunk=32)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_state_in_place_and_empty_and_single():
+    w = inputs.workload("siso", batch=2, seqlen=1, nheads=3)
+    d = inputs.make_prefill_inputs(w, seed=9)
+    c = inputs.random_carry(w, seed=10)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
+    note("prefill L=1, h_out aliases h0")
+    h_io = cg["h0"].clone()
+    y, h = _run_prefill(dg, dict(cg, h0=h_io), chunk=64, h_out=h_io)
+    assert h.data_ptr() == h_io.data_ptr()
+    check_blocks(to64(y), yr, TOL["bf16"], (1, 3, 4), "y L=1", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL["bf16"], (2, 3), "h L=1")
+    note("prefill L=0")
+    d0 = dev_inputs(inputs.make_prefill_inputs(w, seed=9, seqlen=0))
+    y0, h0 = _run_prefill(d0, cg, chunk=64)
+    assert y0.numel() == 0 and torch.equal(h0, cg["h0"])
+    y0, h0 = _run_prefill(d0, None, chunk=64)
+    assert not h0.any()
+
+
+def test_prefill_errors_surface():
+    w = inputs.workload("siso", batch=1, seqlen=16, nheads=1)
+    dg = dev_inputs(inputs.make_prefill_inputs(w, seed=11))
+    note("prefill error paths")
+    with pytest.raises(m3.M3Error, match="M3_ERR_WORKSPACE"):
+        m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS},
+                        workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(m3.M3Error, match="M3_ERR_ALIAS"):
+        m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS}, y=dg["x"])
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+def _decode_case(w, steps, seed, carry_prev=True, h_init=None):
+    d = inputs.make_decode_inputs(w, seed=seed, steps=steps)
+    dg = dev_inputs(d)
+    b, H, N, P = w.batch, w.nheads, w.dstate, w.headdim
+    h0 = torch.randn((b, H, N, P), generator=torch.Generator().manual_seed(seed + 1)) * 0.5 \
+        if h_init is None else h_init
+    h = h0.to("cuda").contiguous().clone()
+    ys = []
+    note(f"decode b={b} H={H} P={P} N={N} R={w.rank} {w.dtype} steps={steps} seed={seed}")
+    for s in range(steps):
+        kw = {}
+        if s > 0 and carry_prev:
+            kw = dict(B_prev=dg["B"][s - 1], x_prev=dg["x"][s - 1])
+        ys.append(m3.decode_step(h, dg["x"][s], dg["B"][s], dg["C"][s], dg["dt"][s], dg["A"],
+                                 dg["lam"][s], dg["theta"][s] if dg["theta"] is not None else None, **kw))
+    torch.cuda.synchronize()
+    y = torch.stack(ys)
+    return d, h0, y, h
+
+
+@pytest.mark.parametrize("shape", [
+    dict(batch=3, nheads=2, headdim=64, dstate=128, rank=4, dtype="bf16"),
+    dict(batch=2, nheads=3, headdim=64, dstate=64, rank=1, dtype="bf16"),
+    dict(batch=2, nheads=2, headdim=16, dstate=16, rank=1, dtype="fp32"),
+    dict(batch=2, nheads=2, headdim=32, dstate=64, rank=2, dtype="fp32"),
+    dict(batch=1, nheads=2, headdim=128, dstate=256, rank=8, dtype="bf16"),
+])
+def test_decode_small(shape):
+    w = inputs.workload("decode", **shape)
+    d, h0, y, h = _decode_case(w, steps=12, seed=12)
+    yr, hr = oracle.decode_steps(h0, d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"])
+    tol = TOL[w.dtype]
+    check_blocks(to64(y), yr, tol, (3, 4), "decode y")
+    check_blocks(to64(h), hr, tol, (2, 3), "decode h")
+
+
+def test_prefill_then_decode_handoff():
+    """prefill(L - k) followed by k decode steps equals prefill(L)."""
+    w = inputs.workload("mimo", batch=2, seqlen=133, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=13)
+    c = inputs.random_carry(w, seed=14)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    k, L = 5, w.seqlen
+    note("handoff prefill + decode")
+    pre = {kk: (v[:, :L - k].contiguous() if kk in ("x", "B", "C", "dt", "lam", "theta") else v)
+           for kk, v in dg.items()}
+    y_pre, h = _run_prefill(pre, cg, chunk=32)
+    ys = []
+    for t in range(L - k, L):
+        ys.append(m3.decode_step(h, dg["x"][:, t].contiguous(), dg["B"][:, t].contiguous(),
+                                 dg["C"][:, t].contiguous(), dg["dt"][:, t].contiguous(), dg["A"],
+                                 dg["lam"][:, t].contiguous(), dg["theta"][:, t].contiguous(),
+                                 B_prev=dg["B"][:, t - 1].contiguous(), x_prev=dg["x"][:, t - 1].contiguous()))
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
+    y_all = np.concatenate([to64(y_pre), np.stack([to64(v) for v in ys], axis=1)], axis=1)
+    check_blocks(y_all, yr, TOL["bf16"], (1, 3, 4), "handoff y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL["bf16"], (2, 3), "handoff h")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled heads
+
+def test_workload_tiny_exact_config():
+    w = inputs.WORKLOADS["tiny"]
+    _prefill_case(w, seed=0, carry=False, chunk=w.chunk)
+
+
+def test_workload_siso_full_size():
+    w = inputs.WORKLOADS["siso"]
+    _prefill_case(w, seed=0, carry=False, chunk=w.chunk, heads=[0, 13, 31])
+
+
+def test_workload_mimo_full_size():
+    w = inputs.WORKLOADS["mimo"]
+    _prefill_case(w, seed=0, carry=False, chunk=w.chunk, heads=[0, 22])
+
+
+def test_workload_long_full_size():
+    w = inputs.WORKLOADS["long"]
+    note("long: generating inputs on the device")
+    d = inputs.make_prefill_inputs(w, seed=0, device="cuda")
+    note(f"prefill long chunk={w.chunk}")
+    y, h = _run_prefill(d, chunk=w.chunk)
+    heads = [5, 30]
+    yr, hr = oracle.scan(**oracle_inputs(d, heads))
+    check_blocks(to64(y[:, :, heads]), yr, TOL["bf16"], (1, 3, 4), "long y", elem_axes=(3, 4))
+    check_blocks(to64(h[:, heads]), hr, TOL["bf16"], (2, 3), "long h")
+
+
+def test_workload_decode_full_size():
+    w = inputs.WORKLOADS["decode"]
+    note("decode workload: generating steps on the device")
+    d = inputs.make_decode_inputs(w, seed=0, device="cuda")
+    h = torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device="cuda")
+    ys = []
+    note("decode workload: 256 steps")
+    for s in range(w.steps):
+        kw = dict(B_prev=d["B"][s - 1], x_prev=d["x"][s - 1]) if s else {}
+        ys.append(m3.decode_step(h, d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"], d["lam"][s],
+                                 d["theta"][s], **kw))
+    torch.cuda.synchronize()
+    seqs, heads = [0, 77, 127], [0, 19, 31]
+    ysel = torch.stack([ys[s][seqs][:, heads] for s in range(w.steps)])
+    sub = {k: (v[:, seqs][:, :, heads] if (v is not None and k != "A") else v) for k, v in d.items()}
+    sub["A"] = d["A"][heads]
+    yr, hr = oracle.decode_steps(np.zeros((3, 3, w.dstate, w.headdim)), sub["x"], sub["B"], sub["C"],
+                                 sub["dt"], sub["A"], sub["lam"], sub["theta"])
+    check_blocks(to64(ysel), yr, TOL["bf16"], (3, 4), "decode workload y")
+    check_blocks(to64(h[seqs][:, heads]), hr, TOL["bf16"], (2, 3), "decode workload h")
