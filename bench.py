@@ -208,7 +208,7 @@ def main():
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
         roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="prefill step (chunk_state + state_pass + chunk_output)",
+                    kernel="prefill_kernel (step also holds a ~2 us reset_kernel)",
                     mfma_tflops=round(r["tflops"], 2),
                     mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFS, 4))
         config = dict(workload=f"{w.name} prefill: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libm3.so")
-SOURCES = ["m3_api.cpp", "m3_decode.hip", "m3_prefill.hip"]
+SOURCES = (["m3_api.cpp", "m3_decode.hip", "m3_util.hip", "m3_fused.hip"] +
+           [f"m3_fused_{t}_n{n}.hip" for t in ("bf16", "f32") for n in (16, 32, 64, 128, 256)])
 ARCH = "gfx950"
 
 
@@ -53,7 +54,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"

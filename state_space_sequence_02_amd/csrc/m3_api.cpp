@@ -33,20 +33,22 @@ m3_status check_common(const m3_shape* s, bool need_seq) {
 }
 
 // Tokens per chunk: the requested value (or a default of 128 / R rows-worth),
-// rounded down to a power of two in [16, 256], then halved until one chunk's
-// LDS tiles fit on a compute unit.
+// rounded down to a power of two in [16, 256], then halved until the chunk's
+// rows and angles fit the kernel's register budget and its LDS tiles fit on a
+// compute unit.
+size_t lds_need(int q, const m3_shape& s) {
+  return fused_lds_bytes(q, s.rank, s.dstate, s.headdim, (int)esize(s.dtype));
+}
+
 int choose_chunk(const m3_shape& s) {
   int q = s.chunk > 0 ? s.chunk : std::max(16, 128 / s.rank);
   int p2 = 16;
   while (p2 * 2 <= q && p2 < 256) p2 *= 2;
   q = std::max(16, std::min(p2, 256));
-  const int es = (int)esize(s.dtype);
-  while (q > 16 && (chunk_output_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget ||
-                    chunk_state_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget))
+  while (q > 16 && (q * s.rank > fused_max_rows(s.dstate) || q * (s.dstate / 2) > kFusedAngleCap))
     q /= 2;
-  if (chunk_output_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget ||
-      chunk_state_lds_bytes(q, s.rank, s.dstate, s.headdim, es) > (size_t)kLdsBudget)
-    return 0;
+  while (q > 16 && lds_need(q, s) > (size_t)kLdsBudget) q /= 2;
+  if (lds_need(q, s) > (size_t)kLdsBudget) return 0;
   return q;
 }
 
@@ -55,16 +57,16 @@ int choose_chunk(const m3_shape& s) {
 bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
   const int q = choose_chunk(s);
   if (q == 0) return false;
-  const int es = (int)esize(s.dtype);
   plan->Q = q;
   plan->nc = s.seqlen > 0 ? (s.seqlen + q - 1) / q : 0;
   const size_t bhc = (size_t)s.batch * s.nheads * plan->nc;
-  plan->off_state = 0;
-  plan->off_decay = align256(plan->off_state + bhc * s.headdim * s.dstate * sizeof(float));
-  plan->off_rot = align256(plan->off_decay + bhc * sizeof(float));
-  plan->bytes = align256(plan->off_rot + bhc * (s.dstate / 2) * sizeof(float2));
-  plan->lds_state = chunk_state_lds_bytes(q, s.rank, s.dstate, s.headdim, es);
-  plan->lds_output = chunk_output_lds_bytes(q, s.rank, s.dstate, s.headdim, es);
+  const size_t map = (size_t)s.headdim * s.dstate * sizeof(float);
+  plan->off_flags = 256;
+  plan->off_recs = align256(plan->off_flags + bhc * sizeof(unsigned));
+  plan->off_maps = align256(plan->off_recs + bhc * (s.dstate + 2) * sizeof(float));
+  plan->off_states = align256(plan->off_maps + bhc * map);
+  plan->bytes = align256(plan->off_states + bhc * map);
+  plan->lds = lds_need(q, s);
   return true;
 }
 
@@ -132,15 +134,17 @@ m3_status m3_scan_prefill(const m3_shape* s,
   if (h_out && h0 && h_out != h0 && overlaps(h_out, sbytes, h0, sbytes)) return M3_ERR_ALIAS;
 
   char* ws = static_cast<char*>(workspace);
-  PrefillParams p;
-  p.x = x; p.B = B; p.C = C; p.dt = dt; p.A = A; p.lam = lam; p.theta = theta;
-  p.h0 = h0; p.Bp = B_prev; p.xp = x_prev; p.y = y; p.h_out = h_out;
-  p.ws_state = reinterpret_cast<float*>(ws + plan.off_state);
-  p.ws_decay = reinterpret_cast<float*>(ws + plan.off_decay);
-  p.ws_rot = reinterpret_cast<float2*>(ws + plan.off_rot);
-  p.batch = b; p.L = L; p.H = H; p.N = N; p.P = P; p.R = R; p.logR = ilog2(R);
-  p.Q = plan.Q; p.nc = plan.nc;
-  if (launch_prefill(p, plan, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
+  FusedParams f;
+  f.x = x; f.B = B; f.C = C; f.dt = dt; f.A = A; f.lam = lam; f.theta = theta;
+  f.h0 = h0; f.Bp = B_prev; f.xp = x_prev; f.y = y; f.h_out = h_out;
+  f.counter = reinterpret_cast<unsigned*>(ws);
+  f.flags = reinterpret_cast<unsigned*>(ws + plan.off_flags);
+  f.recs = reinterpret_cast<float*>(ws + plan.off_recs);
+  f.maps = reinterpret_cast<float*>(ws + plan.off_maps);
+  f.states = reinterpret_cast<float*>(ws + plan.off_states);
+  f.batch = b; f.L = L; f.H = H; f.N = N; f.P = P; f.R = R; f.logR = ilog2(R);
+  f.Q = plan.Q; f.nc = plan.nc;
+  if (launch_fused_prefill(f, plan.lds, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
 }
 

@@ -1,0 +1,3 @@
+// Instantiates the single-pass prefill kernels for one (dtype, state size).
+#include "m3_fused_kernel.h"
+M3_FUSED_INSTANTIATE(float, f32, 64)

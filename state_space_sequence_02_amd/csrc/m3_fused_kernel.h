@@ -1,0 +1,820 @@
+// m3_fused_kernel.h -- single-pass chunked Mamba-3 prefill kernel for gfx950.
+//
+// One workgroup (8 waves) per (sequence, chunk).  Each input element is read
+// from HBM once; besides the outputs a chunk writes one N x P fp32 state (and,
+// only when its successor would otherwise wait, its own affine map).
+//
+// The arithmetic is the exact chunked rearrangement of the recurrence
+//   H_t = alpha_t R(phi_t) H_{t-1} + beta_t R(phi_t) V_{t-1} + gamma_t V_t,
+//   V_t = B_t X_t^T,  Y_t = H_t^T C_t
+// (Mamba-3 explainer panels 1, 3, 4; its chunked-algorithm remark in sec. 3.3;
+// the decay x two-band structured mask of the paper page's Figure 1 and the
+// explainer's Eq. 7; data-dependent RoPE, Prop. 3/4 and Eq. 11).  With
+// chunk-local l_t = sum_{t0<=j<=t} dt_j A and Phi_t = sum_{t0<=j<=t} phi_j:
+//
+//   Y_t  = exp(l_t) C~_t^T S_in + sum_{t0<=s<=t} exp(l_t-l_s) m_ts (C~_t . B~_s) X_s
+//   m_ts = gamma_s (s == t),  gamma_s + (1-lam_{s+1}) dt_{s+1} (s < t)
+//   S_out = a_c R(Psi_c) S_in + U_c,   U_c = R(Psi_c) sum_s exp(l_end-l_s) w_s B~_s X_s^T
+//   w_s  = gamma_s + (1-lam_{s+1}) dt_{s+1}   (the next token's delayed endpoint,
+//          zero after the last token of the sequence)
+//   B~_s = R(-Phi_s) B_s,  C~_t = R(-Phi_t) C_t,  a_c = exp(l_end), Psi_c = Phi_end
+// S_in of the first chunk is h0 + (1-lam_0) dt_0 B_prev X_prev^T; S_out of the
+// last chunk is the final state.  Exponents are differences l_t - l_s <= 0.
+//
+// Passing states between chunks (the setupai page's "hardware-aware parallel
+// scan"): chunk c's map S -> a_c R(Psi_c) S + U_c is affine, so a chunk whose
+// predecessor has not finished composes the predecessors' maps itself
+// (decoupled look-back).  Flags per chunk: 1 = map published, 2 = S_out
+// published.  A chunk publishes its map only when its predecessor's state is
+// not yet there.  Workgroups take chunk-major tickets from an atomic counter,
+// so every chunk a workgroup looks back at holds a lower ticket and is already
+// running: every wait ends.  A bounded spin turns a wait that never ends into
+// NaN outputs.  Cross-workgroup data moves with device-scope relaxed atomic
+// loads/stores; a wave waits for its stores to complete (s_waitcnt 0) and the
+// last wave to finish raises the flag (an LDS counter), so no cache-wide
+// write-back/invalidate and no workgroup barrier is needed to publish.
+//
+// Work order inside a workgroup:
+//   A  scalars (dt, lam -> l, weights per row) and angles (-> cos/sin Phi table)
+//   B  stage B~ (rotated) and X row-major in LDS (one batch of loads per thread)
+//   C  U = R(Psi) sum_s W_s B~_s^T X_s on MFMA (operands by LDS transpose reads);
+//      publish the map if needed
+//   D  look back for S_in; S_out = a R(Psi) S_in + U; stores issued
+//   E  outputs per 16-row tile: C~ S_in and the masked intra-chunk products on
+//      MFMA; y stored; after the first tile, flag 2 raised
+#pragma once
+
+#include <algorithm>
+
+#include "m3_device.h"
+
+namespace m3 {
+namespace fused {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr unsigned kSpinLimit = 1u << 20;
+constexpr int kAngleCap = kFusedAngleCap;   // max Q * N/2 angles per chunk
+
+// Largest number of (token, rank) rows per chunk for state size N (bounds the
+// C~ fragments a wave keeps in registers).
+__host__ __device__ constexpr int fused_rows_cap(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
+
+__host__ __device__ inline int round_up_i(int a, int b) { return (a + b - 1) / b * b; }
+__host__ __device__ inline size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
+
+struct Lds {
+  size_t row, rw, csH, B, X, misc, total;
+  size_t tok, seg;   // aliases inside B (used only before B~ is staged)
+};
+// row: per (token, rank) row float4 {l, w, gamma, W}
+// rw: per row float2 {w, gamma} x exp(l_be - l) with be the last row of the row's
+//     32-row block (the factored decay of the off-diagonal mask blocks)
+// csH: cos/sin of Phi [Q][N/2] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8]
+// B: B~ [QRp][N+8];  X: X [QRp][P+8];  tok (Q floats) and seg (512 floats) live in B's space
+__host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize) {
+  const int QRp = round_up_i(Q * R, 32);
+  Lds o;
+  o.row = 0;
+  o.rw = o.row + sizeof(float4) * QRp;
+  o.csH = o.rw + sizeof(float2) * QRp;
+  o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2), (size_t)esize * P * (N + 8)), 16);
+  o.X = o.B + max_sz((size_t)esize * QRp * (N + 8), sizeof(float) * ((size_t)Q + 512));
+  o.misc = o.X + (size_t)esize * QRp * (P + 8);
+  o.total = o.misc + 32;
+  o.tok = o.B;
+  o.seg = o.B + sizeof(float) * Q;
+  return o;
+}
+
+__device__ __forceinline__ size_t tok_index(const FusedParams& p, int b, int t, int h) {
+  return ((size_t)b * p.L + t) * p.H + h;
+}
+
+// Device-scope relaxed 8-byte load/store of two floats.
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+__device__ __forceinline__ void st_dev2(float* p, float a, float b) {
+  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every memory operation this wave issued has completed.
+__device__ __forceinline__ void mem_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Every wave of the workgroup calls this once after mem_done(); the last one
+// to arrive raises flag `f` to `val`.  `ctr` is an LDS counter starting at 0.
+__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned* f, unsigned val) {
+  if ((threadIdx.x & 63) == 0) {
+    const int n = atomicAdd(ctr, 1);
+    if (n == kWaves - 1) __hip_atomic_store(f, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Raw 8-element loads (bf16: 16 B, fp32: 32 B).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> { uint4 v; };
+template <> struct Raw8<float> { uint4 v[2]; };
+__device__ __forceinline__ void raw_load(Raw8<bf16>& r, const bf16* p) { r.v = *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void raw_load(Raw8<float>& r, const float* p) {
+  r.v[0] = *reinterpret_cast<const uint4*>(p);
+  r.v[1] = *reinterpret_cast<const uint4*>(p + 4);
+}
+__device__ __forceinline__ void raw_zero(Raw8<bf16>& r) { r.v = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void raw_zero(Raw8<float>& r) { r.v[0] = r.v[1] = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void raw_store(bf16* d, const Raw8<bf16>& r) { *reinterpret_cast<uint4*>(d) = r.v; }
+__device__ __forceinline__ void raw_store(float* d, const Raw8<float>& r) {
+  reinterpret_cast<uint4*>(d)[0] = r.v[0];
+  reinterpret_cast<uint4*>(d)[1] = r.v[1];
+}
+__device__ __forceinline__ void raw_unpack(const Raw8<bf16>& r, float (&v)[8]) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void raw_unpack(const Raw8<float>& r, float (&v)[8]) {
+  v[0] = __uint_as_float(r.v[0].x); v[1] = __uint_as_float(r.v[0].y);
+  v[2] = __uint_as_float(r.v[0].z); v[3] = __uint_as_float(r.v[0].w);
+  v[4] = __uint_as_float(r.v[1].x); v[5] = __uint_as_float(r.v[1].y);
+  v[6] = __uint_as_float(r.v[1].z); v[7] = __uint_as_float(r.v[1].w);
+}
+template <typename T> __device__ __forceinline__ void store8(T* d, const float (&v)[8]);
+template <> __device__ __forceinline__ void store8<bf16>(bf16* d, const float (&v)[8]) {
+  bf16x8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = static_cast<bf16>(v[j]);
+  *reinterpret_cast<bf16x8*>(d) = o;
+}
+template <> __device__ __forceinline__ void store8<float>(float* d, const float (&v)[8]) {
+  reinterpret_cast<float4*>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// R(-phi) on the 4 pairs of 8 consecutive state entries (even start), cos/sin from cs.
+__device__ __forceinline__ void rotate_neg(float (&v)[8], const float2* cs) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float2 q = cs[j];
+    const float u = v[2 * j], w = v[2 * j + 1];
+    v[2 * j] = q.x * u + q.y * w;
+    v[2 * j + 1] = -q.y * u + q.x * w;
+  }
+}
+
+// MFMA operand fragment for column c0 + lane%16 of a row-major [row][col] LDS
+// tile, holding rows r0..r0+3 in slots 0..3 and r1..r1+3 in slots 4..7 (r0, r1
+// may depend on the lane's group lane/16).  bf16: two ds_read_b64_tr_b16 (within
+// each 16-lane group, lane i supplies row r + i/4, columns c0 + 4*(i%4)..+3, and
+// lane l receives rows r..r+3 of column c0 + l).  fp32: eight scalar reads.
+__device__ __forceinline__ void frag_tr(Frag<bf16>& f, const bf16* base, int stride, int r0, int r1, int c0) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int i = threadIdx.x & 15;
+  const bf16* p0 = base + (r0 + (i >> 2)) * stride + c0 + 4 * (i & 3);
+  const bf16* p1 = base + (r1 + (i >> 2)) * stride + c0 + 4 * (i & 3);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+  const v4i16 ab[2] = {a, b};
+  f.v = *reinterpret_cast<const bf16x8*>(ab);
+}
+__device__ __forceinline__ void frag_tr(Frag<float>& f, const float* base, int stride, int r0, int r1, int c0) {
+  const int c = c0 + (threadIdx.x & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = base[(r0 + e) * stride + c];
+    f.v[4 + e] = base[(r1 + e) * stride + c];
+  }
+}
+
+// Inclusive scan of a[0..n) (n <= 512) in LDS by the 8 waves; tmp holds 8 floats.
+__device__ inline void block_scan(float* a, int n, float* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float v = tid < n ? a[tid] : 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) tmp[wave] = v;
+  __syncthreads();
+  float base = 0.f;
+  for (int w = 0; w < wave; ++w) base += tmp[w];
+  if (tid < n) a[tid] = v + base;
+  __syncthreads();
+}
+
+// Inclusive scan along tokens of a [Q][NH] table (the .x of float2 entries).
+__device__ inline void column_scan(float2* t, int Q, int NH, float* segtot) {
+  const int tid = threadIdx.x;
+  const int S = min(kThreads / NH, Q);
+  const int len = Q / S;
+  const int k = tid % NH, sg = tid / NH;
+  const bool act = sg < S;
+  float run = 0.f;
+  if (act) {
+    for (int s = sg * len; s < (sg + 1) * len; ++s) {
+      run += t[s * NH + k].x;
+      t[s * NH + k].x = run;
+    }
+    segtot[sg * NH + k] = run;
+  }
+  __syncthreads();
+  if (act && sg > 0) {
+    float base = 0.f;
+    for (int j = 0; j < sg; ++j) base += segtot[j * NH + k];
+    for (int s = sg * len; s < (sg + 1) * len; ++s) t[s * NH + k].x += base;
+  }
+  __syncthreads();
+}
+
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
+  constexpr int NH = N / 2;
+  constexpr int NK = (N + 31) / 32;           // 32-wide slices of the state dimension
+  constexpr int TPt = P / 16;                 // 16-column tiles of the head dimension
+  constexpr int TNt = N / 16;                 // 16-row tiles of the state dimension
+  // state tiles (phases C, D): wave w owns n-tiles nslot + NGRP*i and p-tiles pslot + WPN*j
+  constexpr int NGRP = TNt < kWaves ? TNt : kWaves;
+  constexpr int NPW = TNt / NGRP;
+  constexpr int WPN = kWaves / NGRP;
+  constexpr int PTW = (TPt + WPN - 1) / WPN;
+  constexpr int NS = N + 8;                   // LDS row stride of B~ and S_in^T
+  constexpr int XS = P + 8;                   // LDS row stride of X
+  constexpr int LOGR = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int nslot = wave % NGRP, pslot = wave / NGRP;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Q = p.Q;
+  const Lds lay = lds_layout(Q, R, N, P, sizeof(T));
+  float4* s_row = reinterpret_cast<float4*>(smem + lay.row);
+  float2* s_rw = reinterpret_cast<float2*>(smem + lay.rw);
+  float* s_tok = reinterpret_cast<float*>(smem + lay.tok);
+  float* s_seg = reinterpret_cast<float*>(smem + lay.seg);
+  float2* s_cs = reinterpret_cast<float2*>(smem + lay.csH);
+  T* s_H = reinterpret_cast<T*>(smem + lay.csH);
+  T* s_B = reinterpret_cast<T*>(smem + lay.B);
+  T* s_X = reinterpret_cast<T*>(smem + lay.X);
+  int* s_misc = reinterpret_cast<int*>(smem + lay.misc);
+  constexpr int RTW = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;   // max output row tiles per wave
+
+  // ---- ticket: chunk-major order over all sequences ----
+  if (tid == 0) {
+    s_misc[0] = (int)atomicAdd(p.counter, 1u);
+    s_misc[3] = 0;      // wave counter: map published
+    s_misc[4] = 0;      // wave counter: state published
+  }
+  __syncthreads();
+  const int ticket = s_misc[0];
+  const int nbh = p.batch * p.H;
+  const int c = ticket / nbh, bh = ticket - c * nbh;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int t0 = c * Q;
+  const int nt = min(Q, p.L - t0);
+  const int rows = nt * R;
+  const int QRp = round_up_i(Q * R, 32);
+  const int MT = QRp / 16;
+  const size_t tok0 = tok_index(p, b, t0, h);
+  const size_t tstride = (size_t)p.H;           // token step in [b, L, H] arrays
+  const size_t rowstepB = tstride * R * N, rowstepX = tstride * R * P;
+  unsigned* flags = p.flags + (size_t)bh * p.nc;
+  const T* Bg = static_cast<const T*>(p.B) + tok0 * R * N;
+  const T* Xg = static_cast<const T*>(p.x) + tok0 * R * P;
+  const T* Cg = static_cast<const T*>(p.C) + tok0 * R * N;
+  // output row tiles of this wave, paired (w, MT-1-w) for balance
+  const int ntiles_w = (MT + kWaves - 1 - wave) / kWaves;
+  auto tile_of = [&](int k) {
+    const int pair = k >> 1;
+    return (k & 1) ? MT - 1 - (wave + 2 * kWaves * pair) : wave + 2 * kWaves * pair;
+  };
+
+  // ---- A: scalars and angles ----
+  const float A = p.A[h];
+  float gv = 0.f, wv = 0.f;
+  if (tid < Q) {
+    float lv = 0.f;
+    if (tid < nt) {
+      const size_t tk = tok0 + tid * tstride;
+      const float d = p.dt[tk], lm = p.lam[tk];
+      float dn = 0.f, lmn = 1.f;
+      if (t0 + tid + 1 < p.L) { dn = p.dt[tk + tstride]; lmn = p.lam[tk + tstride]; }
+      lv = d * A;
+      gv = lm * d;
+      wv = gv + (1.f - lmn) * dn;
+    }
+    s_tok[tid] = lv;
+  }
+  if (p.theta) {
+    const float* th = p.theta + tok0 * NH;
+    const int n4 = Q * NH / 4;
+    for (int i = tid; i < n4; i += kThreads) {
+      const int s = (4 * i) / NH, k = (4 * i) - s * NH;
+      const float4 w4 = s < nt ? *reinterpret_cast<const float4*>(th + s * tstride * NH + k)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      s_cs[4 * i].x = w4.x; s_cs[4 * i + 1].x = w4.y; s_cs[4 * i + 2].x = w4.z; s_cs[4 * i + 3].x = w4.w;
+    }
+  }
+  // B and X rows (first batch) and this wave's C rows are loaded now and
+  // consumed after the angles are known.
+  const int nbi = QRp * (N / 8), nxi = QRp * (P / 8), ntot = nbi + nxi;
+  Raw8<T> raw[8];
+  auto issue_batch = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kThreads;
+      raw_zero(raw[u]);
+      if (i < nbi) {
+        const int row = i / (N / 8), ng = i - row * (N / 8);
+        if (row < rows) raw_load(raw[u], Bg + (row >> LOGR) * rowstepB + (row & (R - 1)) * N + ng * 8);
+      } else if (i < ntot) {
+        const int j = i - nbi;
+        const int row = j / (P / 8), pg = j - row * (P / 8);
+        if (row < rows) raw_load(raw[u], Xg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + pg * 8);
+      }
+    }
+  };
+  issue_batch(tid);
+  Raw8<T> craw[RTW][NK];
+#pragma unroll
+  for (int k = 0; k < RTW; ++k) {
+    const int row_a = (k < ntiles_w ? tile_of(k) : 0) * 16 + l16;
+#pragma unroll
+    for (int kn = 0; kn < NK; ++kn) {
+      const int n0 = kn * 32 + 8 * g4;
+      raw_zero(craw[k][kn]);
+      if (k < ntiles_w && row_a < rows && n0 < N)
+        raw_load(craw[k][kn], Cg + (row_a >> LOGR) * rowstepB + (row_a & (R - 1)) * N + n0);
+    }
+  }
+  __syncthreads();
+  block_scan(s_tok, Q, s_seg);
+  const float l_end = s_tok[nt - 1];
+  if (tid < Q) {
+    const float lv = s_tok[tid];
+    const float W = tid < nt ? __expf(l_end - lv) * wv : 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) s_row[tid * R + r] = make_float4(lv, wv, gv, W);
+  }
+  for (int i = Q * R + tid; i < QRp; i += kThreads) s_row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.theta) {
+    column_scan(s_cs, Q, NH, s_seg);
+    for (int i = tid; i < Q * NH; i += kThreads) {
+      float sn, cn;
+      __sincosf(s_cs[i].x, &sn, &cn);
+      s_cs[i] = make_float2(cn, sn);
+    }
+  } else {
+    for (int i = tid; i < Q * NH; i += kThreads) s_cs[i] = make_float2(1.f, 0.f);
+  }
+  __syncthreads();   // angles done; s_tok / s_seg (inside B's space) are dead
+  // Off-diagonal mask blocks use exp(l_t - l_s) = exp(l_t - l_be) exp(l_be - l_s)
+  // with be the last valid row of the source block (s <= be <= t: both factors
+  // <= 1); the second factor times the two-band weight is kept per row.
+  for (int k = tid; k < QRp; k += kThreads) {
+    float2 v = make_float2(0.f, 0.f);
+    if (k < rows) {
+      const float4 rk = s_row[k];
+      const float e = __expf(s_row[min(k | 31, rows - 1)].x - rk.x);
+      v = make_float2(e * rk.y, e * rk.z);
+    }
+    s_rw[k] = v;
+  }
+
+  // ---- B: stage B~ = R(-Phi_s) B_s and X, both row-major ----
+  for (int base = tid; base < ntot; base += kThreads * 8) {
+    if (base != tid) issue_batch(base);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kThreads;
+      if (i < nbi) {
+        const int row = i / (N / 8), ng = i - row * (N / 8);
+        float v[8];
+        raw_unpack(raw[u], v);
+        if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * NH + ng * 4);
+        store8<T>(s_B + row * NS + ng * 8, v);
+      } else if (i < ntot) {
+        const int j = i - nbi;
+        const int row = j / (P / 8), pg = j - row * (P / 8);
+        raw_store(s_X + row * XS + pg * 8, raw[u]);
+      }
+    }
+  }
+  // C~ fragments of this wave's output rows (rotated by -Phi_t)
+  Frag<T> cf[RTW][NK];
+#pragma unroll
+  for (int k = 0; k < RTW; ++k) {
+    const int row_a = (k < ntiles_w ? tile_of(k) : 0) * 16 + l16;
+    const int ta = row_a < rows ? row_a >> LOGR : 0;
+#pragma unroll
+    for (int kn = 0; kn < NK; ++kn) {
+      const int n0 = kn * 32 + 8 * g4;
+      float v[8];
+      raw_unpack(craw[k][kn], v);
+      if (n0 < N) rotate_neg(v, s_cs + ta * NH + n0 / 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) frag_set(cf[k][kn], e, v[e]);
+    }
+  }
+  __syncthreads();
+
+  // ---- C: U[n][p] = R(Psi) sum_k W_k B~[k][n] X[k][p] ----
+  // Lane layout of a (state tile ntl, column tile pt): rows n = 16 ntl + 4 g4 + j
+  // (two whole rotation pairs), column p = 16 pt + l16.
+  f32x4 uacc[NPW][PTW];
+#pragma unroll
+  for (int i = 0; i < NPW; ++i)
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) uacc[i][j] = zero4();
+  for (int ks = 0; ks < QRp; ks += 32) {
+    const int r0 = ks + 8 * g4;
+    float Wk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Wk[e] = s_row[r0 + e].w;
+    Frag<T> xf[PTW];
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) {
+      const int pt = pslot + WPN * j;
+      if (pt < TPt) frag_tr(xf[j], s_X, XS, r0, r0 + 4, pt * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int ntl = nslot + NGRP * i;
+      Frag<T> bt;
+      frag_tr(bt, s_B, NS, r0, r0 + 4, ntl * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) frag_set(bt, e, Wk[e] * frag_get(bt, e));
+#pragma unroll
+      for (int j = 0; j < PTW; ++j)
+        if (pslot + WPN * j < TPt) uacc[i][j] = mma(bt, xf[j], uacc[i][j]);
+    }
+  }
+  float2 psi[NPW][2];
+#pragma unroll
+  for (int i = 0; i < NPW; ++i) {
+    const int k0 = ((nslot + NGRP * i) * 16 + 4 * g4) >> 1;
+    psi[i][0] = s_cs[(nt - 1) * NH + k0];
+    psi[i][1] = s_cs[(nt - 1) * NH + k0 + 1];
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) {
+      f32x4& u = uacc[i][j];
+      const float u0 = psi[i][0].x * u[0] - psi[i][0].y * u[1], u1 = psi[i][0].y * u[0] + psi[i][0].x * u[1];
+      const float u2 = psi[i][1].x * u[2] - psi[i][1].y * u[3], u3 = psi[i][1].y * u[2] + psi[i][1].x * u[3];
+      u[0] = u0; u[1] = u1; u[2] = u2; u[3] = u3;
+    }
+  }
+  const float a_c = __expf(l_end);
+  const size_t slot = (size_t)P * N;
+  const size_t chunk_id = (size_t)bh * p.nc + c;
+  // Publish the map only if the predecessor's state is not there yet.
+  int need_map = 0;
+  if (c > 0 && tid == 0)
+    need_map = __hip_atomic_load(flags + c - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2u ? 0 : 1;
+  if (need_map) {   // thread 0 only: the per-pair rotation record
+    float* rec = p.recs + chunk_id * (2 * NH + 2);
+    st_dev2(rec, a_c, 0.f);
+  }
+  if (tid == 0) s_misc[2] = need_map;
+  __syncthreads();   // s_misc[2] visible; every read of the cos/sin table is done
+  if (s_misc[2]) {
+    float* U = p.maps + chunk_id * slot;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+      float* rec = p.recs + chunk_id * (2 * NH + 2);
+      if (pslot == 0 && l16 == 0) {   // R(Psi) of this lane's two pairs
+        st_dev2(rec + 2 + n0, psi[i][0].x, psi[i][0].y);
+        st_dev2(rec + 2 + n0 + 2, psi[i][1].x, psi[i][1].y);
+      }
+#pragma unroll
+      for (int j = 0; j < PTW; ++j) {
+        const int pt = pslot + WPN * j;
+        if (pt < TPt) {
+          float* d = U + (size_t)(pt * 16 + l16) * N + n0;
+          st_dev2(d, uacc[i][j][0], uacc[i][j][1]);
+          st_dev2(d + 2, uacc[i][j][2], uacc[i][j][3]);
+        }
+      }
+    }
+    mem_done();
+    arrive_and_flag(&s_misc[3], flags + c, 1u);
+  }
+
+  // ---- D: S_in by look-back; S_out = a R(Psi) S_in + U ----
+  float FA = 1.f;
+  float2 Fpsi[NPW][2];
+  f32x4 FU[NPW][PTW], sin_[NPW][PTW];
+#pragma unroll
+  for (int i = 0; i < NPW; ++i) {
+    Fpsi[i][0] = Fpsi[i][1] = make_float2(1.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) { FU[i][j] = zero4(); sin_[i][j] = zero4(); }
+  }
+  bool chain_ok = true;
+  if (c == 0) {
+    float kappa0 = 0.f;
+    if (p.Bp) kappa0 = (1.f - p.lam[tok0]) * p.dt[tok0];
+    const T* Bp = p.Bp ? static_cast<const T*>(p.Bp) + (size_t)bh * R * N : nullptr;
+    const T* xp = p.xp ? static_cast<const T*>(p.xp) + (size_t)bh * R * P : nullptr;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+#pragma unroll
+      for (int j = 0; j < PTW; ++j) {
+        const int pt = pslot + WPN * j;
+        if (pt < TPt) {
+          const int pc = pt * 16 + l16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = p.h0 ? p.h0[((size_t)bh * N + n0 + e) * P + pc] : 0.f;
+            if (Bp) {
+              float acc = 0.f;
+#pragma unroll
+              for (int r = 0; r < R; ++r) acc += to_f(Bp[r * N + n0 + e]) * to_f(xp[r * P + pc]);
+              v += kappa0 * acc;
+            }
+            sin_[i][j][e] = v;
+          }
+        }
+      }
+    }
+  } else {
+    int j = c - 1;
+    while (true) {
+      if (tid == 0) {
+        unsigned f, spins = 0;
+        while ((f = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) break;
+        }
+        s_misc[1] = (int)f;
+      }
+      __syncthreads();
+      const int f = s_misc[1];
+      __syncthreads();
+      if (f == 0) { chain_ok = false; break; }
+      const size_t jid = (size_t)bh * p.nc + j;
+      if (f == 2) {
+        const float* S = p.states + jid * slot;
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+          const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+#pragma unroll
+          for (int jj = 0; jj < PTW; ++jj) {
+            const int pt = pslot + WPN * jj;
+            if (pt < TPt) {
+              const float* q = S + (size_t)(pt * 16 + l16) * N + n0;
+              const float2 x01 = ld_dev2(q), x23 = ld_dev2(q + 2);
+              f32x4 s4;
+              s4[0] = FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y) + FU[i][jj][0];
+              s4[1] = FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y) + FU[i][jj][1];
+              s4[2] = FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y) + FU[i][jj][2];
+              s4[3] = FA * (Fpsi[i][1].y * x23.x + Fpsi[i][1].x * x23.y) + FU[i][jj][3];
+              sin_[i][jj] = s4;
+            }
+          }
+        }
+        break;
+      }
+      // f == 1: F <- F o f_j
+      const float* U = p.maps + jid * slot;
+      const float* rec = p.recs + jid * (2 * NH + 2);
+      const float aj = ld_dev2(rec).x;
+#pragma unroll
+      for (int i = 0; i < NPW; ++i) {
+        const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+        const float2 r0 = ld_dev2(rec + 2 + n0), r1 = ld_dev2(rec + 2 + n0 + 2);
+#pragma unroll
+        for (int jj = 0; jj < PTW; ++jj) {
+          const int pt = pslot + WPN * jj;
+          if (pt < TPt) {
+            const float* q = U + (size_t)(pt * 16 + l16) * N + n0;
+            const float2 x01 = ld_dev2(q), x23 = ld_dev2(q + 2);
+            FU[i][jj][0] += FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y);
+            FU[i][jj][1] += FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y);
+            FU[i][jj][2] += FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y);
+            FU[i][jj][3] += FA * (Fpsi[i][1].y * x23.x + Fpsi[i][1].x * x23.y);
+          }
+        }
+        const float2 a0 = Fpsi[i][0], a1 = Fpsi[i][1];
+        Fpsi[i][0] = make_float2(a0.x * r0.x - a0.y * r0.y, a0.y * r0.x + a0.x * r0.y);
+        Fpsi[i][1] = make_float2(a1.x * r1.x - a1.y * r1.y, a1.y * r1.x + a1.x * r1.y);
+      }
+      FA *= aj;
+      --j;
+    }
+  }
+  const float nanv = __builtin_nanf("");
+  const bool publish = c + 1 < p.nc;
+  // S_in^T goes into the (now free) cos/sin region for the readout
+#pragma unroll
+  for (int i = 0; i < NPW; ++i) {
+    const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) {
+      const int pt = pslot + WPN * j;
+      if (pt < TPt) {
+        const int pc = pt * 16 + l16;
+        f32x4 si = sin_[i][j];
+        if (!chain_ok) si[0] = si[1] = si[2] = si[3] = nanv;
+        T* hd = s_H + pc * NS + n0;
+        hd[0] = from_f<T>(si[0]); hd[1] = from_f<T>(si[1]); hd[2] = from_f<T>(si[2]); hd[3] = from_f<T>(si[3]);
+        const float q0 = a_c * si[0], q1 = a_c * si[1], q2 = a_c * si[2], q3 = a_c * si[3];
+        const f32x4 u = uacc[i][j];
+        const float o0 = psi[i][0].x * q0 - psi[i][0].y * q1 + u[0];
+        const float o1 = psi[i][0].y * q0 + psi[i][0].x * q1 + u[1];
+        const float o2 = psi[i][1].x * q2 - psi[i][1].y * q3 + u[2];
+        const float o3 = psi[i][1].y * q2 + psi[i][1].x * q3 + u[3];
+        if (publish) {
+          float* d = p.states + chunk_id * slot + (size_t)pc * N + n0;
+          st_dev2(d, o0, o1);
+          st_dev2(d + 2, o2, o3);
+        } else if (p.h_out) {
+          float* ho = p.h_out + ((size_t)bh * N + n0) * P + pc;
+          ho[0] = o0; ho[P] = o1; ho[2 * P] = o2; ho[3 * P] = o3;
+        }
+      }
+    }
+  }
+  __syncthreads();   // S_in^T complete in LDS
+
+  // ---- E: outputs, one 16-row tile at a time ----
+  T* Yg = static_cast<T*>(p.y) + tok0 * R * P;
+  bool flag_pending = publish;
+#pragma unroll
+  for (int k = 0; k < RTW; ++k) {
+    if (k >= ntiles_w) break;
+    const int it = tile_of(k);
+    if (it * 16 >= rows) continue;
+    const int row_a = it * 16 + l16;
+    const bool va = row_a < rows;
+    const int ta = row_a >> LOGR;
+    f32x4 yacc[TPt];
+#pragma unroll
+    for (int pn = 0; pn < TPt; ++pn) {
+      yacc[pn] = zero4();
+#pragma unroll
+      for (int kn = 0; kn < NK; ++kn) {
+        const int n0 = kn * 32 + 8 * g4;
+        Frag<T> hf;
+        if (n0 < N) frag_lds8(hf, s_H + (pn * 16 + l16) * NS + n0);
+        else frag_zero(hf);
+        yacc[pn] = mma(cf[k][kn], hf, yacc[pn]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = it * 16 + 4 * g4 + j;
+      const float e = row < rows ? __expf(s_row[row].x) : 0.f;
+#pragma unroll
+      for (int pn = 0; pn < TPt; ++pn) yacc[pn][j] *= e;
+    }
+    const int last_row = min(it * 16 + 15, rows - 1);
+    const int sbmax = last_row / 32;
+    const float l_t = va ? s_row[row_a].x : 0.f;
+    for (int sb = 0; sb <= sbmax; ++sb) {
+      f32x4 st0 = zero4(), st1 = zero4();
+#pragma unroll
+      for (int kn = 0; kn < NK; ++kn) {
+        const int n0 = kn * 32 + 8 * g4;
+        Frag<T> a0, a1;
+        if (n0 < N) {
+          frag_lds8(a0, s_B + (sb * 32 + l16) * NS + n0);
+          frag_lds8(a1, s_B + (sb * 32 + 16 + l16) * NS + n0);
+        } else {
+          frag_zero(a0);
+          frag_zero(a1);
+        }
+        st0 = mma(a0, cf[k][kn], st0);
+        st1 = mma(a1, cf[k][kn], st1);
+      }
+      // decay x two-band mask on the score tile
+      Frag<T> pf;
+      if (sb * 32 + 32 <= it * 16) {
+        // source block wholly before this tile: every s < t, one exp per lane
+        const int be = min(sb * 32 + 31, rows - 1);
+        const float et = va ? __expf(l_t - s_row[be].x) : 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int rb = sb * 32 + hh * 16 + 4 * g4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) frag_set(pf, hh * 4 + j, et * s_rw[rb + j].x * (hh ? st1[j] : st0[j]));
+        }
+      } else {
+        // the block holding this tile: elementwise; a lane's 4 rows in each
+        // 16-row half are min(R, 4)-row groups of one token
+        constexpr int RG = R < 4 ? R : 4;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int rb = sb * 32 + hh * 16 + 4 * g4;
+#pragma unroll
+          for (int q = 0; q < 4; q += RG) {
+            const int srow = rb + q;
+            const int s = srow >> LOGR;
+            float m = 0.f;
+            if (va && srow < rows && s <= ta) {
+              const float4 rw = s_row[srow];
+              m = __expf(l_t - rw.x) * (s < ta ? rw.y : rw.z);
+            }
+#pragma unroll
+            for (int j = q; j < q + RG; ++j) frag_set(pf, hh * 4 + j, m * (hh ? st1[j] : st0[j]));
+          }
+        }
+      }
+#pragma unroll
+      for (int pn = 0; pn < TPt; ++pn) {
+        Frag<T> xf;
+        frag_tr(xf, s_X, XS, sb * 32 + 4 * g4, sb * 32 + 16 + 4 * g4, pn * 16);
+        yacc[pn] = mma(pf, xf, yacc[pn]);
+      }
+    }
+    // the state stores were issued a whole tile ago: wait for them (before
+    // this tile's output stores join the queue) and raise the flag
+    if (flag_pending) {
+      mem_done();
+      arrive_and_flag(&s_misc[4], flags + c, 2u);
+      flag_pending = false;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = it * 16 + 4 * g4 + j;
+      if (row < rows) {
+        T* yo = Yg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + l16;
+#pragma unroll
+        for (int pn = 0; pn < TPt; ++pn) yo[pn * 16] = from_f<T>(chain_ok ? yacc[pn][j] : nanv);
+      }
+    }
+  }
+  if (flag_pending) {
+    mem_done();
+    arrive_and_flag(&s_misc[4], flags + c, 2u);
+  }
+}
+
+// Resets the ticket counter and the per-chunk flags (a kernel, not a memset, so
+// the call stays correct inside a captured graph).
+template <int Unused = 0>
+__global__ void reset_kernel(unsigned* counter, unsigned* flags, size_t nflags) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *counter = 0u;
+  for (size_t j = i; j < nflags; j += (size_t)gridDim.x * blockDim.x) flags[j] = 0u;
+}
+
+template <typename T, int N, int P, int R>
+hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
+  // LDS limit raised once per instantiation
+  static bool lds_set = false;
+  hipError_t e;
+  if (!lds_set && lds > 64 * 1024) {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)) != hipSuccess)
+      return e;
+    lds_set = true;
+  }
+  const size_t nflags = (size_t)p.batch * p.H * p.nc;
+  const unsigned rblocks = (unsigned)std::min<size_t>((nflags + 255) / 256, 1024);
+  hipLaunchKernelGGL(reset_kernel<0>, dim3(rblocks), dim3(256), 0, stream, p.counter, p.flags, nflags);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t grid = nflags;
+  hipLaunchKernelGGL((prefill_kernel<T, N, P, R>), dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int N>
+hipError_t launch_n(const FusedParams& p, size_t lds, hipStream_t s) {
+#define M3_R_CASES(PP)                                          \
+  switch (p.R) {                                                \
+    case 1: return launch<T, N, PP, 1>(p, lds, s);              \
+    case 2: return launch<T, N, PP, 2>(p, lds, s);              \
+    case 4: return launch<T, N, PP, 4>(p, lds, s);              \
+    case 8: return launch<T, N, PP, 8>(p, lds, s);              \
+    default: return hipErrorInvalidValue;                       \
+  }
+  switch (p.P) {
+    case 16: M3_R_CASES(16)
+    case 32: M3_R_CASES(32)
+    case 64: M3_R_CASES(64)
+    case 128: M3_R_CASES(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef M3_R_CASES
+}
+
+}  // namespace fused
+}  // namespace m3
+
+// One translation unit per (dtype, N) instantiates the kernels for all P and R.
+#define M3_FUSED_INSTANTIATE(TYPE, TNAME, NN)                                                   \
+  namespace m3 {                                                                                \
+  hipError_t launch_fused_##TNAME##_##NN(const FusedParams& p, size_t lds, hipStream_t s) {    \
+    return fused::launch_n<TYPE, NN>(p, lds, s);                                                \
+  }                                                                                             \
+  }

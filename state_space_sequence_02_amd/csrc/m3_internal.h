@@ -27,38 +27,36 @@ inline bool supported_head(int P) { return P == 16 || P == 32 || P == 64 || P ==
 inline bool supported_rank(int R) { return R == 1 || R == 2 || R == 4 || R == 8; }
 
 // ---------------------------------------------------------------------------
-// Prefill: three launches per call.
-//   chunk_state : per (b, h, chunk) the chunk's own contribution u_c to the state
-//                 at its last token (physical frame), its decay a_c and rotation.
-//   state_pass  : per (b, h, pair, column) the scan G_c = a_c R(Psi_c) G_{c-1} + u_c
-//                 over chunks; leaves in slot c the state entering chunk c.
-//   chunk_output: per (b, h, chunk) the outputs = intra-chunk quadratic part +
-//                 the entering state read out through the rotated C.
-// Workspace layout (each region 256-byte aligned):
-//   state [b*H][nc][P][N] fp32, decay [b*H][nc] fp32, rot [b*H][nc][N/2] float2.
-struct PrefillParams {
-  const void* x; const void* B; const void* C;
-  const float* dt; const float* A; const float* lam; const float* theta;
-  const float* h0; const void* Bp; const void* xp;
-  void* y; float* h_out;
-  float* ws_state; float* ws_decay; float2* ws_rot;
-  int batch, L, H, N, P, R, logR, Q, nc;
-};
-
+// Prefill: one launch per call (after a tiny reset of the ticket counter and
+// flags), one workgroup per (sequence, chunk); chunk states are handed from
+// chunk to chunk with decoupled look-back.
+// Workspace (each region 256-byte aligned): control block (ticket counter) |
+// flags [b*H*nc] u32 | recs [b*H*nc][N+2] fp32 (a_c, pad, cos/sin Psi_c per
+// pair) | maps [b*H*nc][P][N] fp32 | states [b*H*nc][P][N] fp32.
 struct PrefillPlan {
   int Q;              // tokens per chunk
   int nc;             // chunks per sequence
-  size_t off_state, off_decay, off_rot, bytes;
-  size_t lds_state, lds_output;
+  size_t off_flags, off_recs, off_maps, off_states, bytes;
+  size_t lds;         // dynamic LDS per workgroup
 };
 
 // Fills `plan` for a validated shape; returns false if no chunk size fits.
 bool plan_prefill(const m3_shape& s, PrefillPlan* plan);
-size_t chunk_state_lds_bytes(int Q, int R, int N, int P, int esize);
-size_t chunk_output_lds_bytes(int Q, int R, int N, int P, int esize);
 
-hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, int dtype,
-                          hipStream_t stream);
+struct FusedParams {
+  const void* x; const void* B; const void* C;
+  const float* dt; const float* A; const float* lam; const float* theta;
+  const float* h0; const void* Bp; const void* xp;
+  void* y; float* h_out;
+  unsigned* counter; unsigned* flags; float* recs; float* maps; float* states;
+  int batch, L, H, N, P, R, logR, Q, nc;
+};
+// Chunk limits of the single-pass prefill: (token, rank) rows per chunk and
+// angles (tokens x N/2) per chunk; they bound the per-thread prefetch registers.
+inline int fused_max_rows(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
+constexpr int kFusedAngleCap = 8192;
+size_t fused_lds_bytes(int Q, int R, int N, int P, int esize);
+hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Decode: one workgroup per (sequence, head).

@@ -112,7 +112,11 @@ def test_workspace_size_matches_layout(lib, name):
     nc = -(-w.seqlen // q)
     bhc = w.batch * w.nheads * nc
     a = lambda v: (v + 255) // 256 * 256
-    expect = a(a(a(bhc * w.headdim * w.dstate * 4) + bhc * 4) + bhc * (w.dstate // 2) * 8)
+    # control block | flags | per-chunk records | maps | states
+    recs = a(256 + bhc * 4)
+    maps = a(recs + bhc * (w.dstate + 2) * 4)
+    states = a(maps + bhc * w.headdim * w.dstate * 4)
+    expect = a(states + bhc * w.headdim * w.dstate * 4)
     assert m3.prefill_workspace_bytes(shape) == expect
 
 
