@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import hashlib
 import math
 import os
 import sys
@@ -57,28 +58,46 @@ def table2_intensity(n, p, r):
     return (4 * n * p * r + n * p - p * r) / (2 * (1 + 2 * n * r + p * r + n * p))
 
 
-class Timer:
-    """HIP events on the current stream (the stream the library launches on)."""
+class StepTimer:
+    """HIP events between steps on the current stream (the stream the library
+    launches on): total and per-step durations of one timed loop."""
 
-    def __init__(self):
-        self.s = torch.cuda.Event(enable_timing=True)
-        self.e = torch.cuda.Event(enable_timing=True)
+    def __init__(self, steps):
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
 
-    def start(self):
-        self.s.record(torch.cuda.current_stream())
+    def mark(self, i):
+        self.ev[i].record(torch.cuda.current_stream())
 
-    def stop(self) -> float:
-        self.e.record(torch.cuda.current_stream())
-        self.e.synchronize()
-        return self.s.elapsed_time(self.e)
+    def result(self):
+        self.ev[-1].synchronize()
+        per = [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(len(self.ev) - 1)]
+        total = self.ev[0].elapsed_time(self.ev[-1])
+        per_sorted = sorted(per)
+        return dict(ms=total / len(per), ms_median=per_sorted[len(per) // 2], ms_min=per_sorted[0])
 
 
-def bench_prefill(w, steps, warmup, chunk=None, nsets=2):
+def _timed(step, steps, warmup):
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t = StepTimer(steps)
+    for i in range(steps):
+        t.mark(i)
+        step(i)
+    t.mark(steps)
+    r = t.result()
+    torch.cuda.synchronize()
+    return r
+
+
+def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
+    """One step = one m3_scan_prefill over the whole layer (all heads), with the
+    final state exported; `nsets` input sets alternate so a step cannot be served
+    from the last-level cache left warm by the previous one."""
     dev = torch.device("cuda")
     sets = [inputs.make_prefill_inputs(w, seed=s, device=dev) for s in range(nsets)]
-    q = chunk if chunk is not None else w.chunk
     dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
-    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, q, dcode)
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, chunk, dcode)
     ws = torch.empty(m3.prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
     q_used = m3.prefill_chunk_used(shape)
     ys = [torch.empty_like(s["x"]) for s in sets]
@@ -88,31 +107,26 @@ def bench_prefill(w, steps, warmup, chunk=None, nsets=2):
     def step(i):
         d = sets[i % nsets]
         m3.scan_prefill(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"],
-                        y=ys[i % nsets], h_out=hs[i % nsets], chunk=q, workspace=ws)
+                        y=ys[i % nsets], h_out=hs[i % nsets], chunk=chunk, workspace=ws)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t = Timer()
-    t.start()
-    for i in range(steps):
-        step(i)
-    ms = t.stop() / steps
-    torch.cuda.synchronize()
+    r = _timed(step, steps, warmup)
+    ms = r["ms"]
     tok = w.batch * w.seqlen
     bpt = prefill_bytes_per_token_head(w)
     nbytes = tok * w.nheads * bpt + w.batch * w.nheads * w.dstate * w.headdim * 4
     flops = tok * w.nheads * prefill_flops_per_token_head(w, q_used)
-    return dict(ms=ms, tokens_per_s=tok / (ms * 1e-3), chunk=q_used, bytes=nbytes, flops=flops,
+    del sets, ys, hs, ws
+    return dict(r, tokens_per_s=tok / (ms * 1e-3), chunk=q_used, bytes=nbytes, flops=flops,
                 gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12)
 
 
 def bench_decode(w, steps, warmup, nstate=3):
+    """One step = one m3_decode_step over all (sequence, head) pairs; >= 3 state
+    buffers (384 MiB at the 128-sequence shape) rotate so a step cannot be served
+    from the 256 MB last-level cache left warm by the previous step."""
     dev = torch.device("cuda")
     S = w.steps
     d = inputs.make_decode_inputs(w, seed=0, device=dev)
-    # >= 3 state buffers (384 MiB at the 128-seq shape) so a step cannot be served
-    # from the 256 MB last-level cache left warm by the previous step
     hs = [torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
           for _ in range(nstate)]
     y = torch.empty_like(d["x"][0])
@@ -123,18 +137,39 @@ def bench_decode(w, steps, warmup, nstate=3):
         m3.decode_step(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
                        d["lam"][s], d["theta"][s], y=y, **kw)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t = Timer()
-    t.start()
-    for i in range(steps):
-        step(i)
-    ms = t.stop() / steps
+    r = _timed(step, steps, warmup)
+    ms = r["ms"]
     upd = w.batch * w.nheads
     nbytes = upd * decode_bytes_per_update(w)
-    return dict(ms=ms, updates_per_s=upd / (ms * 1e-3), tokens_per_s=w.batch / (ms * 1e-3),
+    del d, hs
+    return dict(r, updates_per_s=upd / (ms * 1e-3), tokens_per_s=w.batch / (ms * 1e-3),
                 bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "state_space_sequence_02_amd", "csrc")
+
+
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary for this kernel and workload, or None when there is none or the
+    kernel's source has changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_digest") != kernel_source_digest(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -173,13 +208,17 @@ def cpu_baseline(w, target_s=12.0):
                 sample=f"1 sequence x {nh} of {w.nheads} heads x L={w.seqlen}, scaled to a full layer")
 
 
+PREFILL_SOURCES = ["m3_fused_kernel.h", "m3_device.h", "m3_internal.h"]
+DECODE_SOURCES = ["m3_decode.hip", "m3_device.h", "m3_internal.h"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="siso", choices=["siso", "mimo", "long", "decode", "tiny"])
-    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--chunk", type=int, default=0, help="prefill tokens per chunk (0: library default)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -198,36 +237,51 @@ def main():
     if w.steps:
         r = bench_decode(w, args.steps * 10, args.warmup * 10)
         value, unit, ms = r["updates_per_s"], "state-updates/s", r["ms"]
+        traffic = measured_traffic("decode_kernel_decode")
         roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=None, kernel="decode_kernel")
-        config = dict(workload="decode: 128 seq x 32 heads, N=128, P=64, R=4, bf16 in, fp32 state",
+                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic, kernel="decode_kernel",
+                    algorithmic_bytes_per_launch=r["bytes"])
+        config = dict(workload=f"decode: {w.batch} seq x {w.nheads} heads, N={w.dstate}, P={w.headdim}, "
+                               f"R={w.rank}, bf16 in, fp32 state",
                       batch=w.batch, nheads=w.nheads, dstate=w.dstate, headdim=w.headdim, rank=w.rank,
                       state_buffers=3)
+        steps_done = args.steps * 10
     else:
         r = bench_prefill(w, args.steps, args.warmup, chunk=args.chunk)
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
+        traffic = measured_traffic(f"prefill_kernel_{w.name}_q{r['chunk']}")
         roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="prefill_kernel (step also holds a ~2 us reset_kernel)",
+                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="prefill_kernel (the step also runs a ~2 us reset_kernel)",
+                    algorithmic_bytes_per_launch=r["bytes"],
                     mfma_tflops=round(r["tflops"], 2),
                     mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFS, 4))
         config = dict(workload=f"{w.name} prefill: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
                                f"N={w.dstate}, R={w.rank}, {w.dtype} in, fp32 state",
                       batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, dstate=w.dstate,
                       headdim=w.headdim, rank=w.rank, chunk=r["chunk"])
-    out = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
-               ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
+        steps_done = args.steps
+    out = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=steps_done, warmup=args.warmup,
+               ms_per_step=ms, ms_median=r["ms_median"], ms_min=r["ms_min"],
+               higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16" if w.dtype == "bf16" else "f32", data="synthetic (seeded, on device)",
                config=config, roofline=roof)
     if not args.no_secondary and args.workload == "siso":
         sec = {}
-        rm = bench_prefill(inputs.WORKLOADS["mimo"], max(5, args.steps // 2), args.warmup)
-        sec["mimo_prefill"] = dict(tokens_per_s_layer=rm["tokens_per_s"], ms=rm["ms"], chunk=rm["chunk"],
-                                   hbm_frac=round(rm["gbs"] / HBM_PEAK_GBS, 4),
-                                   mfma_frac=round(rm["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+        def pre(name, chunk, steps):
+            wl = inputs.WORKLOADS[name]
+            rr = bench_prefill(wl, steps, 2, chunk=chunk)
+            return dict(tokens_per_s_layer=rr["tokens_per_s"], us=round(rr["ms"] * 1e3, 1),
+                        us_median=round(rr["ms_median"] * 1e3, 1), chunk=rr["chunk"],
+                        hbm_frac=round(rr["gbs"] / HBM_PEAK_GBS, 4),
+                        mfma_frac=round(rr["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+        sec["siso_prefill_chunk64"] = pre("siso", 64, args.steps)
+        sec["mimo_prefill"] = pre("mimo", 0, args.steps)
+        sec["long_prefill"] = pre("long", 0, max(3, args.steps // 4))
         wd = inputs.WORKLOADS["decode"]
         rd = bench_decode(wd, 200, 30)
-        sec["mimo_decode"] = dict(state_updates_per_s=rd["updates_per_s"], us_per_step=rd["ms"] * 1e3,
+        sec["mimo_decode"] = dict(state_updates_per_s=rd["updates_per_s"], us_per_step=round(rd["ms"] * 1e3, 1),
+                                  us_median=round(rd["ms_median"] * 1e3, 1),
                                   hbm_gbs=round(rd["gbs"], 1), hbm_frac=round(rd["gbs"] / HBM_PEAK_GBS, 4),
                                   table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
         out["secondary"] = sec

@@ -32,7 +32,7 @@ m3_status check_common(const m3_shape* s, bool need_seq) {
   return M3_OK;
 }
 
-// Tokens per chunk: the requested value (or a default of 128 / R rows-worth),
+// Tokens per chunk: the requested value (or a default of 256 / R rows-worth),
 // rounded down to a power of two in [16, 256], then halved until the chunk's
 // rows and angles fit the kernel's register budget and its LDS tiles fit on a
 // compute unit.
@@ -41,7 +41,7 @@ size_t lds_need(int q, const m3_shape& s) {
 }
 
 int choose_chunk(const m3_shape& s) {
-  int q = s.chunk > 0 ? s.chunk : std::max(16, 128 / s.rank);
+  int q = s.chunk > 0 ? s.chunk : std::max(16, 256 / s.rank);
   int p2 = 16;
   while (p2 * 2 <= q && p2 < 256) p2 *= 2;
   q = std::max(16, std::min(p2, 256));

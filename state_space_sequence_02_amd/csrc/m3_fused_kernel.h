@@ -54,6 +54,7 @@ namespace fused {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr unsigned kSpinLimit = 1u << 20;
+constexpr int kMapGroup = 1;        // predecessor maps loaded per round trip
 constexpr int kAngleCap = kFusedAngleCap;   // max Q * N/2 angles per chunk
 
 // Largest number of (token, rank) rows per chunk for state size N (bounds the
@@ -297,34 +298,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     return (k & 1) ? MT - 1 - (wave + 2 * kWaves * pair) : wave + 2 * kWaves * pair;
   };
 
-  // ---- A: scalars and angles ----
+  // ---- A: every global load of the chunk is issued before any of it is used ----
   const float A = p.A[h];
-  float gv = 0.f, wv = 0.f;
-  if (tid < Q) {
-    float lv = 0.f;
-    if (tid < nt) {
-      const size_t tk = tok0 + tid * tstride;
-      const float d = p.dt[tk], lm = p.lam[tk];
-      float dn = 0.f, lmn = 1.f;
-      if (t0 + tid + 1 < p.L) { dn = p.dt[tk + tstride]; lmn = p.lam[tk + tstride]; }
-      lv = d * A;
-      gv = lm * d;
-      wv = gv + (1.f - lmn) * dn;
-    }
-    s_tok[tid] = lv;
+  float dv = 0.f, lmv = 0.f, dnv = 0.f, lmnv = 1.f;
+  if (tid < nt) {
+    const size_t tk = tok0 + tid * tstride;
+    dv = p.dt[tk];
+    lmv = p.lam[tk];
+    if (t0 + tid + 1 < p.L) { dnv = p.dt[tk + tstride]; lmnv = p.lam[tk + tstride]; }
   }
-  if (p.theta) {
-    const float* th = p.theta + tok0 * NH;
-    const int n4 = Q * NH / 4;
-    for (int i = tid; i < n4; i += kThreads) {
-      const int s = (4 * i) / NH, k = (4 * i) - s * NH;
-      const float4 w4 = s < nt ? *reinterpret_cast<const float4*>(th + s * tstride * NH + k)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-      s_cs[4 * i].x = w4.x; s_cs[4 * i + 1].x = w4.y; s_cs[4 * i + 2].x = w4.z; s_cs[4 * i + 3].x = w4.w;
-    }
+  constexpr int TH = kAngleCap / 4 / kThreads;   // float4 angle loads per thread
+  const int n4 = Q * NH / 4;
+  float4 th4[TH];
+#pragma unroll
+  for (int u = 0; u < TH; ++u) {
+    const int i = tid + u * kThreads;
+    const int s = (4 * i) / NH, k = (4 * i) - s * NH;
+    th4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.theta && i < n4 && s < nt)
+      th4[u] = *reinterpret_cast<const float4*>(p.theta + tok0 * NH + s * tstride * NH + k);
   }
-  // B and X rows (first batch) and this wave's C rows are loaded now and
-  // consumed after the angles are known.
+  // B and X rows (first batch) and this wave's C rows: consumed once the
+  // angles are known.
   const int nbi = QRp * (N / 8), nxi = QRp * (P / 8), ntot = nbi + nxi;
   Raw8<T> raw[8];
   auto issue_batch = [&](int base) {
@@ -353,6 +348,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
       raw_zero(craw[k][kn]);
       if (k < ntiles_w && row_a < rows && n0 < N)
         raw_load(craw[k][kn], Cg + (row_a >> LOGR) * rowstepB + (row_a & (R - 1)) * N + n0);
+    }
+  }
+  float gv = 0.f, wv = 0.f;
+  if (tid < Q) {
+    gv = lmv * dv;
+    wv = gv + (1.f - lmnv) * dnv;
+    s_tok[tid] = dv * A;
+  }
+  if (p.theta) {
+#pragma unroll
+    for (int u = 0; u < TH; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < n4) {
+        s_cs[4 * i].x = th4[u].x; s_cs[4 * i + 1].x = th4[u].y;
+        s_cs[4 * i + 2].x = th4[u].z; s_cs[4 * i + 3].x = th4[u].w;
+      }
     }
   }
   __syncthreads();
@@ -511,12 +522,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   // ---- D: S_in by look-back; S_out = a R(Psi) S_in + U ----
   float FA = 1.f;
   float2 Fpsi[NPW][2];
-  f32x4 FU[NPW][PTW], sin_[NPW][PTW];
+  // FU: the composed maps' additive part; once the chain ends it holds S_in
+  f32x4 FU[NPW][PTW];
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
     Fpsi[i][0] = Fpsi[i][1] = make_float2(1.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < PTW; ++j) { FU[i][j] = zero4(); sin_[i][j] = zero4(); }
+    for (int j = 0; j < PTW; ++j) FU[i][j] = zero4();
   }
   bool chain_ok = true;
   if (c == 0) {
@@ -541,29 +553,44 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
               for (int r = 0; r < R; ++r) acc += to_f(Bp[r * N + n0 + e]) * to_f(xp[r * P + pc]);
               v += kappa0 * acc;
             }
-            sin_[i][j][e] = v;
+            FU[i][j][e] = v;
           }
         }
       }
     }
   } else {
-    int j = c - 1;
+    // Wave 0 polls the flags of up to 64 predecessors at once (lane k: chunk
+    // hi - k).  The nearest published state ends the walk once every chunk
+    // after it has published at least its map; a chunk with neither is waited
+    // for.  Maps are then loaded together and composed newest first:
+    // F <- F o f_j, i.e. FU += FA R(Fpsi) U_j, Fpsi <- Fpsi + Psi_j, FA <- FA a_j.
+    int hi = c - 1;
     while (true) {
-      if (tid == 0) {
-        unsigned f, spins = 0;
-        while ((f = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
+      if (wave == 0) {
+        const int W = min(hi + 1, 64);
+        unsigned spins = 0;
+        int nmap = 0, state = 0;
+        while (true) {
+          const unsigned f = lane < W ? __hip_atomic_load(flags + hi - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+          const unsigned long long m2 = __ballot(lane < W && f == 2u);
+          const unsigned long long m0 = __ballot(lane < W && f == 0u);
+          const int k2 = m2 ? __builtin_ctzll(m2) : W;    // nearest state (W: none in window)
+          const int k0 = m0 ? __builtin_ctzll(m0) : 64;   // nearest chunk with nothing yet
+          if (k0 > k2 || (k2 == W && k0 >= W)) { nmap = k2; state = k2 < W; break; }
+          if (k0 > 0) { nmap = k0; state = 0; break; }   // compose what is there, then wait
           __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) break;
+          if (++spins > kSpinLimit) { nmap = -1; break; }
         }
-        s_misc[1] = (int)f;
+        if (lane == 0) { s_misc[1] = nmap; s_misc[5] = state; }
       }
       __syncthreads();
-      const int f = s_misc[1];
+      const int nmap = s_misc[1], state = s_misc[5];
       __syncthreads();
-      if (f == 0) { chain_ok = false; break; }
-      const size_t jid = (size_t)bh * p.nc + j;
-      if (f == 2) {
-        const float* S = p.states + jid * slot;
+      if (nmap < 0) { chain_ok = false; break; }
+      // the state (if any) is loaded alongside the maps
+      float2 sx[NPW][PTW][2];
+      if (state) {
+        const float* S = p.states + ((size_t)bh * p.nc + hi - nmap) * slot;
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
           const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
@@ -572,44 +599,75 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
             const int pt = pslot + WPN * jj;
             if (pt < TPt) {
               const float* q = S + (size_t)(pt * 16 + l16) * N + n0;
-              const float2 x01 = ld_dev2(q), x23 = ld_dev2(q + 2);
-              f32x4 s4;
-              s4[0] = FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y) + FU[i][jj][0];
-              s4[1] = FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y) + FU[i][jj][1];
-              s4[2] = FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y) + FU[i][jj][2];
-              s4[3] = FA * (Fpsi[i][1].y * x23.x + Fpsi[i][1].x * x23.y) + FU[i][jj][3];
-              sin_[i][jj] = s4;
+              sx[i][jj][0] = ld_dev2(q);
+              sx[i][jj][1] = ld_dev2(q + 2);
             }
           }
         }
-        break;
       }
-      // f == 1: F <- F o f_j
-      const float* U = p.maps + jid * slot;
-      const float* rec = p.recs + jid * (2 * NH + 2);
-      const float aj = ld_dev2(rec).x;
+      for (int m0 = 0; m0 < nmap; m0 += kMapGroup) {
+        float2 ux[kMapGroup][NPW][PTW][2], rx[kMapGroup][NPW][2];
+        float ax[kMapGroup];
 #pragma unroll
-      for (int i = 0; i < NPW; ++i) {
-        const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
-        const float2 r0 = ld_dev2(rec + 2 + n0), r1 = ld_dev2(rec + 2 + n0 + 2);
+        for (int g = 0; g < kMapGroup; ++g) {
+          if (m0 + g < nmap) {
+            const size_t jid = (size_t)bh * p.nc + hi - m0 - g;
+            const float* U = p.maps + jid * slot;
+            const float* rec = p.recs + jid * (2 * NH + 2);
+            ax[g] = ld_dev2(rec).x;
 #pragma unroll
-        for (int jj = 0; jj < PTW; ++jj) {
-          const int pt = pslot + WPN * jj;
-          if (pt < TPt) {
-            const float* q = U + (size_t)(pt * 16 + l16) * N + n0;
-            const float2 x01 = ld_dev2(q), x23 = ld_dev2(q + 2);
+            for (int i = 0; i < NPW; ++i) {
+              const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+              rx[g][i][0] = ld_dev2(rec + 2 + n0);
+              rx[g][i][1] = ld_dev2(rec + 2 + n0 + 2);
+#pragma unroll
+              for (int jj = 0; jj < PTW; ++jj) {
+                const int pt = pslot + WPN * jj;
+                if (pt < TPt) {
+                  const float* q = U + (size_t)(pt * 16 + l16) * N + n0;
+                  ux[g][i][jj][0] = ld_dev2(q);
+                  ux[g][i][jj][1] = ld_dev2(q + 2);
+                }
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < kMapGroup; ++g) {
+          if (m0 + g < nmap) {
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) {
+#pragma unroll
+              for (int jj = 0; jj < PTW; ++jj) {
+                const float2 x01 = ux[g][i][jj][0], x23 = ux[g][i][jj][1];
+                FU[i][jj][0] += FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y);
+                FU[i][jj][1] += FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y);
+                FU[i][jj][2] += FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y);
+                FU[i][jj][3] += FA * (Fpsi[i][1].y * x23.x + Fpsi[i][1].x * x23.y);
+              }
+              const float2 a0 = Fpsi[i][0], a1 = Fpsi[i][1], r0 = rx[g][i][0], r1 = rx[g][i][1];
+              Fpsi[i][0] = make_float2(a0.x * r0.x - a0.y * r0.y, a0.y * r0.x + a0.x * r0.y);
+              Fpsi[i][1] = make_float2(a1.x * r1.x - a1.y * r1.y, a1.y * r1.x + a1.x * r1.y);
+            }
+            FA *= ax[g];
+          }
+        }
+      }
+      if (state) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+#pragma unroll
+          for (int jj = 0; jj < PTW; ++jj) {
+            const float2 x01 = sx[i][jj][0], x23 = sx[i][jj][1];
             FU[i][jj][0] += FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y);
             FU[i][jj][1] += FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y);
             FU[i][jj][2] += FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y);
             FU[i][jj][3] += FA * (Fpsi[i][1].y * x23.x + Fpsi[i][1].x * x23.y);
           }
         }
-        const float2 a0 = Fpsi[i][0], a1 = Fpsi[i][1];
-        Fpsi[i][0] = make_float2(a0.x * r0.x - a0.y * r0.y, a0.y * r0.x + a0.x * r0.y);
-        Fpsi[i][1] = make_float2(a1.x * r1.x - a1.y * r1.y, a1.y * r1.x + a1.x * r1.y);
+        break;
       }
-      FA *= aj;
-      --j;
+      hi -= nmap;
     }
   }
   const float nanv = __builtin_nanf("");
@@ -623,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
       const int pt = pslot + WPN * j;
       if (pt < TPt) {
         const int pc = pt * 16 + l16;
-        f32x4 si = sin_[i][j];
+        f32x4 si = FU[i][j];
         if (!chain_ok) si[0] = si[1] = si[2] = si[3] = nanv;
         T* hd = s_H + pc * NS + n0;
         hd[0] = from_f<T>(si[0]); hd[1] = from_f<T>(si[1]); hd[2] = from_f<T>(si[2]); hd[3] = from_f<T>(si[3]);
