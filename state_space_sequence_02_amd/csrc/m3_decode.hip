@@ -12,16 +12,135 @@
 // lanes take consecutive quads of the same row pair, so every load/store
 // instruction covers whole 16-byte-aligned runs of a row.  The rotation of a
 // pair is lane-local because both of its rows sit in the same unit.
-// All small per-token operands (B, C, B_prev, x, x_prev, cos/sin) are staged in
-// LDS as fp32 first; the readout Y = H^T C is reduced across lanes that share a
-// quad (xor shuffles within the wave, then LDS across waves).
+// The coefficients are folded into the small operands once per workgroup:
+//   H <- [alpha R(phi)] H + sum_r (beta R(phi) B_prev)[:, r] x_prev[r]^T + (gamma B)[:, r] x[r]^T
+// so each state element costs one 2x2 rotation and one 2R-long FMA chain.  The
+// small operands are staged in LDS as fp32; the readout Y = H^T C is reduced
+// across lanes that share a quad (xor shuffles within the wave, then LDS
+// across waves).
 #include "m3_device.h"
 
 namespace m3 {
 namespace {
 
+// Raw 8-element loads (bf16: one 16-byte load; fp32: two).
+template <typename T> struct Raw;
+template <> struct Raw<bf16> { uint4 v[1]; };
+template <> struct Raw<float> { uint4 v[2]; };
+__device__ __forceinline__ void raw_zero(Raw<bf16>& r) { r.v[0] = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void raw_zero(Raw<float>& r) { r.v[0] = r.v[1] = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void raw_load(Raw<bf16>& r, const bf16* p) { r.v[0] = *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void raw_load(Raw<float>& r, const float* p) {
+  r.v[0] = *reinterpret_cast<const uint4*>(p);
+  r.v[1] = *reinterpret_cast<const uint4*>(p + 4);
+}
+__device__ __forceinline__ void raw_unpack(const Raw<bf16>& r, float (&v)[8]) {
+  const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void raw_unpack(const Raw<float>& r, float (&v)[8]) {
+  v[0] = __uint_as_float(r.v[0].x); v[1] = __uint_as_float(r.v[0].y);
+  v[2] = __uint_as_float(r.v[0].z); v[3] = __uint_as_float(r.v[0].w);
+  v[4] = __uint_as_float(r.v[1].x); v[5] = __uint_as_float(r.v[1].y);
+  v[6] = __uint_as_float(r.v[1].z); v[7] = __uint_as_float(r.v[1].w);
+}
+
+// The small per-token operands of one (sequence, head), as 8-element items:
+// [B | C | B_prev] (R*N/8 items each), [x | x_prev] (R*P/8 each), then the
+// angles (4 per item).  A NULL source reads as zeros.  A B_prev item also
+// carries the angles of its 4 row pairs (it is rotated when staged).
+// (Pointers are passed one by one: a struct of them selected by a run-time
+// index would be placed in private memory.)
+template <typename T>
+struct Item { Raw<T> raw; uint4 th; bool ok, tok; };   // masks applied when staged
+
+// Branch-free on purpose: every item issues its loads unconditionally from a
+// clamped address (B stands in for a missing source) and masks the result, so
+// the compiler need not wait for a load at a control-flow merge and the state
+// loads issued after these stay in flight.
+__device__ __forceinline__ uint4 mask4(uint4 v, bool ok) {
+  const uint32_t m = ok ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+template <typename T>
+__device__ __forceinline__ Item<T> load_item(const T* B, const T* C, const T* Bp, const T* X,
+                                             const T* Xp, const float* theta, int N,
+                                             int nb8, int nx8, int nitems, int i) {
+  const int nbB = 3 * nb8, nbX = nbB + 2 * nx8;
+  const bool isB = i < nbB, isX = !isB && i < nbX, isT = !isB && !isX && i < nitems;
+  const int wb = isB ? i / nb8 : 0;
+  const int wx = isX ? (i - nbB) / nx8 : 0;
+  const int j = isB ? i - wb * nb8 : (isX ? i - nbB - wx * nx8 : 0);
+  const T* src = isB ? (wb == 0 ? B : (wb == 1 ? C : Bp)) : (wx == 0 ? X : Xp);
+  const bool ok = (isB || isX) && src != nullptr;
+  Item<T> it;
+  raw_load(it.raw, ok ? src + 8 * j : B);
+  // angles: the 4 row pairs of a B_prev item, or an angle item
+  const bool tb = isB && wb == 2 && src != nullptr && theta != nullptr;
+  const bool tok = tb || (isT && theta != nullptr);
+  const int toff = tb ? (8 * j - ((8 * j) / N) * N) / 2 : 4 * (i - nbX);
+  it.th = *reinterpret_cast<const uint4*>(tok ? theta + toff : reinterpret_cast<const float*>(B));
+  it.ok = ok;
+  it.tok = tok;
+  return it;
+}
+
+// Widens an item to fp32 into LDS:
+//   sW [N][2R]: (beta R(phi) B_prev) in slots 0..R-1, (gamma B) in R..2R-1
+//   sC [N][R], sXX [2R][P]: x_prev rows then x rows, sCS [N/2]: alpha (cos, sin).
+template <typename T, int R>
+__device__ __forceinline__ void stage_item(float* sW, float* sC, float* sXX, float2* sCS,
+                                           int N, int P, int nb8, int nx8, int nitems,
+                                           float alpha, float beta, float gamma,
+                                           int i, const Item<T>& it) {
+  Raw<T> raw = it.raw;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(raw.v) / sizeof(uint4)); ++k) raw.v[k] = mask4(raw.v[k], it.ok);
+  const uint4 tm = mask4(it.th, it.tok);
+  const float4 th = make_float4(__uint_as_float(tm.x), __uint_as_float(tm.y), __uint_as_float(tm.z), __uint_as_float(tm.w));
+  float v[8];
+  raw_unpack(raw, v);
+  if (i < 3 * nb8) {
+    const int which = i / nb8, j = i - which * nb8;
+    const int rr = (8 * j) / N, n0 = 8 * j - rr * N;
+    if (which == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sW[(n0 + e) * 2 * R + R + rr] = gamma * v[e];
+    } else if (which == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sC[(n0 + e) * R + rr] = v[e];
+    } else {
+      const float a[4] = {th.x, th.y, th.z, th.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = __cosf(a[e]), sn = __sinf(a[e]);
+        const float u = v[2 * e], w = v[2 * e + 1];
+        sW[(n0 + 2 * e) * 2 * R + rr] = beta * (c * u - sn * w);
+        sW[(n0 + 2 * e + 1) * 2 * R + rr] = beta * (sn * u + c * w);
+      }
+    }
+  } else if (i < 3 * nb8 + 2 * nx8) {
+    const int k = i - 3 * nb8;
+    const int which = k / nx8, j = k - which * nx8;
+    const int rr = (8 * j) / P, p0 = 8 * j - rr * P;
+    float* dst = sXX + (which == 0 ? R + rr : rr) * P + p0;
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else if (i < nitems) {
+    const int j = i - 3 * nb8 - 2 * nx8;
+    const float a[4] = {th.x, th.y, th.z, th.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sCS[4 * j + e] = make_float2(alpha * __cosf(a[e]), alpha * __sinf(a[e]));
+  }
+}
+
 template <typename T, int R, int UPT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
   const int bh = blockIdx.x;
   const int h_idx = bh % p.H;
   const int N = p.N, P = p.P;
@@ -31,65 +150,56 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int lane = tid & 63, wave = tid >> 6, nwaves = NT >> 6;
 
   extern __shared__ float smem[];
-  float* sB = smem;                      // [N][R]  current B, pair-friendly layout
-  float* sC = sB + N * R;                // [N][R]
-  float* sBp = sC + N * R;               // [N][R]  previous B
-  float* sX = sBp + N * R;               // [R][P]
-  float* sXp = sX + R * P;               // [R][P]
-  float2* sCS = reinterpret_cast<float2*>(sXp + R * P);     // [N/2] cos, sin
-  float* sRed = reinterpret_cast<float*>(sCS + (N >> 1));   // [nwaves][R][P]
+  float* sW = smem;                      // [N][2R]
+  float* sC = sW + 2 * N * R;            // [N][R]
+  float* sXX = sC + N * R;               // [2R][P]
+  float2* sCS = reinterpret_cast<float2*>(sXX + 2 * R * P);   // [N/2]
+  float* sRed = reinterpret_cast<float*>(sCS + (N >> 1));     // [nwaves][R][P]
 
   const int q = tid % QP;                // constant across this thread's units
   const int units = (N >> 1) * QP;
   float* hg = p.h + (size_t)bh * N * P;
-
-  // The state is the only large operand: issue all of this thread's state loads
-  // first, so their latency overlaps the staging of the small per-token
-  // operands below instead of following it.
-  float4 h0v[UPT], h1v[UPT];
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + i * NT;
-    if (u < units) {
-      const int k = u / QP;
-      h0v[i] = ld_stream4(hg + (size_t)(2 * k) * P + 4 * q);
-      h1v[i] = ld_stream4(hg + (size_t)(2 * k + 1) * P + 4 * q);
-    }
-  }
 
   const T* Bg = static_cast<const T*>(p.B) + (size_t)bh * R * N;
   const T* Cg = static_cast<const T*>(p.C) + (size_t)bh * R * N;
   const T* Xg = static_cast<const T*>(p.x) + (size_t)bh * R * P;
   const T* Bpg = p.Bp ? static_cast<const T*>(p.Bp) + (size_t)bh * R * N : nullptr;
   const T* Xpg = p.xp ? static_cast<const T*>(p.xp) + (size_t)bh * R * P : nullptr;
+  const float* thg = p.theta ? p.theta + (size_t)bh * (N >> 1) : nullptr;
 
-  for (int i = tid; i < R * N; i += NT) {
-    const int r = i / N, n = i - r * N;
-    sB[n * R + r] = to_f(Bg[i]);
-    sC[n * R + r] = to_f(Cg[i]);
-    sBp[n * R + r] = Bpg ? to_f(Bpg[i]) : 0.f;
+  // Small operands first (at most two items per thread), then the state.  Loads
+  // complete in order, so the operands are staged into LDS and the barrier is
+  // passed while the state is still in flight.
+  const int nb8 = (R * N) >> 3, nx8 = (R * P) >> 3;
+  const int nth4 = thg ? (N >> 3) : 0;
+  const int nitems = 3 * nb8 + 2 * nx8 + nth4;
+  const float d = p.dt[bh], lm = p.lam[bh], Ah = p.A[h_idx];
+  const Item<T> it0 = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, tid);
+  const Item<T> it1 = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, tid + NT);
+
+  // (unconditional, from a clamped unit: a load under a branch would make the
+  // compiler wait for everything at the merge)
+  float4 h0v[UPT], h1v[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int k = min(tid + i * NT, units - 1) / QP;
+    h0v[i] = ld_stream4(hg + (size_t)(2 * k) * P + 4 * q);
+    h1v[i] = ld_stream4(hg + (size_t)(2 * k + 1) * P + 4 * q);
   }
-  for (int i = tid; i < R * P; i += NT) {
-    sX[i] = to_f(Xg[i]);
-    sXp[i] = Xpg ? to_f(Xpg[i]) : 0.f;
-  }
-  for (int k = tid; k < (N >> 1); k += NT) {
-    float c = 1.f, s = 0.f;
-    if (p.theta) sincosf(p.theta[(size_t)bh * (N >> 1) + k], &s, &c);
-    sCS[k] = make_float2(c, s);
-  }
-  const float d = p.dt[bh], lm = p.lam[bh];
-  const float alpha = __expf(d * p.A[h_idx]);
+
+  const float alpha = __expf(d * Ah);
   const float beta = (1.f - lm) * d * alpha;
   const float gamma = lm * d;
+  stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, tid, it0);
+  stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, tid + NT, it1);
+  // large shapes (more than two items per thread): the rest, loaded and staged here
+  for (int i = tid + 2 * NT; i < nitems; i += NT)
+    stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, i,
+                     load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, i));
+  if (!thg)
+    for (int k = tid; k < (N >> 1); k += NT) sCS[k] = make_float2(alpha, 0.f);
   __syncthreads();
 
-  float4 xr[R], xpr[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    xr[r] = *reinterpret_cast<const float4*>(sX + r * P + 4 * q);
-    xpr[r] = *reinterpret_cast<const float4*>(sXp + r * P + 4 * q);
-  }
   float4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -99,30 +209,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const int u = tid + i * NT;
     if (u < units) {
       const int k = u / QP;
-      const float* b0 = sB + (2 * k) * R;  const float* b1 = b0 + R;
-      const float* p0 = sBp + (2 * k) * R; const float* p1 = p0 + R;
-      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0, w0 = v0, w1 = v0;
+      const float2 cs = sCS[k];          // alpha (cos, sin) of pair k
+      const float4 a = h0v[i], b = h1v[i];
+      float4 n0, n1;
+      n0.x = cs.x * a.x - cs.y * b.x; n1.x = cs.y * a.x + cs.x * b.x;
+      n0.y = cs.x * a.y - cs.y * b.y; n1.y = cs.y * a.y + cs.x * b.y;
+      n0.z = cs.x * a.z - cs.y * b.z; n1.z = cs.y * a.z + cs.x * b.z;
+      n0.w = cs.x * a.w - cs.y * b.w; n1.w = cs.y * a.w + cs.x * b.w;
+      const float* w0 = sW + (2 * k) * 2 * R;
+      const float* w1 = w0 + 2 * R;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        // previous write rows 2k, 2k+1 and current write rows 2k, 2k+1
-        w0.x += p0[r] * xpr[r].x; w0.y += p0[r] * xpr[r].y; w0.z += p0[r] * xpr[r].z; w0.w += p0[r] * xpr[r].w;
-        w1.x += p1[r] * xpr[r].x; w1.y += p1[r] * xpr[r].y; w1.z += p1[r] * xpr[r].z; w1.w += p1[r] * xpr[r].w;
-        v0.x += b0[r] * xr[r].x;  v0.y += b0[r] * xr[r].y;  v0.z += b0[r] * xr[r].z;  v0.w += b0[r] * xr[r].w;
-        v1.x += b1[r] * xr[r].x;  v1.y += b1[r] * xr[r].y;  v1.z += b1[r] * xr[r].z;  v1.w += b1[r] * xr[r].w;
+      for (int j = 0; j < 2 * R; ++j) {
+        // x_prev / x columns 4q..4q+3 are re-read from LDS per unit (same address
+        // across the lanes of a quad; keeps them out of the register budget)
+        const float4 xx = *reinterpret_cast<const float4*>(sXX + j * P + 4 * q);
+        const float c0 = w0[j], c1 = w1[j];
+        n0.x += c0 * xx.x; n0.y += c0 * xx.y; n0.z += c0 * xx.z; n0.w += c0 * xx.w;
+        n1.x += c1 * xx.x; n1.y += c1 * xx.y; n1.z += c1 * xx.z; n1.w += c1 * xx.w;
       }
-      const float2 cs = sCS[k];
-      float4 a0, a1, n0, n1;
-      a0.x = alpha * h0v[i].x + beta * w0.x; a0.y = alpha * h0v[i].y + beta * w0.y;
-      a0.z = alpha * h0v[i].z + beta * w0.z; a0.w = alpha * h0v[i].w + beta * w0.w;
-      a1.x = alpha * h1v[i].x + beta * w1.x; a1.y = alpha * h1v[i].y + beta * w1.y;
-      a1.z = alpha * h1v[i].z + beta * w1.z; a1.w = alpha * h1v[i].w + beta * w1.w;
-      n0.x = cs.x * a0.x - cs.y * a1.x + gamma * v0.x; n1.x = cs.y * a0.x + cs.x * a1.x + gamma * v1.x;
-      n0.y = cs.x * a0.y - cs.y * a1.y + gamma * v0.y; n1.y = cs.y * a0.y + cs.x * a1.y + gamma * v1.y;
-      n0.z = cs.x * a0.z - cs.y * a1.z + gamma * v0.z; n1.z = cs.y * a0.z + cs.x * a1.z + gamma * v1.z;
-      n0.w = cs.x * a0.w - cs.y * a1.w + gamma * v0.w; n1.w = cs.y * a0.w + cs.x * a1.w + gamma * v1.w;
       st_stream4(hg + (size_t)(2 * k) * P + 4 * q, n0);
       st_stream4(hg + (size_t)(2 * k + 1) * P + 4 * q, n1);
-      const float* c0 = sC + (2 * k) * R; const float* c1 = c0 + R;
+      const float* c0 = sC + (2 * k) * R;
+      const float* c1 = c0 + R;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         acc[r].x += n0.x * c0[r] + n1.x * c1[r];
@@ -160,11 +268,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 template <typename T, int R>
 hipError_t dispatch_upt(const DecodeParams& p, hipStream_t stream) {
   const int units = (p.N / 2) * (p.P / 4);
-  const int nt = units >= 256 ? 256 : (units <= 64 ? 64 : ((units + 63) / 64) * 64);
+  const int nt = units >= 512 ? 512 : (units <= 64 ? 64 : ((units + 63) / 64) * 64);
   const int upt = (units + nt - 1) / nt;
   const int nwaves = nt / 64;
   const size_t lds = sizeof(float) * (3 * (size_t)p.N * R + 2 * (size_t)R * p.P + p.N +
-                                      (size_t)nwaves * R * p.P);
+                                      (size_t)nwaves * R * p.P);   // sW, sC, sXX, sCS, sRed
   const dim3 grid(p.batch * p.H), block(nt);
   switch (upt) {
     case 1: hipLaunchKernelGGL((decode_kernel<T, R, 1>), grid, block, lds, stream, p); break;
