@@ -35,13 +35,24 @@
 // write-back/invalidate and no workgroup barrier is needed to publish.
 //
 // Work order inside a workgroup:
-//   A  scalars (dt, lam -> l, weights per row) and angles (-> cos/sin Phi table)
-//   B  stage B~ (rotated) and X row-major in LDS (one batch of loads per thread)
+//   A  all global loads issued; chunk-local cumulative log decay and phases:
+//      each thread scans its own tokens in registers, lanes combine with
+//      shuffles, waves with one barrier; cos/sin table of Phi in LDS
+//   B  stage B~ (rotated) and X in LDS; the wave's C~ rows are kept in
+//      registers as MFMA operands
 //   C  U = R(Psi) sum_s W_s B~_s^T X_s on MFMA (operands by LDS transpose reads);
 //      publish the map if needed
 //   D  look back for S_in; S_out = a R(Psi) S_in + U; stores issued
-//   E  outputs per 16-row tile: C~ S_in and the masked intra-chunk products on
-//      MFMA; y stored; after the first tile, flag 2 raised
+//   E  outputs of the wave's 16-row tiles, together: C~ S_in, then per 32-row
+//      source block the masked intra-chunk products on MFMA (each B~ / X read
+//      serves every tile of the wave); flag 2 raised; y stored.
+//
+// Column order: X is staged in LDS with its columns permuted so that the
+// 16-column MFMA tile pt holds head columns TPt*l + pt (l = 0..15, TPt = P/16).
+// U, the chunk states in the workspace, S_in^T and the output accumulators all
+// follow that order; a lane then holds TPt consecutive head columns of each of
+// its output rows, and y leaves as full row segments.  h0, h_out, x_prev and y
+// are read/written in the head's own column order.
 #pragma once
 
 #include <algorithm>
@@ -65,26 +76,29 @@ __host__ __device__ inline int round_up_i(int a, int b) { return (a + b - 1) / b
 __host__ __device__ inline size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 
 struct Lds {
-  size_t row, rw, csH, B, X, misc, total;
-  size_t tok, seg;   // aliases inside B (used only before B~ is staged)
+  size_t row, rw, W, csH, B, X, misc, total;
+  size_t segl, sega;   // scan scratch, inside B (used only before B~ is staged)
 };
 // row: per (token, rank) row float4 {l, w, gamma, W}
-// rw: per row float2 {w, gamma} x exp(l_be - l) with be the last row of the row's
-//     32-row block (the factored decay of the off-diagonal mask blocks)
-// csH: cos/sin of Phi [Q][N/2] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8]
-// B: B~ [QRp][N+8];  X: X [QRp][P+8];  tok (Q floats) and seg (512 floats) live in B's space
+// rw: per row exp(l_be - l) w with be the last row of the row's 32-row block
+//     (the factored decay of the off-diagonal mask blocks);  W: per row W
+// csH: cos/sin of Phi [Q][N/2 + 4] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8]
+// B: B~ [QRp][N+8];  X: X [QRp][P+8] (permuted columns)
+// segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
 __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize) {
   const int QRp = round_up_i(Q * R, 32);
+  const size_t scan = sizeof(float) * kWaves + sizeof(float4) * (size_t)kWaves * (N / 8);
   Lds o;
   o.row = 0;
   o.rw = o.row + sizeof(float4) * QRp;
-  o.csH = o.rw + sizeof(float2) * QRp;
-  o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2), (size_t)esize * P * (N + 8)), 16);
-  o.X = o.B + max_sz((size_t)esize * QRp * (N + 8), sizeof(float) * ((size_t)Q + 512));
+  o.W = o.rw + sizeof(float) * QRp;
+  o.csH = o.W + sizeof(float) * QRp;
+  o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2 + 4), (size_t)esize * P * (N + 8)), 16);
+  o.X = o.B + round_up_i((int)max_sz((size_t)esize * QRp * (N + 8), scan), 16);
   o.misc = o.X + (size_t)esize * QRp * (P + 8);
   o.total = o.misc + 32;
-  o.tok = o.B;
-  o.seg = o.B + sizeof(float) * Q;
+  o.segl = o.B;
+  o.sega = o.B + sizeof(float) * kWaves;
   return o;
 }
 
@@ -195,50 +209,55 @@ __device__ __forceinline__ void frag_tr(Frag<float>& f, const float* base, int s
   }
 }
 
-// Inclusive scan of a[0..n) (n <= 512) in LDS by the 8 waves; tmp holds 8 floats.
-__device__ inline void block_scan(float* a, int n, float* tmp) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float v = tid < n ? a[tid] : 0.f;
+// Stores the 8 head columns c0..c0+7 of one X row into the permuted LDS row:
+// head column c goes to LDS column (c % TPt) * 16 + c / TPt.
+template <int TPt, typename T>
+__device__ __forceinline__ void store_x_permuted(T* row, int c0, const Raw8<T>& r) {
+  T v[8];
+  static_assert(sizeof(Raw8<T>) == sizeof(v), "raw size");
+  __builtin_memcpy(v, &r, sizeof(v));
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float u = __shfl_up(v, off);
-    if (lane >= off) v += u;
+  for (int t = 0; t < (TPt < 8 ? TPt : 8); ++t) {
+    T* d = row + t * 16 + c0 / TPt;
+#pragma unroll
+    for (int m = 0; m < 8 / TPt; ++m) d[m] = v[t + m * TPt];
   }
-  if (lane == 63) tmp[wave] = v;
-  __syncthreads();
-  float base = 0.f;
-  for (int w = 0; w < wave; ++w) base += tmp[w];
-  if (tid < n) a[tid] = v + base;
-  __syncthreads();
 }
 
-// Inclusive scan along tokens of a [Q][NH] table (the .x of float2 entries).
-__device__ inline void column_scan(float2* t, int Q, int NH, float* segtot) {
-  const int tid = threadIdx.x;
-  const int S = min(kThreads / NH, Q);
-  const int len = Q / S;
-  const int k = tid % NH, sg = tid / NH;
-  const bool act = sg < S;
-  float run = 0.f;
-  if (act) {
-    for (int s = sg * len; s < (sg + 1) * len; ++s) {
-      run += t[s * NH + k].x;
-      t[s * NH + k].x = run;
+// Stores n (= TPt) consecutive outputs of one row.
+template <typename T, int TPt>
+__device__ __forceinline__ void store_row(T* d, const float (&v)[TPt]) {
+  if constexpr (sizeof(T) == 2 && TPt % 2 == 0) {
+    uint32_t w[TPt / 2];
+#pragma unroll
+    for (int i = 0; i < TPt / 2; ++i) {
+      const bf16 lo = static_cast<bf16>(v[2 * i]), hi = static_cast<bf16>(v[2 * i + 1]);
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    segtot[sg * NH + k] = run;
+    if constexpr (TPt == 2) *reinterpret_cast<uint32_t*>(d) = w[0];
+    else if constexpr (TPt == 4) *reinterpret_cast<uint2*>(d) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint4*>(d) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (sizeof(T) == 4 && TPt % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < TPt / 4; ++i)
+      reinterpret_cast<float4*>(d)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPt; ++i) d[i] = from_f<T>(v[i]);
   }
-  __syncthreads();
-  if (act && sg > 0) {
-    float base = 0.f;
-    for (int j = 0; j < sg; ++j) base += segtot[j * NH + k];
-    for (int s = sg * len; s < (sg + 1) * len; ++s) t[s * NH + k].x += base;
-  }
-  __syncthreads();
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+__device__ __forceinline__ float4 sub4(float4 a, float4 b) { return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w); }
+__device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
+  return make_float4(__shfl_up(v.x, off), __shfl_up(v.y, off), __shfl_up(v.z, off), __shfl_up(v.w, off));
 }
 
 template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   constexpr int NH = N / 2;
+  constexpr int NG = NH / 4;                  // 4-pair column groups of the angle table
+  constexpr int CSS = NH + 4;                 // angle table row stride (float2): rows 32 B apart in banks
   constexpr int NK = (N + 31) / 32;           // 32-wide slices of the state dimension
   constexpr int TPt = P / 16;                 // 16-column tiles of the head dimension
   constexpr int TNt = N / 16;                 // 16-row tiles of the state dimension
@@ -250,23 +269,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   constexpr int NS = N + 8;                   // LDS row stride of B~ and S_in^T
   constexpr int XS = P + 8;                   // LDS row stride of X
   constexpr int LOGR = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;
+  constexpr int RTW = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;   // max output row tiles per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int nslot = wave % NGRP, pslot = wave / NGRP;
+  // head column held by lane l16 in 16-column tile pt (the permuted order)
+  auto hcol = [&](int pt) { return l16 * TPt + pt; };
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int Q = p.Q;
   const Lds lay = lds_layout(Q, R, N, P, sizeof(T));
   float4* s_row = reinterpret_cast<float4*>(smem + lay.row);
-  float2* s_rw = reinterpret_cast<float2*>(smem + lay.rw);
-  float* s_tok = reinterpret_cast<float*>(smem + lay.tok);
-  float* s_seg = reinterpret_cast<float*>(smem + lay.seg);
+  float* s_rw = reinterpret_cast<float*>(smem + lay.rw);
+  float* s_W = reinterpret_cast<float*>(smem + lay.W);
+  float* s_segl = reinterpret_cast<float*>(smem + lay.segl);
+  float4* s_sega = reinterpret_cast<float4*>(smem + lay.sega);
   float2* s_cs = reinterpret_cast<float2*>(smem + lay.csH);
   T* s_H = reinterpret_cast<T*>(smem + lay.csH);
   T* s_B = reinterpret_cast<T*>(smem + lay.B);
   T* s_X = reinterpret_cast<T*>(smem + lay.X);
   int* s_misc = reinterpret_cast<int*>(smem + lay.misc);
-  constexpr int RTW = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;   // max output row tiles per wave
 
   // ---- ticket: chunk-major order over all sequences ----
   if (tid == 0) {
@@ -299,123 +321,172 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   };
 
   // ---- A: every global load of the chunk is issued before any of it is used ----
+  // Loads are unconditional, from clamped (valid) addresses, and out-of-range
+  // values are masked only when consumed: a load under a branch merged with a
+  // default value makes the compiler wait for it at the merge, which would
+  // serialise the whole batch.
   const float A = p.A[h];
-  float dv = 0.f, lmv = 0.f, dnv = 0.f, lmnv = 1.f;
-  if (tid < nt) {
-    const size_t tk = tok0 + tid * tstride;
-    dv = p.dt[tk];
-    lmv = p.lam[tk];
-    if (t0 + tid + 1 < p.L) { dnv = p.dt[tk + tstride]; lmnv = p.lam[tk + tstride]; }
-  }
-  constexpr int TH = kAngleCap / 4 / kThreads;   // float4 angle loads per thread
-  const int n4 = Q * NH / 4;
-  float4 th4[TH];
+  const int tq = min(tid, nt - 1);
+  const size_t tk = tok0 + tq * tstride;
+  const size_t tkn = tok_index(p, b, min(t0 + tq + 1, p.L - 1), h);
+  const float dv_raw = p.dt[tk], lmv_raw = p.lam[tk];
+  const float dnv_raw = p.dt[tkn], lmnv_raw = p.lam[tkn];
+  // angles: thread -> (segment sg, column group cg): tokens sg*ALEN .. +ALEN-1,
+  // pairs 4cg .. 4cg+3 (ALEN <= 4 since Q * N/2 <= kAngleCap)
+  const int NSEG = min(kThreads / NG, Q);
+  const int ALEN = Q / NSEG;
+  const int cg = tid % NG, sg = tid / NG;
+  float4 th4[4];
+  unsigned th_ok = 0;
 #pragma unroll
-  for (int u = 0; u < TH; ++u) {
-    const int i = tid + u * kThreads;
-    const int s = (4 * i) / NH, k = (4 * i) - s * NH;
-    th4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.theta && i < n4 && s < nt)
-      th4[u] = *reinterpret_cast<const float4*>(p.theta + tok0 * NH + s * tstride * NH + k);
+  for (int j = 0; j < 4; ++j) {
+    const int s = sg * ALEN + j;
+    const bool ok = p.theta && j < ALEN && sg < NSEG && s < nt;
+    th_ok |= ok ? 1u << j : 0u;
+    const float* src = ok ? p.theta + (tok0 + s * tstride) * NH + 4 * cg : p.dt + tok0;
+    th4[j] = *reinterpret_cast<const float4*>(src);
   }
   // B and X rows (first batch) and this wave's C rows: consumed once the
   // angles are known.
   const int nbi = QRp * (N / 8), nxi = QRp * (P / 8), ntot = nbi + nxi;
   Raw8<T> raw[8];
+  unsigned raw_ok = 0;
   auto issue_batch = [&](int base) {
+    raw_ok = 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = base + u * kThreads;
-      raw_zero(raw[u]);
-      if (i < nbi) {
-        const int row = i / (N / 8), ng = i - row * (N / 8);
-        if (row < rows) raw_load(raw[u], Bg + (row >> LOGR) * rowstepB + (row & (R - 1)) * N + ng * 8);
-      } else if (i < ntot) {
-        const int j = i - nbi;
-        const int row = j / (P / 8), pg = j - row * (P / 8);
-        if (row < rows) raw_load(raw[u], Xg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + pg * 8);
-      }
+      const bool isb = i < nbi;
+      const int j = isb ? i : i - nbi;
+      const int row = isb ? i / (N / 8) : j / (P / 8);
+      const int g = isb ? i - row * (N / 8) : j - row * (P / 8);
+      const bool ok = i < ntot && row < rows;
+      const T* src = isb ? Bg + (row >> LOGR) * rowstepB + (row & (R - 1)) * N + g * 8
+                         : Xg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + g * 8;
+      raw_ok |= ok ? 1u << u : 0u;
+      raw_load(raw[u], ok ? src : Bg);
     }
   };
   issue_batch(tid);
   Raw8<T> craw[RTW][NK];
+  unsigned craw_ok = 0;
 #pragma unroll
   for (int k = 0; k < RTW; ++k) {
     const int row_a = (k < ntiles_w ? tile_of(k) : 0) * 16 + l16;
 #pragma unroll
     for (int kn = 0; kn < NK; ++kn) {
       const int n0 = kn * 32 + 8 * g4;
-      raw_zero(craw[k][kn]);
-      if (k < ntiles_w && row_a < rows && n0 < N)
-        raw_load(craw[k][kn], Cg + (row_a >> LOGR) * rowstepB + (row_a & (R - 1)) * N + n0);
+      const bool ok = k < ntiles_w && row_a < rows && n0 < N;
+      craw_ok |= ok ? 1u << (k * NK + kn) : 0u;
+      raw_load(craw[k][kn], ok ? Cg + (row_a >> LOGR) * rowstepB + (row_a & (R - 1)) * N + n0 : Cg);
     }
   }
-  float gv = 0.f, wv = 0.f;
+  const bool tok_ok = tid < nt;
+  const float dv = tok_ok ? dv_raw : 0.f, lmv = tok_ok ? lmv_raw : 0.f;
+  const bool nxt_ok = tok_ok && t0 + tid + 1 < p.L;
+  const float dnv = nxt_ok ? dnv_raw : 0.f, lmnv = nxt_ok ? lmnv_raw : 1.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (!(th_ok & (1u << j))) th4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // chunk-local cumulative log decay (token tid) and phases (this thread's
+  // tokens and pairs): in-register / in-wave scans, one barrier across waves
+  float gv = 0.f, wv = 0.f, lsc = 0.f;
   if (tid < Q) {
     gv = lmv * dv;
     wv = gv + (1.f - lmnv) * dnv;
-    s_tok[tid] = dv * A;
+    lsc = dv * A;
   }
-  if (p.theta) {
 #pragma unroll
-    for (int u = 0; u < TH; ++u) {
-      const int i = tid + u * kThreads;
-      if (i < n4) {
-        s_cs[4 * i].x = th4[u].x; s_cs[4 * i + 1].x = th4[u].y;
-        s_cs[4 * i + 2].x = th4[u].z; s_cs[4 * i + 3].x = th4[u].w;
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(lsc, off);
+    if (lane >= off) lsc += u;
+  }
+#pragma unroll
+  for (int j = 1; j < 4; ++j)
+    if (j < ALEN) th4[j] = add4(th4[j], th4[j - 1]);
+  float4 atot = th4[0];   // this thread's segment total (constant indices only:
+#pragma unroll               // a run-time index would put th4 in private memory)
+  for (int j = 1; j < 4; ++j)
+    if (j < ALEN) atot = th4[j];
+  float4 ainc = atot;
+#pragma unroll
+  for (int off = NG; off < 64; off <<= 1) {
+    const float4 u = shfl_up4(ainc, off);
+    if (lane >= off) ainc = add4(ainc, u);
+  }
+  if (lane == 63) s_segl[wave] = lsc;
+  if (lane >= 64 - NG) s_sega[wave * NG + cg] = ainc;
+  __syncthreads();
+  float lbase = 0.f, l_end = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float t = s_segl[w];
+    if (w < wave) lbase += t;
+    l_end += t;
+  }
+  float4 abase = sub4(ainc, atot);
+  for (int w = 0; w < wave; ++w) abase = add4(abase, s_sega[w * NG + cg]);
+  __syncthreads();   // scan scratch (inside B's space) is dead after this
+  if (tid < Q) {
+    const float lv = lsc + lbase;
+    const float W = tid < nt ? __expf(l_end - lv) * wv : 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s_row[tid * R + r] = make_float4(lv, wv, gv, W);
+      s_W[tid * R + r] = W;
+    }
+  }
+  for (int i = Q * R + tid; i < QRp; i += kThreads) {
+    s_row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    s_W[i] = 0.f;
+  }
+  if (sg < NSEG) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < ALEN) {
+        const float4 ph = add4(abase, th4[j]);
+        float s0, c0, s1, c1, s2, c2, s3, c3;
+        __sincosf(ph.x, &s0, &c0);
+        __sincosf(ph.y, &s1, &c1);
+        __sincosf(ph.z, &s2, &c2);
+        __sincosf(ph.w, &s3, &c3);
+        float4* d = reinterpret_cast<float4*>(s_cs + (sg * ALEN + j) * CSS + 4 * cg);
+        d[0] = make_float4(c0, s0, c1, s1);
+        d[1] = make_float4(c2, s2, c3, s3);
       }
     }
   }
-  __syncthreads();
-  block_scan(s_tok, Q, s_seg);
-  const float l_end = s_tok[nt - 1];
-  if (tid < Q) {
-    const float lv = s_tok[tid];
-    const float W = tid < nt ? __expf(l_end - lv) * wv : 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) s_row[tid * R + r] = make_float4(lv, wv, gv, W);
-  }
-  for (int i = Q * R + tid; i < QRp; i += kThreads) s_row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (p.theta) {
-    column_scan(s_cs, Q, NH, s_seg);
-    for (int i = tid; i < Q * NH; i += kThreads) {
-      float sn, cn;
-      __sincosf(s_cs[i].x, &sn, &cn);
-      s_cs[i] = make_float2(cn, sn);
-    }
-  } else {
-    for (int i = tid; i < Q * NH; i += kThreads) s_cs[i] = make_float2(1.f, 0.f);
-  }
-  __syncthreads();   // angles done; s_tok / s_seg (inside B's space) are dead
+  __syncthreads();   // angles done
   // Off-diagonal mask blocks use exp(l_t - l_s) = exp(l_t - l_be) exp(l_be - l_s)
   // with be the last valid row of the source block (s <= be <= t: both factors
   // <= 1); the second factor times the two-band weight is kept per row.
   for (int k = tid; k < QRp; k += kThreads) {
-    float2 v = make_float2(0.f, 0.f);
+    float v = 0.f;
     if (k < rows) {
       const float4 rk = s_row[k];
-      const float e = __expf(s_row[min(k | 31, rows - 1)].x - rk.x);
-      v = make_float2(e * rk.y, e * rk.z);
+      v = __expf(s_row[min(k | 31, rows - 1)].x - rk.x) * rk.y;
     }
     s_rw[k] = v;
   }
 
-  // ---- B: stage B~ = R(-Phi_s) B_s and X, both row-major ----
+  // ---- B: stage B~ = R(-Phi_s) B_s and X (permuted columns) ----
   for (int base = tid; base < ntot; base += kThreads * 8) {
     if (base != tid) issue_batch(base);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = base + u * kThreads;
+      if (!(raw_ok & (1u << u))) raw_zero(raw[u]);
       if (i < nbi) {
         const int row = i / (N / 8), ng = i - row * (N / 8);
         float v[8];
         raw_unpack(raw[u], v);
-        if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * NH + ng * 4);
+        if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * CSS + ng * 4);
         store8<T>(s_B + row * NS + ng * 8, v);
       } else if (i < ntot) {
         const int j = i - nbi;
         const int row = j / (P / 8), pg = j - row * (P / 8);
-        raw_store(s_X + row * XS + pg * 8, raw[u]);
+        store_x_permuted<TPt>(s_X + row * XS, pg * 8, raw[u]);
       }
     }
   }
@@ -429,8 +500,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     for (int kn = 0; kn < NK; ++kn) {
       const int n0 = kn * 32 + 8 * g4;
       float v[8];
+      if (!(craw_ok & (1u << (k * NK + kn)))) raw_zero(craw[k][kn]);
       raw_unpack(craw[k][kn], v);
-      if (n0 < N) rotate_neg(v, s_cs + ta * NH + n0 / 2);
+      if (n0 < N) rotate_neg(v, s_cs + ta * CSS + n0 / 2);
 #pragma unroll
       for (int e = 0; e < 8; ++e) frag_set(cf[k][kn], e, v[e]);
     }
@@ -447,9 +519,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     for (int j = 0; j < PTW; ++j) uacc[i][j] = zero4();
   for (int ks = 0; ks < QRp; ks += 32) {
     const int r0 = ks + 8 * g4;
-    float Wk[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) Wk[e] = s_row[r0 + e].w;
+    const float4 w0 = *reinterpret_cast<const float4*>(s_W + r0);
+    const float4 w1 = *reinterpret_cast<const float4*>(s_W + r0 + 4);
+    const float Wk[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     Frag<T> xf[PTW];
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
@@ -472,8 +544,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
     const int k0 = ((nslot + NGRP * i) * 16 + 4 * g4) >> 1;
-    psi[i][0] = s_cs[(nt - 1) * NH + k0];
-    psi[i][1] = s_cs[(nt - 1) * NH + k0 + 1];
+    psi[i][0] = s_cs[(nt - 1) * CSS + k0];
+    psi[i][1] = s_cs[(nt - 1) * CSS + k0 + 1];
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       f32x4& u = uacc[i][j];
@@ -543,14 +615,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
       for (int j = 0; j < PTW; ++j) {
         const int pt = pslot + WPN * j;
         if (pt < TPt) {
-          const int pc = pt * 16 + l16;
+          const int hc = hcol(pt);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float v = p.h0 ? p.h0[((size_t)bh * N + n0 + e) * P + pc] : 0.f;
+            float v = p.h0 ? p.h0[((size_t)bh * N + n0 + e) * P + hc] : 0.f;
             if (Bp) {
               float acc = 0.f;
 #pragma unroll
-              for (int r = 0; r < R; ++r) acc += to_f(Bp[r * N + n0 + e]) * to_f(xp[r * P + pc]);
+              for (int r = 0; r < R; ++r) acc += to_f(Bp[r * N + n0 + e]) * to_f(xp[r * P + hc]);
               v += kappa0 * acc;
             }
             FU[i][j][e] = v;
@@ -696,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
           st_dev2(d, o0, o1);
           st_dev2(d + 2, o2, o3);
         } else if (p.h_out) {
-          float* ho = p.h_out + ((size_t)bh * N + n0) * P + pc;
+          float* ho = p.h_out + ((size_t)bh * N + n0) * P + hcol(pt);
           ho[0] = o0; ho[P] = o1; ho[2 * P] = o2; ho[3 * P] = o3;
         }
       }
@@ -704,72 +776,105 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   }
   __syncthreads();   // S_in^T complete in LDS
 
-  // ---- E: outputs, one 16-row tile at a time ----
+  // ---- E: outputs of this wave's 16-row tiles (up to RTW), all together ----
   T* Yg = static_cast<T*>(p.y) + tok0 * R * P;
-  bool flag_pending = publish;
+  int itk[RTW], sbm[RTW];
+  bool vk[RTW];
 #pragma unroll
   for (int k = 0; k < RTW; ++k) {
-    if (k >= ntiles_w) break;
-    const int it = tile_of(k);
-    if (it * 16 >= rows) continue;
-    const int row_a = it * 16 + l16;
-    const bool va = row_a < rows;
-    const int ta = row_a >> LOGR;
-    f32x4 yacc[TPt];
+    itk[k] = k < ntiles_w ? tile_of(k) : 0;
+    vk[k] = k < ntiles_w && itk[k] * 16 < rows;
+    sbm[k] = vk[k] ? min(itk[k] * 16 + 15, rows - 1) / 32 : -1;
+  }
+  int sbmax = -1;
 #pragma unroll
-    for (int pn = 0; pn < TPt; ++pn) {
-      yacc[pn] = zero4();
+  for (int k = 0; k < RTW; ++k) sbmax = max(sbmax, sbm[k]);
+  // inter-chunk term C~_t^T S_in, scaled by exp(l_t)
+  f32x4 yacc[RTW][TPt];
 #pragma unroll
-      for (int kn = 0; kn < NK; ++kn) {
-        const int n0 = kn * 32 + 8 * g4;
-        Frag<T> hf;
-        if (n0 < N) frag_lds8(hf, s_H + (pn * 16 + l16) * NS + n0);
-        else frag_zero(hf);
-        yacc[pn] = mma(cf[k][kn], hf, yacc[pn]);
-      }
+  for (int k = 0; k < RTW; ++k)
+#pragma unroll
+    for (int pn = 0; pn < TPt; ++pn) yacc[k][pn] = zero4();
+#pragma unroll
+  for (int pn = 0; pn < TPt; ++pn) {
+#pragma unroll
+    for (int kn = 0; kn < NK; ++kn) {
+      const int n0 = kn * 32 + 8 * g4;
+      Frag<T> hf;
+      if (n0 < N) frag_lds8(hf, s_H + (pn * 16 + l16) * NS + n0);
+      else frag_zero(hf);
+#pragma unroll
+      for (int k = 0; k < RTW; ++k)
+        if (vk[k]) yacc[k][pn] = mma(cf[k][kn], hf, yacc[k][pn]);
     }
+  }
+  float l_t[RTW];
+#pragma unroll
+  for (int k = 0; k < RTW; ++k) {
+    if (!vk[k]) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = it * 16 + 4 * g4 + j;
+      const int row = itk[k] * 16 + 4 * g4 + j;
       const float e = row < rows ? __expf(s_row[row].x) : 0.f;
 #pragma unroll
-      for (int pn = 0; pn < TPt; ++pn) yacc[pn][j] *= e;
+      for (int pn = 0; pn < TPt; ++pn) yacc[k][pn][j] *= e;
     }
-    const int last_row = min(it * 16 + 15, rows - 1);
-    const int sbmax = last_row / 32;
-    const float l_t = va ? s_row[row_a].x : 0.f;
-    for (int sb = 0; sb <= sbmax; ++sb) {
-      f32x4 st0 = zero4(), st1 = zero4();
+    const int row_a = itk[k] * 16 + l16;
+    l_t[k] = row_a < rows ? s_row[row_a].x : 0.f;
+  }
+  // the state stores were issued before the inter term: wait for them and
+  // raise the flag before the intra-chunk work
+  if (publish) {
+    mem_done();
+    arrive_and_flag(&s_misc[4], flags + c, 2u);
+  }
+  for (int sb = 0; sb <= sbmax; ++sb) {
+    // S^T block = B~[32 rows of block sb] C~[tile]^T, for every tile of the wave
+    f32x4 st[RTW][2];
 #pragma unroll
-      for (int kn = 0; kn < NK; ++kn) {
-        const int n0 = kn * 32 + 8 * g4;
-        Frag<T> a0, a1;
-        if (n0 < N) {
-          frag_lds8(a0, s_B + (sb * 32 + l16) * NS + n0);
-          frag_lds8(a1, s_B + (sb * 32 + 16 + l16) * NS + n0);
-        } else {
-          frag_zero(a0);
-          frag_zero(a1);
-        }
-        st0 = mma(a0, cf[k][kn], st0);
-        st1 = mma(a1, cf[k][kn], st1);
+    for (int k = 0; k < RTW; ++k) st[k][0] = st[k][1] = zero4();
+#pragma unroll
+    for (int kn = 0; kn < NK; ++kn) {
+      const int n0 = kn * 32 + 8 * g4;
+      Frag<T> a0, a1;
+      if (n0 < N) {
+        frag_lds8(a0, s_B + (sb * 32 + l16) * NS + n0);
+        frag_lds8(a1, s_B + (sb * 32 + 16 + l16) * NS + n0);
+      } else {
+        frag_zero(a0);
+        frag_zero(a1);
       }
-      // decay x two-band mask on the score tile
-      Frag<T> pf;
-      if (sb * 32 + 32 <= it * 16) {
+#pragma unroll
+      for (int k = 0; k < RTW; ++k) {
+        if (sb <= sbm[k]) {
+          st[k][0] = mma(a0, cf[k][kn], st[k][0]);
+          st[k][1] = mma(a1, cf[k][kn], st[k][1]);
+        }
+      }
+    }
+    // decay x two-band mask on each score tile
+    Frag<T> pf[RTW];
+#pragma unroll
+    for (int k = 0; k < RTW; ++k) {
+      if (sb > sbm[k]) continue;
+      const int row_a = itk[k] * 16 + l16;
+      const bool va = row_a < rows;
+      if (sb * 32 + 32 <= itk[k] * 16) {
         // source block wholly before this tile: every s < t, one exp per lane
         const int be = min(sb * 32 + 31, rows - 1);
-        const float et = va ? __expf(l_t - s_row[be].x) : 0.f;
+        const float et = va ? __expf(l_t[k] - s_row[be].x) : 0.f;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int rb = sb * 32 + hh * 16 + 4 * g4;
+          const float4 rw = *reinterpret_cast<const float4*>(s_rw + sb * 32 + hh * 16 + 4 * g4);
+          const float r4[4] = {rw.x, rw.y, rw.z, rw.w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) frag_set(pf, hh * 4 + j, et * s_rw[rb + j].x * (hh ? st1[j] : st0[j]));
+          for (int j = 0; j < 4; ++j) frag_set(pf[k], hh * 4 + j, et * r4[j] * st[k][hh][j]);
         }
       } else {
         // the block holding this tile: elementwise; a lane's 4 rows in each
         // 16-row half are min(R, 4)-row groups of one token
         constexpr int RG = R < 4 ? R : 4;
+        const int ta = row_a >> LOGR;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int rb = sb * 32 + hh * 16 + 4 * g4;
@@ -780,40 +885,38 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
             float m = 0.f;
             if (va && srow < rows && s <= ta) {
               const float4 rw = s_row[srow];
-              m = __expf(l_t - rw.x) * (s < ta ? rw.y : rw.z);
+              m = __expf(l_t[k] - rw.x) * (s < ta ? rw.y : rw.z);
             }
 #pragma unroll
-            for (int j = q; j < q + RG; ++j) frag_set(pf, hh * 4 + j, m * (hh ? st1[j] : st0[j]));
+            for (int j = q; j < q + RG; ++j) frag_set(pf[k], hh * 4 + j, m * st[k][hh][j]);
           }
         }
       }
-#pragma unroll
-      for (int pn = 0; pn < TPt; ++pn) {
-        Frag<T> xf;
-        frag_tr(xf, s_X, XS, sb * 32 + 4 * g4, sb * 32 + 16 + 4 * g4, pn * 16);
-        yacc[pn] = mma(pf, xf, yacc[pn]);
-      }
     }
-    // the state stores were issued a whole tile ago: wait for them (before
-    // this tile's output stores join the queue) and raise the flag
-    if (flag_pending) {
-      mem_done();
-      arrive_and_flag(&s_misc[4], flags + c, 2u);
-      flag_pending = false;
-    }
+    // (mask o S) X, each X fragment shared by the tiles
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = it * 16 + 4 * g4 + j;
-      if (row < rows) {
-        T* yo = Yg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + l16;
+    for (int pn = 0; pn < TPt; ++pn) {
+      Frag<T> xf;
+      frag_tr(xf, s_X, XS, sb * 32 + 4 * g4, sb * 32 + 16 + 4 * g4, pn * 16);
 #pragma unroll
-        for (int pn = 0; pn < TPt; ++pn) yo[pn * 16] = from_f<T>(chain_ok ? yacc[pn][j] : nanv);
-      }
+      for (int k = 0; k < RTW; ++k)
+        if (sb <= sbm[k]) yacc[k][pn] = mma(pf[k], xf, yacc[k][pn]);
     }
   }
-  if (flag_pending) {
-    mem_done();
-    arrive_and_flag(&s_misc[4], flags + c, 2u);
+  // y: a lane holds head columns TPt*l16 .. TPt*l16+TPt-1 of 4 rows per tile
+#pragma unroll
+  for (int k = 0; k < RTW; ++k) {
+    if (!vk[k]) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = itk[k] * 16 + 4 * g4 + j;
+      if (row < rows) {
+        float v[TPt];
+#pragma unroll
+        for (int pn = 0; pn < TPt; ++pn) v[pn] = chain_ok ? yacc[k][pn][j] : nanv;
+        store_row<T, TPt>(Yg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + TPt * l16, v);
+      }
+    }
   }
 }
 
