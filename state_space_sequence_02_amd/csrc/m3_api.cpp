@@ -60,7 +60,7 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
   plan->Q = q;
   plan->nc = s.seqlen > 0 ? (s.seqlen + q - 1) / q : 0;
   const size_t bhc = (size_t)s.batch * s.nheads * plan->nc;
-  const size_t map = (size_t)s.headdim * s.dstate * sizeof(float);
+  const size_t map = (size_t)fused_slot_floats(s.dstate, s.headdim) * sizeof(float);
   plan->off_flags = 256;
   plan->off_recs = align256(plan->off_flags + bhc * sizeof(unsigned));
   plan->off_maps = align256(plan->off_recs + bhc * (s.dstate + 2) * sizeof(float));

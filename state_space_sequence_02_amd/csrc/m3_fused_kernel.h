@@ -62,8 +62,9 @@
 namespace m3 {
 namespace fused {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = kFusedThreads;
 constexpr int kWaves = kThreads / 64;
+constexpr int kMaxBatch = 12;         // 16-byte B/X loads per thread per batch, at most
 constexpr unsigned kSpinLimit = 1u << 20;
 constexpr int kMapGroup = 1;        // predecessor maps loaded per round trip
 constexpr int kAngleCap = kFusedAngleCap;   // max Q * N/2 angles per chunk
@@ -72,7 +73,8 @@ constexpr int kAngleCap = kFusedAngleCap;   // max Q * N/2 angles per chunk
 // C~ fragments a wave keeps in registers).
 __host__ __device__ constexpr int fused_rows_cap(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
 
-__host__ __device__ inline int round_up_i(int a, int b) { return (a + b - 1) / b * b; }
+__host__ __device__ constexpr int round_up_i(int a, int b) { return (a + b - 1) / b * b; }
+
 __host__ __device__ inline size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 
 struct Lds {
@@ -82,7 +84,7 @@ struct Lds {
 // row: per (token, rank) row float4 {l, w, gamma, W}
 // rw: per row exp(l_be - l) w with be the last row of the row's 32-row block
 //     (the factored decay of the off-diagonal mask blocks);  W: per row W
-// csH: cos/sin of Phi [Q][N/2 + 4] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8]
+// csH: cos/sin of Phi [Q][N/2 + 1] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8]
 // B: B~ [QRp][N+8];  X: X [QRp][P+8] (permuted columns)
 // segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
 __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize) {
@@ -93,7 +95,7 @@ __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize)
   o.rw = o.row + sizeof(float4) * QRp;
   o.W = o.rw + sizeof(float) * QRp;
   o.csH = o.W + sizeof(float) * QRp;
-  o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2 + 4), (size_t)esize * P * (N + 8)), 16);
+  o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2 + 1), (size_t)esize * P * (N + 8)), 16);
   o.X = o.B + round_up_i((int)max_sz((size_t)esize * QRp * (N + 8), scan), 16);
   o.misc = o.X + (size_t)esize * QRp * (P + 8);
   o.total = o.misc + 32;
@@ -209,6 +211,37 @@ __device__ __forceinline__ void frag_tr(Frag<float>& f, const float* base, int s
   }
 }
 
+// Raw buffer access: a descriptor with a byte extent; loads at offsets past
+// the extent return zeros.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kCpolDevice = 16;   // sc1: the coherence bit of device-scope atomic accesses
+__device__ __forceinline__ Rsrc buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float buf_load_f32(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float4 buf_load_f32x4(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void raw_load_buf(Raw8<bf16>& d, Rsrc r, uint32_t off) {
+  d.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void raw_load_buf(Raw8<float>& d, Rsrc r, uint32_t off) {
+  d.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  d.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+}
+
+// 16-byte loads/stores with the cache policy of device-scope atomics (sc1):
+// written by one workgroup, read by another after a flag.
+__device__ __forceinline__ f32x4 buf_load_dev4(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ void buf_store_dev4(Rsrc r, uint32_t off, f32x4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolDevice);
+}
+
 // Stores the 8 head columns c0..c0+7 of one X row into the permuted LDS row:
 // head column c goes to LDS column (c % TPt) * 16 + c / TPt.
 template <int TPt, typename T>
@@ -253,11 +286,13 @@ __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
   return make_float4(__shfl_up(v.x, off), __shfl_up(v.y, off), __shfl_up(v.z, off), __shfl_up(v.w, off));
 }
 
-template <typename T, int N, int P, int R>
+// RT: output row tiles per wave (the chunk has at most RT * 16 * kWaves rows);
+// register arrays are sized by it.
+template <typename T, int N, int P, int R, int RT>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   constexpr int NH = N / 2;
   constexpr int NG = NH / 4;                  // 4-pair column groups of the angle table
-  constexpr int CSS = NH + 4;                 // angle table row stride (float2): rows 32 B apart in banks
+  constexpr int CSS = NH + 1;                 // angle table row stride (float2): rows 2 banks apart
   constexpr int NK = (N + 31) / 32;           // 32-wide slices of the state dimension
   constexpr int TPt = P / 16;                 // 16-column tiles of the head dimension
   constexpr int TNt = N / 16;                 // 16-row tiles of the state dimension
@@ -269,12 +304,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   constexpr int NS = N + 8;                   // LDS row stride of B~ and S_in^T
   constexpr int XS = P + 8;                   // LDS row stride of X
   constexpr int LOGR = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;
-  constexpr int RTW = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;   // max output row tiles per wave
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int nslot = wave % NGRP, pslot = wave / NGRP;
-  // head column held by lane l16 in 16-column tile pt (the permuted order)
-  auto hcol = [&](int pt) { return l16 * TPt + pt; };
+  constexpr int RTW = RT;                     // max output row tiles per wave
+  // B/X loads per thread per batch: the whole chunk in one batch when it fits
+  constexpr int kBatchRaw = (round_up_i(RT * 16 * kWaves * (N / 8), kThreads) + RT * 16 * kWaves * (P / 8) +
+                             kThreads - 1) / kThreads;
+  constexpr int kBatch = kBatchRaw < kMaxBatch ? kBatchRaw : kMaxBatch;
+  const int tid = threadIdx.x;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int Q = p.Q;
@@ -291,103 +326,116 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   int* s_misc = reinterpret_cast<int*>(smem + lay.misc);
 
   // ---- ticket: chunk-major order over all sequences ----
-  if (tid == 0) {
-    s_misc[0] = (int)atomicAdd(p.counter, 1u);
-    s_misc[3] = 0;      // wave counter: map published
-    s_misc[4] = 0;      // wave counter: state published
-  }
+  const int nbh = p.batch * p.H;
+  if (tid == 0) s_misc[0] = (int)atomicAdd(p.counter, 1u);
   __syncthreads();
   const int ticket = s_misc[0];
-  const int nbh = p.batch * p.H;
-  const int c = ticket / nbh, bh = ticket - c * nbh;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int t0 = c * Q;
-  const int nt = min(Q, p.L - t0);
-  const int rows = nt * R;
   const int QRp = round_up_i(Q * R, 32);
   const int MT = QRp / 16;
-  const size_t tok0 = tok_index(p, b, t0, h);
   const size_t tstride = (size_t)p.H;           // token step in [b, L, H] arrays
   const size_t rowstepB = tstride * R * N, rowstepX = tstride * R * P;
-  unsigned* flags = p.flags + (size_t)bh * p.nc;
-  const T* Bg = static_cast<const T*>(p.B) + tok0 * R * N;
-  const T* Xg = static_cast<const T*>(p.x) + tok0 * R * P;
-  const T* Cg = static_cast<const T*>(p.C) + tok0 * R * N;
+  constexpr uint32_t kOff = 0x80000000u;        // an offset past every extent
+  const uint32_t tsb = (uint32_t)tstride * 4;   // token step of [b, L, H] fp32 arrays, bytes
+  const uint32_t esz = sizeof(T);
+  const uint32_t rsB = (uint32_t)rowstepB * esz, rsX = (uint32_t)rowstepX * esz;
+  float dv, lmv, dnv, lmnv_raw;
+  float4 th4[4];
+  Raw8<T> raw[kBatch];
+  Raw8<T> craw[RTW][NK];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int nslot = wave % NGRP, pslot = wave / NGRP;
+  // head column held by lane l16 in 16-column tile pt (the permuted order)
+  auto hcol = [&](int pt) { return l16 * TPt + pt; };
   // output row tiles of this wave, paired (w, MT-1-w) for balance
   const int ntiles_w = (MT + kWaves - 1 - wave) / kWaves;
   auto tile_of = [&](int k) {
     const int pair = k >> 1;
     return (k & 1) ? MT - 1 - (wave + 2 * kWaves * pair) : wave + 2 * kWaves * pair;
   };
-
-  // ---- A: every global load of the chunk is issued before any of it is used ----
-  // Loads are unconditional, from clamped (valid) addresses, and out-of-range
-  // values are masked only when consumed: a load under a branch merged with a
-  // default value makes the compiler wait for it at the merge, which would
-  // serialise the whole batch.
-  const float A = p.A[h];
-  const int tq = min(tid, nt - 1);
-  const size_t tk = tok0 + tq * tstride;
-  const size_t tkn = tok_index(p, b, min(t0 + tq + 1, p.L - 1), h);
-  const float dv_raw = p.dt[tk], lmv_raw = p.lam[tk];
-  const float dnv_raw = p.dt[tkn], lmnv_raw = p.lam[tkn];
   // angles: thread -> (segment sg, column group cg): tokens sg*ALEN .. +ALEN-1,
   // pairs 4cg .. 4cg+3 (ALEN <= 4 since Q * N/2 <= kAngleCap)
   const int NSEG = min(kThreads / NG, Q);
   const int ALEN = Q / NSEG;
   const int cg = tid % NG, sg = tid / NG;
-  float4 th4[4];
-  unsigned th_ok = 0;
+  // B items are padded to a multiple of the workgroup size so every item slot
+  // of a batch reads one tensor (a uniform descriptor).
+  const int nbi = QRp * (N / 8), nxi = QRp * (P / 8);
+  const int nbp = round_up_i(nbi, kThreads), ntot = nbp + nxi;
+
+  // ---- A: every global load of the chunk is issued before any of it is used ----
+  // Raw buffer loads: 32-bit offsets from per-chunk descriptors whose extent
+  // ends after the chunk's last valid token, so rows past the sequence end (and
+  // unused item slots) read as zeros without masks or branches.  (A load under
+  // a branch merged with a default value would make the compiler wait for it at
+  // the merge and serialise the batch.)
+  auto batch_loads = [&](Rsrc rB, Rsrc rX, int base) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int s = sg * ALEN + j;
-    const bool ok = p.theta && j < ALEN && sg < NSEG && s < nt;
-    th_ok |= ok ? 1u << j : 0u;
-    const float* src = ok ? p.theta + (tok0 + s * tstride) * NH + 4 * cg : p.dt + tok0;
-    th4[j] = *reinterpret_cast<const float4*>(src);
-  }
-  // B and X rows (first batch) and this wave's C rows: consumed once the
-  // angles are known.
-  const int nbi = QRp * (N / 8), nxi = QRp * (P / 8), ntot = nbi + nxi;
-  Raw8<T> raw[8];
-  unsigned raw_ok = 0;
-  auto issue_batch = [&](int base) {
-    raw_ok = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const int i = base + u * kThreads;
-      const bool isb = i < nbi;
-      const int j = isb ? i : i - nbi;
-      const int row = isb ? i / (N / 8) : j / (P / 8);
-      const int g = isb ? i - row * (N / 8) : j - row * (P / 8);
-      const bool ok = i < ntot && row < rows;
-      const T* src = isb ? Bg + (row >> LOGR) * rowstepB + (row & (R - 1)) * N + g * 8
-                         : Xg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + g * 8;
-      raw_ok |= ok ? 1u << u : 0u;
-      raw_load(raw[u], ok ? src : Bg);
+      if (base - tid + u * kThreads < nbp) {     // uniform: this slot reads B
+        const int row = i / (N / 8), g = i - row * (N / 8);
+        raw_load_buf(raw[u], rB, i < nbi ? (uint32_t)(row >> LOGR) * rsB + ((row & (R - 1)) * N + g * 8) * esz : kOff);
+      } else {
+        const int j = i - nbp;
+        const int row = j / (P / 8), g = j - row * (P / 8);
+        raw_load_buf(raw[u], rX, j < nxi ? (uint32_t)(row >> LOGR) * rsX + ((row & (R - 1)) * P + g * 8) * esz : kOff);
+      }
     }
   };
-  issue_batch(tid);
-  Raw8<T> craw[RTW][NK];
-  unsigned craw_ok = 0;
+  auto issue_chunk = [&](int tk) {
+    const int c = tk / nbh, bh = tk - c * nbh;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int t0 = c * Q;
+    const int nt = min(Q, p.L - t0);
+    const size_t tok0 = tok_index(p, b, t0, h);
+    const Rsrc rD = buf_rsrc(p.dt + tok0, (nt - 1) * tsb + 4);
+    const Rsrc rL = buf_rsrc(p.lam + tok0, (nt - 1) * tsb + 4);
+    const int nnext = min(nt, p.L - t0 - 1);    // tokens whose successor exists
+    const Rsrc rDn = buf_rsrc(p.dt + tok0 + tstride, nnext > 0 ? (nnext - 1) * tsb + 4 : 0);
+    const Rsrc rLn = buf_rsrc(p.lam + tok0 + tstride, nnext > 0 ? (nnext - 1) * tsb + 4 : 0);
+    const uint32_t toff = tid < Q ? tid * tsb : kOff;
+    dv = buf_load_f32(rD, toff);
+    lmv = buf_load_f32(rL, toff);
+    dnv = buf_load_f32(rDn, toff);
+    lmnv_raw = buf_load_f32(rLn, toff);
+    const Rsrc rT = buf_rsrc(p.theta ? p.theta + tok0 * NH : nullptr, p.theta ? (nt - 1) * tsb * NH + NH * 4 : 0);
 #pragma unroll
-  for (int k = 0; k < RTW; ++k) {
-    const int row_a = (k < ntiles_w ? tile_of(k) : 0) * 16 + l16;
-#pragma unroll
-    for (int kn = 0; kn < NK; ++kn) {
-      const int n0 = kn * 32 + 8 * g4;
-      const bool ok = k < ntiles_w && row_a < rows && n0 < N;
-      craw_ok |= ok ? 1u << (k * NK + kn) : 0u;
-      raw_load(craw[k][kn], ok ? Cg + (row_a >> LOGR) * rowstepB + (row_a & (R - 1)) * N + n0 : Cg);
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = j < ALEN && sg < NSEG;
+      th4[j] = buf_load_f32x4(rT, ok ? (uint32_t)(sg * ALEN + j) * tsb * NH + 16 * cg : kOff);
     }
-  }
-  const bool tok_ok = tid < nt;
-  const float dv = tok_ok ? dv_raw : 0.f, lmv = tok_ok ? lmv_raw : 0.f;
-  const bool nxt_ok = tok_ok && t0 + tid + 1 < p.L;
-  const float dnv = nxt_ok ? dnv_raw : 0.f, lmnv = nxt_ok ? lmnv_raw : 1.f;
+    const uint32_t extB = (uint32_t)(nt - 1) * rsB + R * N * esz;
+    batch_loads(buf_rsrc(static_cast<const T*>(p.B) + tok0 * R * N, extB),
+                buf_rsrc(static_cast<const T*>(p.x) + tok0 * R * P, (uint32_t)(nt - 1) * rsX + R * P * esz), tid);
+    const Rsrc rC = buf_rsrc(static_cast<const T*>(p.C) + tok0 * R * N, extB);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (!(th_ok & (1u << j))) th4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < RTW; ++k) {
+      const int row_a = (k < ntiles_w ? tile_of(k) : 0) * 16 + l16;
+#pragma unroll
+      for (int kn = 0; kn < NK; ++kn) {
+        const int n0 = kn * 32 + 8 * g4;
+        const bool ok = k < ntiles_w && n0 < N;
+        raw_load_buf(craw[k][kn], rC, ok ? (uint32_t)(row_a >> LOGR) * rsB + ((row_a & (R - 1)) * N + n0) * esz : kOff);
+      }
+    }
+  };
+  issue_chunk(ticket);
+  const int c = ticket / nbh, bh = ticket - c * nbh;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int t0 = c * Q;
+  const int nt = min(Q, p.L - t0);
+  const int rows = nt * R;
+  const size_t tok0 = tok_index(p, b, t0, h);
+  unsigned* flags = p.flags + (size_t)bh * p.nc;
+  const T* Bg = static_cast<const T*>(p.B) + tok0 * R * N;
+  const T* Xg = static_cast<const T*>(p.x) + tok0 * R * P;
+  const float A = p.A[h];
+  if (tid == 0) {
+    s_misc[3] = 0;      // wave counter: map published
+    s_misc[4] = 0;      // wave counter: state published
+  }
+  const float lmnv = (t0 + tid + 1 < p.L && tid < nt) ? lmnv_raw : 1.f;   // (only multiplies dnv = 0 otherwise)
 
   // chunk-local cumulative log decay (token tid) and phases (this thread's
   // tokens and pairs): in-register / in-wave scans, one barrier across waves
@@ -451,9 +499,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
         __sincosf(ph.y, &s1, &c1);
         __sincosf(ph.z, &s2, &c2);
         __sincosf(ph.w, &s3, &c3);
-        float4* d = reinterpret_cast<float4*>(s_cs + (sg * ALEN + j) * CSS + 4 * cg);
-        d[0] = make_float4(c0, s0, c1, s1);
-        d[1] = make_float4(c2, s2, c3, s3);
+        float2* d = s_cs + (sg * ALEN + j) * CSS + 4 * cg;
+        d[0] = make_float2(c0, s0);
+        d[1] = make_float2(c1, s1);
+        d[2] = make_float2(c2, s2);
+        d[3] = make_float2(c3, s3);
       }
     }
   }
@@ -471,20 +521,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   }
 
   // ---- B: stage B~ = R(-Phi_s) B_s and X (permuted columns) ----
-  for (int base = tid; base < ntot; base += kThreads * 8) {
-    if (base != tid) issue_batch(base);
+  for (int base = tid; base < ntot; base += kThreads * kBatch) {
+    if (base != tid)
+      batch_loads(buf_rsrc(Bg, (uint32_t)(nt - 1) * rsB + R * N * esz),
+                  buf_rsrc(Xg, (uint32_t)(nt - 1) * rsX + R * P * esz), base);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const int i = base + u * kThreads;
-      if (!(raw_ok & (1u << u))) raw_zero(raw[u]);
       if (i < nbi) {
         const int row = i / (N / 8), ng = i - row * (N / 8);
         float v[8];
         raw_unpack(raw[u], v);
         if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * CSS + ng * 4);
         store8<T>(s_B + row * NS + ng * 8, v);
-      } else if (i < ntot) {
-        const int j = i - nbi;
+      } else if (i >= nbp && i < ntot) {
+        const int j = i - nbp;
         const int row = j / (P / 8), pg = j - row * (P / 8);
         store_x_permuted<TPt>(s_X + row * XS, pg * 8, raw[u]);
       }
@@ -500,7 +551,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     for (int kn = 0; kn < NK; ++kn) {
       const int n0 = kn * 32 + 8 * g4;
       float v[8];
-      if (!(craw_ok & (1u << (k * NK + kn)))) raw_zero(craw[k][kn]);
       raw_unpack(craw[k][kn], v);
       if (n0 < N) rotate_neg(v, s_cs + ta * CSS + n0 / 2);
 #pragma unroll
@@ -555,7 +605,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     }
   }
   const float a_c = __expf(l_end);
-  const size_t slot = (size_t)P * N;
+  // chunk maps and states: stored in register order, each lane's 4 values of a
+  // state tile contiguous (a wave writes or reads 1 KB runs), with the cache
+  // policy of device-scope atomics
+  constexpr uint32_t SLOT = fused_slot_floats(N, P);
+  auto slot_off = [&](int i, int jj) { return (uint32_t)(((i * PTW + jj) * kThreads + tid) * 16); };
   const size_t chunk_id = (size_t)bh * p.nc + c;
   // Publish the map only if the predecessor's state is not there yet.
   int need_map = 0;
@@ -568,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   if (tid == 0) s_misc[2] = need_map;
   __syncthreads();   // s_misc[2] visible; every read of the cos/sin table is done
   if (s_misc[2]) {
-    float* U = p.maps + chunk_id * slot;
+    const Rsrc rU = buf_rsrc(p.maps + chunk_id * SLOT, SLOT * 4);
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
       const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
@@ -580,11 +634,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
 #pragma unroll
       for (int j = 0; j < PTW; ++j) {
         const int pt = pslot + WPN * j;
-        if (pt < TPt) {
-          float* d = U + (size_t)(pt * 16 + l16) * N + n0;
-          st_dev2(d, uacc[i][j][0], uacc[i][j][1]);
-          st_dev2(d + 2, uacc[i][j][2], uacc[i][j][3]);
-        }
+        if (pt < TPt) buf_store_dev4(rU, slot_off(i, j), uacc[i][j]);
       }
     }
     mem_done();
@@ -660,31 +710,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
       __syncthreads();
       if (nmap < 0) { chain_ok = false; break; }
       // the state (if any) is loaded alongside the maps
-      float2 sx[NPW][PTW][2];
+      f32x4 sx[NPW][PTW];
       if (state) {
-        const float* S = p.states + ((size_t)bh * p.nc + hi - nmap) * slot;
+        const Rsrc rS = buf_rsrc(p.states + ((size_t)bh * p.nc + hi - nmap) * SLOT, SLOT * 4);
 #pragma unroll
-        for (int i = 0; i < NPW; ++i) {
-          const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+        for (int i = 0; i < NPW; ++i)
 #pragma unroll
-          for (int jj = 0; jj < PTW; ++jj) {
-            const int pt = pslot + WPN * jj;
-            if (pt < TPt) {
-              const float* q = S + (size_t)(pt * 16 + l16) * N + n0;
-              sx[i][jj][0] = ld_dev2(q);
-              sx[i][jj][1] = ld_dev2(q + 2);
-            }
-          }
-        }
+          for (int jj = 0; jj < PTW; ++jj)
+            if (pslot + WPN * jj < TPt) sx[i][jj] = buf_load_dev4(rS, slot_off(i, jj));
       }
       for (int m0 = 0; m0 < nmap; m0 += kMapGroup) {
-        float2 ux[kMapGroup][NPW][PTW][2], rx[kMapGroup][NPW][2];
+        f32x4 ux[kMapGroup][NPW][PTW];
+        float2 rx[kMapGroup][NPW][2];
         float ax[kMapGroup];
 #pragma unroll
         for (int g = 0; g < kMapGroup; ++g) {
           if (m0 + g < nmap) {
             const size_t jid = (size_t)bh * p.nc + hi - m0 - g;
-            const float* U = p.maps + jid * slot;
+            const Rsrc rU = buf_rsrc(p.maps + jid * SLOT, SLOT * 4);
             const float* rec = p.recs + jid * (2 * NH + 2);
             ax[g] = ld_dev2(rec).x;
 #pragma unroll
@@ -693,14 +736,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
               rx[g][i][0] = ld_dev2(rec + 2 + n0);
               rx[g][i][1] = ld_dev2(rec + 2 + n0 + 2);
 #pragma unroll
-              for (int jj = 0; jj < PTW; ++jj) {
-                const int pt = pslot + WPN * jj;
-                if (pt < TPt) {
-                  const float* q = U + (size_t)(pt * 16 + l16) * N + n0;
-                  ux[g][i][jj][0] = ld_dev2(q);
-                  ux[g][i][jj][1] = ld_dev2(q + 2);
-                }
-              }
+              for (int jj = 0; jj < PTW; ++jj)
+                if (pslot + WPN * jj < TPt) ux[g][i][jj] = buf_load_dev4(rU, slot_off(i, jj));
             }
           }
         }
@@ -711,7 +748,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
             for (int i = 0; i < NPW; ++i) {
 #pragma unroll
               for (int jj = 0; jj < PTW; ++jj) {
-                const float2 x01 = ux[g][i][jj][0], x23 = ux[g][i][jj][1];
+                const float2 x01 = make_float2(ux[g][i][jj][0], ux[g][i][jj][1]);
+                const float2 x23 = make_float2(ux[g][i][jj][2], ux[g][i][jj][3]);
                 FU[i][jj][0] += FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y);
                 FU[i][jj][1] += FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y);
                 FU[i][jj][2] += FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y);
@@ -730,7 +768,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
         for (int i = 0; i < NPW; ++i) {
 #pragma unroll
           for (int jj = 0; jj < PTW; ++jj) {
-            const float2 x01 = sx[i][jj][0], x23 = sx[i][jj][1];
+            const float2 x01 = make_float2(sx[i][jj][0], sx[i][jj][1]);
+            const float2 x23 = make_float2(sx[i][jj][2], sx[i][jj][3]);
             FU[i][jj][0] += FA * (Fpsi[i][0].x * x01.x - Fpsi[i][0].y * x01.y);
             FU[i][jj][1] += FA * (Fpsi[i][0].y * x01.x + Fpsi[i][0].x * x01.y);
             FU[i][jj][2] += FA * (Fpsi[i][1].x * x23.x - Fpsi[i][1].y * x23.y);
@@ -744,6 +783,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   }
   const float nanv = __builtin_nanf("");
   const bool publish = c + 1 < p.nc;
+  const Rsrc rSo = buf_rsrc(p.states + chunk_id * SLOT, publish ? SLOT * 4 : 0);
   // S_in^T goes into the (now free) cos/sin region for the readout
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
@@ -755,8 +795,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
         const int pc = pt * 16 + l16;
         f32x4 si = FU[i][j];
         if (!chain_ok) si[0] = si[1] = si[2] = si[3] = nanv;
-        T* hd = s_H + pc * NS + n0;
-        hd[0] = from_f<T>(si[0]); hd[1] = from_f<T>(si[1]); hd[2] = from_f<T>(si[2]); hd[3] = from_f<T>(si[3]);
+        const float sv4[4] = {si[0], si[1], si[2], si[3]};
+        store_row<T, 4>(s_H + pc * NS + n0, sv4);
         const float q0 = a_c * si[0], q1 = a_c * si[1], q2 = a_c * si[2], q3 = a_c * si[3];
         const f32x4 u = uacc[i][j];
         const float o0 = psi[i][0].x * q0 - psi[i][0].y * q1 + u[0];
@@ -764,9 +804,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
         const float o2 = psi[i][1].x * q2 - psi[i][1].y * q3 + u[2];
         const float o3 = psi[i][1].y * q2 + psi[i][1].x * q3 + u[3];
         if (publish) {
-          float* d = p.states + chunk_id * slot + (size_t)pc * N + n0;
-          st_dev2(d, o0, o1);
-          st_dev2(d + 2, o2, o3);
+          buf_store_dev4(rSo, slot_off(i, j), f32x4{o0, o1, o2, o3});
         } else if (p.h_out) {
           float* ho = p.h_out + ((size_t)bh * N + n0) * P + hcol(pt);
           ho[0] = o0; ho[P] = o1; ho[2 * P] = o2; ho[3 * P] = o3;
@@ -929,13 +967,13 @@ __global__ void reset_kernel(unsigned* counter, unsigned* flags, size_t nflags) 
   for (size_t j = i; j < nflags; j += (size_t)gridDim.x * blockDim.x) flags[j] = 0u;
 }
 
-template <typename T, int N, int P, int R>
+template <typename T, int N, int P, int R, int RT>
 hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   // LDS limit raised once per instantiation
   static bool lds_set = false;
   hipError_t e;
   if (!lds_set && lds > 64 * 1024) {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R>),
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)) != hipSuccess)
       return e;
     lds_set = true;
@@ -945,18 +983,34 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   hipLaunchKernelGGL(reset_kernel<0>, dim3(rblocks), dim3(256), 0, stream, p.counter, p.flags, nflags);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t grid = nflags;
-  hipLaunchKernelGGL((prefill_kernel<T, N, P, R>), dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT>), dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
+}
+
+// Row tiles per wave for a chunk of Q tokens x R ranks (rows rounded up to 32).
+inline int row_tiles_per_wave(int Q, int R) {
+  const int rows = round_up_i(Q * R, 32);
+  return (rows / 16 + kWaves - 1) / kWaves;
+}
+
+template <typename T, int N, int P, int R>
+hipError_t launch_rt(const FusedParams& p, size_t lds, hipStream_t s) {
+  const int rt = row_tiles_per_wave(p.Q, R);
+  constexpr int kMaxRT = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;
+  if (rt <= 1) return launch<T, N, P, R, 1>(p, lds, s);
+  if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1)>(p, lds, s);
+  if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1)>(p, lds, s);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int N>
 hipError_t launch_n(const FusedParams& p, size_t lds, hipStream_t s) {
 #define M3_R_CASES(PP)                                          \
   switch (p.R) {                                                \
-    case 1: return launch<T, N, PP, 1>(p, lds, s);              \
-    case 2: return launch<T, N, PP, 2>(p, lds, s);              \
-    case 4: return launch<T, N, PP, 4>(p, lds, s);              \
-    case 8: return launch<T, N, PP, 8>(p, lds, s);              \
+    case 1: return launch_rt<T, N, PP, 1>(p, lds, s);           \
+    case 2: return launch_rt<T, N, PP, 2>(p, lds, s);           \
+    case 4: return launch_rt<T, N, PP, 4>(p, lds, s);           \
+    case 8: return launch_rt<T, N, PP, 8>(p, lds, s);           \
     default: return hipErrorInvalidValue;                       \
   }
   switch (p.P) {

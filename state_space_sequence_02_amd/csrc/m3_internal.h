@@ -32,7 +32,7 @@ inline bool supported_rank(int R) { return R == 1 || R == 2 || R == 4 || R == 8;
 // chunk to chunk with decoupled look-back.
 // Workspace (each region 256-byte aligned): control block (ticket counter) |
 // flags [b*H*nc] u32 | recs [b*H*nc][N+2] fp32 (a_c, pad, cos/sin Psi_c per
-// pair) | maps [b*H*nc][P][N] fp32 | states [b*H*nc][P][N] fp32.
+// pair) | maps [b*H*nc][fused_slot_floats] fp32 | states [b*H*nc][same] fp32.
 struct PrefillPlan {
   int Q;              // tokens per chunk
   int nc;             // chunks per sequence
@@ -51,6 +51,17 @@ struct FusedParams {
   unsigned* counter; unsigned* flags; float* recs; float* maps; float* states;
   int batch, L, H, N, P, R, logR, Q, nc;
 };
+// Threads per prefill workgroup, and the floats one chunk's map or state
+// occupies in the workspace: each thread stores its state tiles (n-tile x
+// p-tile of 16 x 16 shared out over the 8 waves as NPW x PTW tiles per wave,
+// 4 floats per lane) contiguously.
+constexpr int kFusedThreads = 512;
+__host__ __device__ constexpr int fused_slot_floats(int N, int P) {
+  return ((N / 16) / ((N / 16) < kFusedThreads / 64 ? (N / 16) : kFusedThreads / 64)) *
+         (((P / 16) + (kFusedThreads / 64) / ((N / 16) < kFusedThreads / 64 ? (N / 16) : kFusedThreads / 64) - 1) /
+          ((kFusedThreads / 64) / ((N / 16) < kFusedThreads / 64 ? (N / 16) : kFusedThreads / 64))) *
+         kFusedThreads * 4;
+}
 // Chunk limits of the single-pass prefill: (token, rank) rows per chunk and
 // angles (tokens x N/2) per chunk; they bound the per-thread prefetch registers.
 inline int fused_max_rows(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }

@@ -112,11 +112,17 @@ def test_workspace_size_matches_layout(lib, name):
     nc = -(-w.seqlen // q)
     bhc = w.batch * w.nheads * nc
     a = lambda v: (v + 255) // 256 * 256
-    # control block | flags | per-chunk records | maps | states
+    # control block | flags | per-chunk records | maps | states; a map or state
+    # slot holds each of the 512 threads' NPW x PTW state tiles (16 x 16 tiles
+    # shared out over 8 waves), 4 floats per lane
+    tn, tp = w.dstate // 16, w.headdim // 16
+    ngrp = min(tn, 8)
+    slot = (tn // ngrp) * (-(-tp // (8 // ngrp))) * 512 * 4
+    assert slot >= w.dstate * w.headdim
     recs = a(256 + bhc * 4)
     maps = a(recs + bhc * (w.dstate + 2) * 4)
-    states = a(maps + bhc * w.headdim * w.dstate * 4)
-    expect = a(states + bhc * w.headdim * w.dstate * 4)
+    states = a(maps + bhc * slot * 4)
+    expect = a(states + bhc * slot * 4)
     assert m3.prefill_workspace_bytes(shape) == expect
 
 
