@@ -41,7 +41,10 @@ size_t lds_need(int q, const m3_shape& s) {
 }
 
 int choose_chunk(const m3_shape& s) {
-  int q = s.chunk > 0 ? s.chunk : std::max(16, 256 / s.rank);
+  // default: 128 (token, rank) rows per chunk for N <= 64, 256 above (the
+  // state hand-off per chunk grows with N; so does the work that amortises it)
+  const int rows = s.dstate <= 64 ? 128 : 256;
+  int q = s.chunk > 0 ? s.chunk : std::max(16, rows / s.rank);
   int p2 = 16;
   while (p2 * 2 <= q && p2 < 256) p2 *= 2;
   q = std::max(16, std::min(p2, 256));

@@ -288,8 +288,13 @@ __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
 
 // RT: output row tiles per wave (the chunk has at most RT * 16 * kWaves rows);
 // register arrays are sized by it.
+// Two workgroups per CU need at most 128 VGPRs (4 waves per SIMD); the
+// instantiations that come close are held to it.
+template <int N, int RT>
+constexpr int prefill_waves_per_simd() { return (N <= 64 && RT <= 2) ? 4 : 2; }
+
 template <typename T, int N, int P, int R, int RT>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
+__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<N, RT>())) void prefill_kernel(FusedParams p) {
   constexpr int NH = N / 2;
   constexpr int NG = NH / 4;                  // 4-pair column groups of the angle table
   constexpr int CSS = NH + 1;                 // angle table row stride (float2): rows 2 banks apart
@@ -558,6 +563,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     }
   }
   __syncthreads();
+  // Wave 0 reads the flags of up to 64 predecessors (lane k: chunk c-1-k) now;
+  // the answer arrives during the map's MFMAs and serves both the choice of
+  // publishing the map and the first step of the look-back.
+  const int W0 = min(c, 64);
+  unsigned fpoll = 1u;
+  if (wave == 0 && lane < W0)
+    fpoll = __hip_atomic_load(flags + c - 1 - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- C: U[n][p] = R(Psi) sum_k W_k B~[k][n] X[k][p] ----
   // Lane layout of a (state tile ntl, column tile pt): rows n = 16 ntl + 4 g4 + j
@@ -611,15 +623,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
   constexpr uint32_t SLOT = fused_slot_floats(N, P);
   auto slot_off = [&](int i, int jj) { return (uint32_t)(((i * PTW + jj) * kThreads + tid) * 16); };
   const size_t chunk_id = (size_t)bh * p.nc + c;
-  // Publish the map only if the predecessor's state is not there yet.
-  int need_map = 0;
-  if (c > 0 && tid == 0)
-    need_map = __hip_atomic_load(flags + c - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2u ? 0 : 1;
-  if (need_map) {   // thread 0 only: the per-pair rotation record
-    float* rec = p.recs + chunk_id * (2 * NH + 2);
-    st_dev2(rec, a_c, 0.f);
+  // Publish the map only if the predecessor's state was not there at the poll.
+  if (wave == 0) {
+    const bool pred_state = (__ballot(lane < W0 && fpoll == 2u) & 1ull) != 0;
+    const int need_map = c > 0 && !pred_state;
+    if (lane == 0) {
+      s_misc[2] = need_map;
+      if (need_map) st_dev2(p.recs + chunk_id * (2 * NH + 2), a_c, 0.f);   // the record's decay
+    }
   }
-  if (tid == 0) s_misc[2] = need_map;
   __syncthreads();   // s_misc[2] visible; every read of the cos/sin table is done
   if (s_misc[2]) {
     const Rsrc rU = buf_rsrc(p.maps + chunk_id * SLOT, SLOT * 4);
@@ -687,13 +699,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FusedParams p) {
     // for.  Maps are then loaded together and composed newest first:
     // F <- F o f_j, i.e. FU += FA R(Fpsi) U_j, Fpsi <- Fpsi + Psi_j, FA <- FA a_j.
     int hi = c - 1;
+    bool first = true;   // the early poll covers the first window (hi = c - 1)
     while (true) {
       if (wave == 0) {
         const int W = min(hi + 1, 64);
         unsigned spins = 0;
         int nmap = 0, state = 0;
         while (true) {
-          const unsigned f = lane < W ? __hip_atomic_load(flags + hi - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+          unsigned f = 1u;
+          if (first) f = lane < W ? fpoll : 1u;
+          else if (lane < W) f = __hip_atomic_load(flags + hi - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          first = false;
           const unsigned long long m2 = __ballot(lane < W && f == 2u);
           const unsigned long long m0 = __ballot(lane < W && f == 0u);
           const int k2 = m2 ? __builtin_ctzll(m2) : W;    // nearest state (W: none in window)

@@ -133,4 +133,4 @@ def test_chunk_request_rounding(lib):
     assert m3.prefill_chunk_used(s(5)) == 16            # at least 16
     assert m3.prefill_chunk_used(s(4096)) <= 256
     assert m3.prefill_chunk_used(s(0, R=4, N=128)) == 64          # 256 rows by default
-    assert m3.prefill_chunk_used(s(0)) == 256
+    assert m3.prefill_chunk_used(s(0)) == 128                     # N <= 64: 128 rows by default
