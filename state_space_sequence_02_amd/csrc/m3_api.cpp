@@ -32,7 +32,8 @@ m3_status check_common(const m3_shape* s, bool need_seq) {
   return M3_OK;
 }
 
-// Tokens per chunk: the requested value (or a default of 256 / R rows-worth),
+// Tokens per chunk: the requested value (or a default of 128 (token, rank)
+// rows for N <= 64 and 256 rows above),
 // rounded down to a power of two in [16, 256], then halved until the chunk's
 // rows and angles fit the kernel's register budget and its LDS tiles fit on a
 // compute unit.

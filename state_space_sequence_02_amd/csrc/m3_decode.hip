@@ -139,15 +139,25 @@ __device__ __forceinline__ void stage_item(float* sW, float* sC, float* sXX, flo
   }
 }
 
-template <typename T, int R, int UPT>
-__global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
+// Threads per workgroup and units per thread for an N x P state: one unit per
+// thread up to 512 threads, then more units per thread.
+constexpr int decode_units(int N, int P) { return (N / 2) * (P / 4); }
+constexpr int decode_threads(int N, int P) {
+  return decode_units(N, P) >= 512 ? 512 : decode_units(N, P) <= 64 ? 64 : (decode_units(N, P) + 63) / 64 * 64;
+}
+
+// N and P are template parameters: the index arithmetic then needs no integer
+// division at run time.
+template <typename T, int R, int N, int P>
+__global__ __launch_bounds__(decode_threads(N, P)) void decode_kernel(DecodeParams p) {
+  constexpr int NT = decode_threads(N, P);
+  constexpr int UPT = (decode_units(N, P) + NT - 1) / NT;
   const int bh = blockIdx.x;
   const int h_idx = bh % p.H;
-  const int N = p.N, P = p.P;
-  const int QP = P >> 2;                 // quads per row
-  const int NT = blockDim.x;
+  constexpr int QP = P >> 2;             // quads per row
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, nwaves = NT >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int nwaves = NT >> 6;
 
   extern __shared__ float smem[];
   float* sW = smem;                      // [N][2R]
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
   float* sRed = reinterpret_cast<float*>(sCS + (N >> 1));     // [nwaves][R][P]
 
   const int q = tid % QP;                // constant across this thread's units
-  const int units = (N >> 1) * QP;
+  constexpr int units = (N >> 1) * QP;
   float* hg = p.h + (size_t)bh * N * P;
 
   const T* Bg = static_cast<const T*>(p.B) + (size_t)bh * R * N;
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
   // Small operands first (at most two items per thread), then the state.  Loads
   // complete in order, so the operands are staged into LDS and the barrier is
   // passed while the state is still in flight.
-  const int nb8 = (R * N) >> 3, nx8 = (R * P) >> 3;
+  constexpr int nb8 = (R * N) >> 3, nx8 = (R * P) >> 3;
   const int nth4 = thg ? (N >> 3) : 0;
   const int nitems = 3 * nb8 + 2 * nx8 + nth4;
   const float d = p.dt[bh], lm = p.lam[bh], Ah = p.A[h_idx];
@@ -265,33 +275,46 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <typename T, int R>
-hipError_t dispatch_upt(const DecodeParams& p, hipStream_t stream) {
-  const int units = (p.N / 2) * (p.P / 4);
-  const int nt = units >= 512 ? 512 : (units <= 64 ? 64 : ((units + 63) / 64) * 64);
-  const int upt = (units + nt - 1) / nt;
-  const int nwaves = nt / 64;
-  const size_t lds = sizeof(float) * (3 * (size_t)p.N * R + 2 * (size_t)R * p.P + p.N +
-                                      (size_t)nwaves * R * p.P);   // sW, sC, sXX, sCS, sRed
-  const dim3 grid(p.batch * p.H), block(nt);
-  switch (upt) {
-    case 1: hipLaunchKernelGGL((decode_kernel<T, R, 1>), grid, block, lds, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<T, R, 2>), grid, block, lds, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<T, R, 4>), grid, block, lds, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<T, R, 8>), grid, block, lds, stream, p); break;
-    case 16: hipLaunchKernelGGL((decode_kernel<T, R, 16>), grid, block, lds, stream, p); break;
+template <typename T, int R, int N, int P>
+hipError_t dispatch_shape(const DecodeParams& p, hipStream_t stream) {
+  constexpr int nt = decode_threads(N, P);
+  constexpr int nwaves = nt / 64;
+  const size_t lds = sizeof(float) * (3 * (size_t)N * R + 2 * (size_t)R * P + N +
+                                      (size_t)nwaves * R * P);   // sW, sC, sXX, sCS, sRed
+  hipLaunchKernelGGL((decode_kernel<T, R, N, P>), dim3(p.batch * p.H), dim3(nt), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int R, int N>
+hipError_t dispatch_p(const DecodeParams& p, hipStream_t stream) {
+  switch (p.P) {
+    case 16: return dispatch_shape<T, R, N, 16>(p, stream);
+    case 32: return dispatch_shape<T, R, N, 32>(p, stream);
+    case 64: return dispatch_shape<T, R, N, 64>(p, stream);
+    case 128: return dispatch_shape<T, R, N, 128>(p, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+template <typename T, int R>
+hipError_t dispatch_n(const DecodeParams& p, hipStream_t stream) {
+  switch (p.N) {
+    case 16: return dispatch_p<T, R, 16>(p, stream);
+    case 32: return dispatch_p<T, R, 32>(p, stream);
+    case 64: return dispatch_p<T, R, 64>(p, stream);
+    case 128: return dispatch_p<T, R, 128>(p, stream);
+    case 256: return dispatch_p<T, R, 256>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T>
 hipError_t dispatch_rank(const DecodeParams& p, hipStream_t stream) {
   switch (p.R) {
-    case 1: return dispatch_upt<T, 1>(p, stream);
-    case 2: return dispatch_upt<T, 2>(p, stream);
-    case 4: return dispatch_upt<T, 4>(p, stream);
-    case 8: return dispatch_upt<T, 8>(p, stream);
+    case 1: return dispatch_n<T, 1>(p, stream);
+    case 2: return dispatch_n<T, 2>(p, stream);
+    case 4: return dispatch_n<T, 4>(p, stream);
+    case 8: return dispatch_n<T, 8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -189,6 +189,18 @@ def test_decode_small(shape):
     check_blocks(to64(h), hr, tol, (2, 3), "decode h")
 
 
+def test_decode_several_pairs_per_workgroup():
+    """640 (sequence, head) pairs at N=128, P=64, R=4: more than the 512
+    workgroups of this shape that fit on the chip at once, so workgroups take
+    several pairs each and every pair after the first is prefetched."""
+    w = inputs.workload("decode", batch=20, nheads=32, headdim=64, dstate=128, rank=4, dtype="bf16")
+    d, h0, y, h = _decode_case(w, steps=3, seed=21)
+    yr, hr = oracle.decode_steps(h0, d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"])
+    tol = TOL[w.dtype]
+    check_blocks(to64(y), yr, tol, (3, 4), "decode y")
+    check_blocks(to64(h), hr, tol, (2, 3), "decode h")
+
+
 def test_prefill_then_decode_handoff():
     """prefill(L - k) followed by k decode steps equals prefill(L)."""
     w = inputs.workload("mimo", batch=2, seqlen=133, nheads=2)
