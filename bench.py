@@ -59,35 +59,57 @@ def table2_intensity(n, p, r):
 
 
 class StepTimer:
-    """HIP events between steps on the current stream (the stream the library
-    launches on): total and per-step durations of one timed loop."""
+    """HIP events on the current stream (the stream the library launches on):
+    one before every step and one after the last, plus (bracket=True) one right
+    after every step, so that each launch's own duration is measured apart from
+    the gap before the next launch."""
 
-    def __init__(self, steps):
+    def __init__(self, steps, bracket=False):
         self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        self.after = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if bracket else None
 
     def mark(self, i):
         self.ev[i].record(torch.cuda.current_stream())
+
+    def mark_after(self, i):
+        if self.after is not None:
+            self.after[i].record(torch.cuda.current_stream())
 
     def result(self):
         self.ev[-1].synchronize()
         per = [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(len(self.ev) - 1)]
         total = self.ev[0].elapsed_time(self.ev[-1])
         per_sorted = sorted(per)
-        return dict(ms=total / len(per), ms_median=per_sorted[len(per) // 2], ms_min=per_sorted[0])
+        out = dict(ms=total / len(per), ms_median=per_sorted[len(per) // 2], ms_min=per_sorted[0])
+        if self.after is not None:
+            own = sorted(self.ev[i].elapsed_time(self.after[i]) for i in range(len(self.after)))
+            out.update(ms_launch=sum(own) / len(own), ms_launch_median=own[len(own) // 2])
+        return out
 
 
 def _timed(step, steps, warmup):
+    """Times `steps` back-to-back steps (the throughput), then the same number
+    again with an event right after each launch (each launch's own duration,
+    which is what the kernel-trace profile reports; the extra events lengthen
+    the steps of that second loop, so it gives no throughput)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    t = StepTimer(steps)
-    for i in range(steps):
-        t.mark(i)
-        step(i)
-    t.mark(steps)
-    r = t.result()
-    torch.cuda.synchronize()
-    return r
+    out = None
+    for bracket in (False, True):
+        t = StepTimer(steps, bracket)
+        for i in range(steps):
+            t.mark(i)
+            step(i)
+            t.mark_after(i)
+        t.mark(steps)
+        r = t.result()
+        torch.cuda.synchronize()
+        if out is None:
+            out = r
+        else:
+            out.update(ms_launch=r["ms_launch"], ms_launch_median=r["ms_launch_median"])
+    return out
 
 
 def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
@@ -116,8 +138,10 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
     nbytes = tok * w.nheads * bpt + w.batch * w.nheads * w.dstate * w.headdim * 4
     flops = tok * w.nheads * prefill_flops_per_token_head(w, q_used)
     del sets, ys, hs, ws
+    msl = r["ms_launch"]
     return dict(r, tokens_per_s=tok / (ms * 1e-3), chunk=q_used, bytes=nbytes, flops=flops,
-                gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12)
+                gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
+                gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
 
 def bench_decode(w, steps, warmup, nstate=3):
@@ -143,7 +167,8 @@ def bench_decode(w, steps, warmup, nstate=3):
     nbytes = upd * decode_bytes_per_update(w)
     del d, hs
     return dict(r, updates_per_s=upd / (ms * 1e-3), tokens_per_s=w.batch / (ms * 1e-3),
-                bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
+                bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                gbs_launch=nbytes / (r["ms_launch"] * 1e-3) / 1e9)
 
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
@@ -216,7 +241,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="siso", choices=["siso", "mimo", "long", "decode", "tiny"])
     ap.add_argument("--chunk", type=int, default=0, help="prefill tokens per chunk (0: library default)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -238,9 +263,9 @@ def main():
         r = bench_decode(w, args.steps * 10, args.warmup * 10)
         value, unit, ms = r["updates_per_s"], "state-updates/s", r["ms"]
         traffic = measured_traffic("decode_kernel_decode")
-        roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic, kernel="decode_kernel",
-                    algorithmic_bytes_per_launch=r["bytes"])
+        roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(r["gbs_launch"] / HBM_PEAK_GBS, 4), traffic=traffic, kernel="decode_kernel",
+                    algorithmic_bytes_per_launch=r["bytes"], us_per_launch=round(r["ms_launch"] * 1e3, 2))
         config = dict(workload=f"decode: {w.batch} seq x {w.nheads} heads, N={w.dstate}, P={w.headdim}, "
                                f"R={w.rank}, bf16 in, fp32 state",
                       batch=w.batch, nheads=w.nheads, dstate=w.dstate, headdim=w.headdim, rank=w.rank,
@@ -250,12 +275,13 @@ def main():
         r = bench_prefill(w, args.steps, args.warmup, chunk=args.chunk)
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
         traffic = measured_traffic(f"prefill_kernel_{w.name}_q{r['chunk']}")
-        roof = dict(bound="hbm", achieved=round(r["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+        roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(r["gbs_launch"] / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="prefill_kernel (the step also runs a ~2 us reset_kernel)",
                     algorithmic_bytes_per_launch=r["bytes"],
-                    mfma_tflops=round(r["tflops"], 2),
-                    mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+                    us_per_launch=round(r["ms_launch"] * 1e3, 2),
+                    mfma_tflops=round(r["tflops_launch"], 2),
+                    mfma_frac=round(r["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4))
         config = dict(workload=f"{w.name} prefill: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
                                f"N={w.dstate}, R={w.rank}, {w.dtype} in, fp32 state",
                       batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, dstate=w.dstate,
@@ -270,11 +296,12 @@ def main():
         sec = {}
         def pre(name, chunk, steps):
             wl = inputs.WORKLOADS[name]
-            rr = bench_prefill(wl, steps, 2, chunk=chunk)
+            rr = bench_prefill(wl, steps, args.warmup if name == "siso" else max(2, args.warmup // 5), chunk=chunk)
             return dict(tokens_per_s_layer=rr["tokens_per_s"], us=round(rr["ms"] * 1e3, 1),
                         us_median=round(rr["ms_median"] * 1e3, 1), chunk=rr["chunk"],
-                        hbm_frac=round(rr["gbs"] / HBM_PEAK_GBS, 4),
-                        mfma_frac=round(rr["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+                        us_per_launch=round(rr["ms_launch"] * 1e3, 1),
+                        hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
+                        mfma_frac=round(rr["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4))
         sec["siso_prefill_chunk64"] = pre("siso", 64, args.steps)
         sec["mimo_prefill"] = pre("mimo", 0, args.steps)
         sec["long_prefill"] = pre("long", 0, max(3, args.steps // 4))
@@ -282,7 +309,8 @@ def main():
         rd = bench_decode(wd, 200, 30)
         sec["mimo_decode"] = dict(state_updates_per_s=rd["updates_per_s"], us_per_step=round(rd["ms"] * 1e3, 1),
                                   us_median=round(rd["ms_median"] * 1e3, 1),
-                                  hbm_gbs=round(rd["gbs"], 1), hbm_frac=round(rd["gbs"] / HBM_PEAK_GBS, 4),
+                                  us_per_launch=round(rd["ms_launch"] * 1e3, 1),
+                                  hbm_gbs=round(rd["gbs_launch"], 1), hbm_frac=round(rd["gbs_launch"] / HBM_PEAK_GBS, 4),
                                   table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
         out["secondary"] = sec
     if not args.no_cpu_baseline:
