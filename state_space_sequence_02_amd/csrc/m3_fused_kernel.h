@@ -62,8 +62,6 @@
 namespace m3 {
 namespace fused {
 
-constexpr int kThreads = kFusedThreads;
-constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBatch = 12;         // 16-byte B/X loads per thread per batch, at most
 constexpr unsigned kSpinLimit = 1u << 20;
 constexpr int kMapGroup = 1;        // predecessor maps loaded per round trip
@@ -89,6 +87,7 @@ struct Lds {
 // segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
 __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize) {
   const int QRp = round_up_i(Q * R, 32);
+  const int kWaves = fused_threads(N) / 64;
   const size_t scan = sizeof(float) * kWaves + sizeof(float4) * (size_t)kWaves * (N / 8);
   Lds o;
   o.row = 0;
@@ -124,12 +123,13 @@ __device__ __forceinline__ void mem_done() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-// Every wave of the workgroup calls this once after mem_done(); the last one
-// to arrive raises flag `f` to `val`.  `ctr` is an LDS counter starting at 0.
-__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned* f, unsigned val) {
+// Every one of the workgroup's `nwaves` waves calls this once after
+// mem_done(); the last one to arrive raises flag `f` to `val`.  `ctr` is an
+// LDS counter starting at 0.
+__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned* f, unsigned val, int nwaves) {
   if ((threadIdx.x & 63) == 0) {
     const int n = atomicAdd(ctr, 1);
-    if (n == kWaves - 1) __hip_atomic_store(f, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n == nwaves - 1) __hip_atomic_store(f, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -288,13 +288,16 @@ __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
 
 // RT: output row tiles per wave (the chunk has at most RT * 16 * kWaves rows);
 // register arrays are sized by it.
-// Two workgroups per CU need at most 128 VGPRs (4 waves per SIMD); the
-// instantiations that come close are held to it.
+// Waves per SIMD the register allocation must allow: two 512-thread
+// workgroups per CU (128 VGPRs) for the instantiations that come close to it,
+// and a 1024-thread workgroup needs 4 anyway.
 template <int N, int RT>
-constexpr int prefill_waves_per_simd() { return (N <= 64 && RT <= 2) ? 4 : 2; }
+constexpr int prefill_waves_per_simd() { return (fused_threads(N) == 1024 || (N <= 64 && RT <= 2)) ? 4 : 2; }
 
 template <typename T, int N, int P, int R, int RT>
-__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<N, RT>())) void prefill_kernel(FusedParams p) {
+__global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())) void prefill_kernel(FusedParams p) {
+  constexpr int kThreads = fused_threads(N);
+  constexpr int kWaves = kThreads / 64;
   constexpr int NH = N / 2;
   constexpr int NG = NH / 4;                  // 4-pair column groups of the angle table
   constexpr int CSS = NH + 1;                 // angle table row stride (float2): rows 2 banks apart
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<N, RT>())) void p
       }
     }
     mem_done();
-    arrive_and_flag(&s_misc[3], flags + c, 1u);
+    arrive_and_flag(&s_misc[3], flags + c, 1u, kWaves);
   }
 
   // ---- D: S_in by look-back; S_out = a R(Psi) S_in + U ----
@@ -880,7 +883,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<N, RT>())) void p
   // raise the flag before the intra-chunk work
   if (publish) {
     mem_done();
-    arrive_and_flag(&s_misc[4], flags + c, 2u);
+    arrive_and_flag(&s_misc[4], flags + c, 2u, kWaves);
   }
   for (int sb = 0; sb <= sbmax; ++sb) {
     // S^T block = B~[32 rows of block sb] C~[tile]^T, for every tile of the wave
@@ -999,19 +1002,21 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   hipLaunchKernelGGL(reset_kernel<0>, dim3(rblocks), dim3(256), 0, stream, p.counter, p.flags, nflags);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t grid = nflags;
-  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT>), dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, p);
   return hipGetLastError();
 }
 
-// Row tiles per wave for a chunk of Q tokens x R ranks (rows rounded up to 32).
-inline int row_tiles_per_wave(int Q, int R) {
-  const int rows = round_up_i(Q * R, 32);
-  return (rows / 16 + kWaves - 1) / kWaves;
+// Row tiles per wave for a chunk of Q tokens x R ranks (rows rounded up to 32)
+// shared out over the waves of an N-state workgroup.
+inline int row_tiles_per_wave(int Q, int R, int N) {
+  const int rows = round_up_i(Q * R, 32), waves = fused_threads(N) / 64;
+  return (rows / 16 + waves - 1) / waves;
 }
 
 template <typename T, int N, int P, int R>
 hipError_t launch_rt(const FusedParams& p, size_t lds, hipStream_t s) {
-  const int rt = row_tiles_per_wave(p.Q, R);
+  const int rt = row_tiles_per_wave(p.Q, R, N);
+  constexpr int kWaves = fused_threads(N) / 64;
   constexpr int kMaxRT = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;
   if (rt <= 1) return launch<T, N, P, R, 1>(p, lds, s);
   if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1)>(p, lds, s);

@@ -51,16 +51,17 @@ struct FusedParams {
   unsigned* counter; unsigned* flags; float* recs; float* maps; float* states;
   int batch, L, H, N, P, R, logR, Q, nc;
 };
-// Threads per prefill workgroup, and the floats one chunk's map or state
-// occupies in the workspace: each thread stores its state tiles (n-tile x
-// p-tile of 16 x 16 shared out over the 8 waves as NPW x PTW tiles per wave,
-// 4 floats per lane) contiguously.
-constexpr int kFusedThreads = 512;
+// Threads per prefill workgroup: 1024 for N >= 128 (one workgroup fills a CU
+// there, and twice the waves share each chunk's work), 512 below.
+__host__ __device__ constexpr int fused_threads(int N) { return N >= 128 ? 1024 : 512; }
+// Floats one chunk's map or state occupies in the workspace: each thread
+// stores its state tiles (n-tile x p-tile of 16 x 16 shared out over the
+// waves as NPW x PTW tiles per wave, 4 floats per lane) contiguously.
 __host__ __device__ constexpr int fused_slot_floats(int N, int P) {
-  return ((N / 16) / ((N / 16) < kFusedThreads / 64 ? (N / 16) : kFusedThreads / 64)) *
-         (((P / 16) + (kFusedThreads / 64) / ((N / 16) < kFusedThreads / 64 ? (N / 16) : kFusedThreads / 64) - 1) /
-          ((kFusedThreads / 64) / ((N / 16) < kFusedThreads / 64 ? (N / 16) : kFusedThreads / 64))) *
-         kFusedThreads * 4;
+  return ((N / 16) / ((N / 16) < fused_threads(N) / 64 ? (N / 16) : fused_threads(N) / 64)) *
+         (((P / 16) + (fused_threads(N) / 64) / ((N / 16) < fused_threads(N) / 64 ? (N / 16) : fused_threads(N) / 64) - 1) /
+          ((fused_threads(N) / 64) / ((N / 16) < fused_threads(N) / 64 ? (N / 16) : fused_threads(N) / 64))) *
+         fused_threads(N) * 4;
 }
 // Chunk limits of the single-pass prefill: (token, rank) rows per chunk and
 // angles (tokens x N/2) per chunk; they bound the per-thread prefetch registers.

@@ -113,11 +113,13 @@ def test_workspace_size_matches_layout(lib, name):
     bhc = w.batch * w.nheads * nc
     a = lambda v: (v + 255) // 256 * 256
     # control block | flags | per-chunk records | maps | states; a map or state
-    # slot holds each of the 512 threads' NPW x PTW state tiles (16 x 16 tiles
-    # shared out over 8 waves), 4 floats per lane
+    # slot holds each thread's NPW x PTW state tiles (16 x 16 tiles shared out
+    # over the waves: 1024 threads for N >= 128, else 512), 4 floats per lane
+    threads = 1024 if w.dstate >= 128 else 512
+    waves = threads // 64
     tn, tp = w.dstate // 16, w.headdim // 16
-    ngrp = min(tn, 8)
-    slot = (tn // ngrp) * (-(-tp // (8 // ngrp))) * 512 * 4
+    ngrp = min(tn, waves)
+    slot = (tn // ngrp) * (-(-tp // (waves // ngrp))) * threads * 4
     assert slot >= w.dstate * w.headdim
     recs = a(256 + bhc * 4)
     maps = a(recs + bhc * (w.dstate + 2) * 4)
