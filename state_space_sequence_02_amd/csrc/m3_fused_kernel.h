@@ -79,10 +79,20 @@ struct Lds {
   size_t row, rw, W, csH, B, X, misc, total;
   size_t segl, sega;   // scan scratch, inside B (used only before B~ is staged)
 };
+// LDS row stride (elements) of the X tile.  bf16 X is read with 8-byte
+// transposing reads in which 16 lanes take 4 columns of 4 consecutive rows:
+// a stride of 8 or 24 banks (16 or 48 elements mod 64) puts the 4 rows on
+// disjoint banks.  fp32 X is read one element per lane along a row.
+__host__ __device__ constexpr int x_stride(int P, int esize) {
+  return esize == 2 ? (P == 16 ? 16 : P + 16) : P + 8;
+}
+
 // row: per (token, rank) row float4 {l, w, gamma, W}
 // rw: per row exp(l_be - l) w with be the last row of the row's 32-row block
 //     (the factored decay of the off-diagonal mask blocks);  W: per row W
-// csH: cos/sin of Phi [Q][N/2 + 1] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8]
+// csH: cos/sin of Phi [Q][N/2 + 1] while B~, C~ and R(Psi) are formed, then S_in^T [P][N+8].
+//      Within a row, pair k = 4g + j is at column j * N/8 + g: the 16 lanes of an
+//      access that take consecutive groups g of one row read consecutive entries.
 // B: B~ [QRp][N+8];  X: X [QRp][P+8] (permuted columns)
 // segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
 __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize) {
@@ -96,7 +106,7 @@ __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize)
   o.csH = o.W + sizeof(float) * QRp;
   o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2 + 1), (size_t)esize * P * (N + 8)), 16);
   o.X = o.B + round_up_i((int)max_sz((size_t)esize * QRp * (N + 8), scan), 16);
-  o.misc = o.X + (size_t)esize * QRp * (P + 8);
+  o.misc = o.X + (size_t)esize * QRp * x_stride(P, esize);
   o.total = o.misc + 32;
   o.segl = o.B;
   o.sega = o.B + sizeof(float) * kWaves;
@@ -175,11 +185,12 @@ template <> __device__ __forceinline__ void store8<float>(float* d, const float 
   reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// R(-phi) on the 4 pairs of 8 consecutive state entries (even start), cos/sin from cs.
-__device__ __forceinline__ void rotate_neg(float (&v)[8], const float2* cs) {
+// R(-phi) on the 4 pairs of 8 consecutive state entries (even start); the
+// cos/sin of pair j are at cs[j * stride].
+__device__ __forceinline__ void rotate_neg(float (&v)[8], const float2* cs, int stride) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float2 q = cs[j];
+    const float2 q = cs[j * stride];
     const float u = v[2 * j], w = v[2 * j + 1];
     v[2 * j] = q.x * u + q.y * w;
     v[2 * j + 1] = -q.y * u + q.x * w;
@@ -243,17 +254,37 @@ __device__ __forceinline__ void buf_store_dev4(Rsrc r, uint32_t off, f32x4 v) {
 }
 
 // Stores the 8 head columns c0..c0+7 of one X row into the permuted LDS row:
-// head column c goes to LDS column (c % TPt) * 16 + c / TPt.
+// head column c goes to LDS column (c % TPt) * 16 + c / TPt.  The 8/TPt
+// columns that land side by side go out as one store (c0 is a multiple of 8,
+// so such a run starts on a multiple of its own size).
 template <int TPt, typename T>
 __device__ __forceinline__ void store_x_permuted(T* row, int c0, const Raw8<T>& r) {
   T v[8];
   static_assert(sizeof(Raw8<T>) == sizeof(v), "raw size");
   __builtin_memcpy(v, &r, sizeof(v));
+  constexpr int RUN = TPt < 8 ? 8 / TPt : 1;   // consecutive LDS columns per store
 #pragma unroll
   for (int t = 0; t < (TPt < 8 ? TPt : 8); ++t) {
     T* d = row + t * 16 + c0 / TPt;
+    T run[RUN];
 #pragma unroll
-    for (int m = 0; m < 8 / TPt; ++m) d[m] = v[t + m * TPt];
+    for (int m = 0; m < RUN; ++m) run[m] = v[t + m * TPt];
+    if constexpr (RUN * sizeof(T) == 4) {
+      uint32_t w;
+      __builtin_memcpy(&w, run, 4);
+      *reinterpret_cast<uint32_t*>(d) = w;
+    } else if constexpr (RUN * sizeof(T) == 8) {
+      uint2 w;
+      __builtin_memcpy(&w, run, 8);
+      *reinterpret_cast<uint2*>(d) = w;
+    } else if constexpr (RUN * sizeof(T) == 16) {
+      uint4 w;
+      __builtin_memcpy(&w, run, 16);
+      *reinterpret_cast<uint4*>(d) = w;
+    } else {
+#pragma unroll
+      for (int m = 0; m < RUN; ++m) d[m] = run[m];
+    }
   }
 }
 
@@ -301,6 +332,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   constexpr int NH = N / 2;
   constexpr int NG = NH / 4;                  // 4-pair column groups of the angle table
   constexpr int CSS = NH + 1;                 // angle table row stride (float2): rows 2 banks apart
+  // angle table column of pair k (4-pair group k/4, slot k%4)
+  auto cs_col = [](int k) { return (k & 3) * NG + (k >> 2); };
   constexpr int NK = (N + 31) / 32;           // 32-wide slices of the state dimension
   constexpr int TPt = P / 16;                 // 16-column tiles of the head dimension
   constexpr int TNt = N / 16;                 // 16-row tiles of the state dimension
@@ -310,7 +343,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   constexpr int WPN = kWaves / NGRP;
   constexpr int PTW = (TPt + WPN - 1) / WPN;
   constexpr int NS = N + 8;                   // LDS row stride of B~ and S_in^T
-  constexpr int XS = P + 8;                   // LDS row stride of X
+  constexpr int XS = x_stride(P, sizeof(T));  // LDS row stride of X
   constexpr int LOGR = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;
   constexpr int RTW = RT;                     // max output row tiles per wave
   // B/X loads per thread per batch: the whole chunk in one batch when it fits
@@ -507,11 +540,11 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
         __sincosf(ph.y, &s1, &c1);
         __sincosf(ph.z, &s2, &c2);
         __sincosf(ph.w, &s3, &c3);
-        float2* d = s_cs + (sg * ALEN + j) * CSS + 4 * cg;
+        float2* d = s_cs + (sg * ALEN + j) * CSS + cg;
         d[0] = make_float2(c0, s0);
-        d[1] = make_float2(c1, s1);
-        d[2] = make_float2(c2, s2);
-        d[3] = make_float2(c3, s3);
+        d[NG] = make_float2(c1, s1);
+        d[2 * NG] = make_float2(c2, s2);
+        d[3 * NG] = make_float2(c3, s3);
       }
     }
   }
@@ -540,7 +573,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
         const int row = i / (N / 8), ng = i - row * (N / 8);
         float v[8];
         raw_unpack(raw[u], v);
-        if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * CSS + ng * 4);
+        if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * CSS + ng, NG);
         store8<T>(s_B + row * NS + ng * 8, v);
       } else if (i >= nbp && i < ntot) {
         const int j = i - nbp;
@@ -560,7 +593,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
       const int n0 = kn * 32 + 8 * g4;
       float v[8];
       raw_unpack(craw[k][kn], v);
-      if (n0 < N) rotate_neg(v, s_cs + ta * CSS + n0 / 2);
+      if (n0 < N) rotate_neg(v, s_cs + ta * CSS + n0 / 8, NG);
 #pragma unroll
       for (int e = 0; e < 8; ++e) frag_set(cf[k][kn], e, v[e]);
     }
@@ -609,8 +642,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
     const int k0 = ((nslot + NGRP * i) * 16 + 4 * g4) >> 1;
-    psi[i][0] = s_cs[(nt - 1) * CSS + k0];
-    psi[i][1] = s_cs[(nt - 1) * CSS + k0 + 1];
+    psi[i][0] = s_cs[(nt - 1) * CSS + cs_col(k0)];
+    psi[i][1] = s_cs[(nt - 1) * CSS + cs_col(k0 + 1)];
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       f32x4& u = uacc[i][j];
