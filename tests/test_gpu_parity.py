@@ -66,6 +66,10 @@ SMALL = [
     dict(name="mimo", kw=dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=128, rank=2), chunk=32),
     dict(name="mimo", kw=dict(batch=1, seqlen=64, nheads=1, headdim=64, dstate=256, rank=1), chunk=32),
     dict(name="long", kw=dict(seqlen=515, nheads=2), chunk=128),
+    # 256 and 512 (token, rank) rows per chunk: two and four 16-row output tiles per wave
+    dict(name="siso", kw=dict(batch=1, seqlen=600, nheads=2), chunk=256),
+    dict(name="mimo", kw=dict(batch=1, seqlen=300, nheads=2, headdim=64, dstate=32, rank=4), chunk=128),
+    dict(name="tiny", kw=dict(batch=1, seqlen=700, nheads=2, headdim=32, dstate=16, rank=2), chunk=256),
 ]
 
 
