@@ -87,11 +87,25 @@ class StepTimer:
         return out
 
 
+PREWARM_S = 0.3
+
+
 def _timed(step, steps, warmup):
     """Times `steps` back-to-back steps (the throughput), then the same number
     again with an event right after each launch (each launch's own duration,
     which is what the kernel-trace profile reports; the extra events lengthen
-    the steps of that second loop, so it gives no throughput)."""
+    the steps of that second loop, so it gives no throughput).
+
+    Before the `warmup` untimed steps the step runs for PREWARM_S seconds of
+    wall time: the GPU takes tens of milliseconds of steady work to reach its
+    running clocks, longer than a few hundred 50 us steps."""
+    t_end = time.perf_counter() + PREWARM_S
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()

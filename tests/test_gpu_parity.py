@@ -205,6 +205,50 @@ def test_decode_several_pairs_per_workgroup():
     check_blocks(to64(h), hr, tol, (2, 3), "decode h")
 
 
+def test_decode_graph_replay_matches_eager():
+    """Decode steps captured in a HIP graph give the eager calls' bits on every
+    replay, with unrelated eager work and synchronisations between replays."""
+    w = inputs.workload("decode", batch=4, nheads=8, headdim=64, dstate=128, rank=4, dtype="bf16")
+    steps = 3
+    d = inputs.make_decode_inputs(w, seed=31, steps=steps)
+    dg = dev_inputs(d)
+    h0 = (torch.randn((w.batch, w.nheads, w.dstate, w.headdim), generator=torch.Generator().manual_seed(32))
+          * 0.5).to("cuda")
+
+    def run(h, ys):
+        for s in range(steps):
+            kw = dict(B_prev=dg["B"][s - 1], x_prev=dg["x"][s - 1]) if s else {}
+            m3.decode_step(h, dg["x"][s], dg["B"][s], dg["C"][s], dg["dt"][s], dg["A"], dg["lam"][s],
+                           dg["theta"][s], y=ys[s], **kw)
+
+    note("decode graph replay vs eager")
+    h_ref = h0.clone()
+    y_ref = [torch.empty_like(dg["x"][0]) for _ in range(steps)]
+    run(h_ref, y_ref)
+    torch.cuda.synchronize()
+    h = torch.empty_like(h0)
+    ys = [torch.empty_like(dg["x"][0]) for _ in range(steps)]
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run(h, ys)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.copy_(h0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_ref), f"state differs on replay {rep}"
+        for s in range(steps):
+            assert torch.equal(ys[s], y_ref[s]), f"y of step {s} differs on replay {rep}"
+        float(torch.randn(4096, device="cuda").square().sum())   # unrelated eager work
+
+
 def test_prefill_then_decode_handoff():
     """prefill(L - k) followed by k decode steps equals prefill(L)."""
     w = inputs.workload("mimo", batch=2, seqlen=133, nheads=2)
