@@ -122,3 +122,39 @@ def decode_steps(h0, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None,
     y, h = scan(tok_major(x), tok_major(B), tok_major(C), tok_major(dt), A, tok_major(lam),
                 tok_major(theta), h0, B_prev, x_prev, nthreads=nthreads)
     return np.ascontiguousarray(np.moveaxis(y, 1, 0)), h
+
+
+def round_bf16(a) -> np.ndarray:
+    """Each value rounded to the nearest bfloat16 number, ties to even, returned
+    as float64.  bfloat16 keeps 8 significant bits with float32's exponent
+    range: a normal number's spacing is 2^(e-8) for a value in [2^(e-1), 2^e),
+    and below the smallest normal, 2^-126, the spacing is 2^-133.  numpy's
+    `round` rounds halves to even."""
+    v = _as64(a)
+    m, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133).astype(np.float64)
+    return np.round(np.ldexp(v, (-q).astype(np.int64))) * np.exp2(q)
+
+
+def decode_steps_bf16_state(h0, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None,
+                            nthreads: int = 0):
+    """Successive single-token steps with the state held in bfloat16 between
+    steps (the paper page's Table 6 benchmarks decode with an FP32 or a BF16
+    state): each step is the float64 recurrence of `scan` (explainer panel 3's
+    physical-frame loop, one token) from the stored state, y is read from the
+    updated state before it is stored, and the stored state is the updated state
+    rounded to bfloat16.  h0 is rounded the same way before the first step.
+    Shapes as `decode_steps`; returns (y [S,b,H,R,P], h_final [b,H,N,P])."""
+    x, B, C, dt, lam = map(_as64, (x, B, C, dt, lam))
+    theta, B_prev, x_prev = map(_as64, (theta, B_prev, x_prev))
+    S = x.shape[0]
+    h = round_bf16(h0)
+    ys = []
+    for s in range(S):
+        bp, xp = (B[s - 1], x[s - 1]) if s else (B_prev, x_prev)
+        th = None if theta is None else theta[s][:, None]
+        y, h_new = scan(x[s][:, None], B[s][:, None], C[s][:, None], dt[s][:, None], A, lam[s][:, None],
+                        th, h, bp, xp, nthreads=nthreads)
+        ys.append(y[:, 0])
+        h = round_bf16(h_new)
+    return np.stack(ys), h

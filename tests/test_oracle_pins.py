@@ -363,3 +363,46 @@ def test_decode_steps_wrapper_equals_scan():
                              h0=hs, **kw)
         np.testing.assert_allclose(y[s], ys[:, 0], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(h, hs, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 state between decode steps (paper page Table 6: FP32 or BF16 state)
+
+def test_round_bf16_matches_torch_cast():
+    """The format's rounding against torch's float32 -> bfloat16 cast (round to
+    nearest even) on float32 values: random magnitudes, exact ties between
+    neighbouring bfloat16 numbers, values already in bfloat16, subnormals."""
+    import torch
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(20000) * np.exp2(rng.integers(-140, 120, 20000))
+    bf = torch.tensor(rng.standard_normal(4000), dtype=torch.bfloat16).double().numpy()
+    ulp = np.exp2(np.frexp(bf)[1] - 8.0)
+    ties = np.concatenate([bf + ulp / 2, bf - ulp / 2, bf])
+    tiny = rng.standard_normal(2000) * 1e-39
+    vals = np.concatenate([v, ties, tiny]).astype(np.float32).astype(np.float64)
+    ref = torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    got = oracle.round_bf16(vals)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_state_first_step_and_representable_states():
+    """Step 1 from a bfloat16 h0 reads the same y as the float64 step and stores
+    that step's state rounded; every stored state is a bfloat16 number; over 24
+    steps the state stays within the accumulated rounding bound of the float64
+    run (each step adds at most half a spacing, 2^-9 relative, and the update
+    does not amplify: |alpha| <= 1 and the rotation keeps norms)."""
+    w = inputs.workload("decode", batch=2, nheads=3, headdim=16, dstate=32, rank=2, dtype="bf16")
+    d = inputs.make_decode_inputs(w, seed=41, steps=24)
+    rng = np.random.default_rng(42)
+    h0 = oracle.round_bf16(rng.standard_normal((2, 3, 32, 16)))
+    args = (d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"])
+    y1, h1 = oracle.decode_steps_bf16_state(h0, *[a[:1] if i != 4 else a for i, a in enumerate(args)])
+    y1r, h1r = oracle.decode_steps(h0, *[a[:1] if i != 4 else a for i, a in enumerate(args)])
+    assert np.array_equal(y1, y1r)
+    assert np.array_equal(h1, oracle.round_bf16(h1r))
+    yb, hb = oracle.decode_steps_bf16_state(h0, *args)
+    yr, hr = oracle.decode_steps(h0, *args)
+    assert np.array_equal(oracle.round_bf16(hb), hb)
+    scale = max(np.abs(hr).max(), np.abs(h0).max())
+    assert np.abs(hb - hr).max() <= 24 * 2.0 ** -9 * scale * 2
+    assert np.abs(hb - hr).max() > 0          # the rounding is really applied
