@@ -48,9 +48,10 @@ def prefill_flops_per_token_head(w, q) -> float:
     return (q + 1) * R * R * (N + P) + 4 * N * P * R
 
 
-def decode_bytes_per_update(w) -> int:
+def decode_bytes_per_update(w, state_bytes=4) -> int:
     es, R, N, P = esize(w), w.rank, w.dstate, w.headdim
-    return 2 * N * P * 4 + R * P * es + 2 * R * N * es + R * N * es + R * P * es + 8 + (N // 2) * 4 + R * P * es
+    return (2 * N * P * state_bytes + R * P * es + 2 * R * N * es + R * N * es + R * P * es + 8 + (N // 2) * 4
+            + R * P * es)
 
 
 def table2_intensity(n, p, r):
@@ -158,14 +159,14 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
                 gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
 
-def bench_decode(w, steps, warmup, nstate=3):
+def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32):
     """One step = one m3_decode_step over all (sequence, head) pairs; >= 3 state
     buffers (384 MiB at the 128-sequence shape) rotate so a step cannot be served
     from the 256 MB last-level cache left warm by the previous step."""
     dev = torch.device("cuda")
     S = w.steps
     d = inputs.make_decode_inputs(w, seed=0, device=dev)
-    hs = [torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+    hs = [torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=state_dtype, device=dev)
           for _ in range(nstate)]
     y = torch.empty_like(d["x"][0])
 
@@ -178,7 +179,7 @@ def bench_decode(w, steps, warmup, nstate=3):
     r = _timed(step, steps, warmup)
     ms = r["ms"]
     upd = w.batch * w.nheads
-    nbytes = upd * decode_bytes_per_update(w)
+    nbytes = upd * decode_bytes_per_update(w, 2 if state_dtype == torch.bfloat16 else 4)
     del d, hs
     return dict(r, updates_per_s=upd / (ms * 1e-3), tokens_per_s=w.batch / (ms * 1e-3),
                 bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
@@ -326,6 +327,20 @@ def main():
                                   us_per_launch=round(rd["ms_launch"] * 1e3, 1),
                                   hbm_gbs=round(rd["gbs_launch"], 1), hbm_frac=round(rd["gbs_launch"] / HBM_PEAK_GBS, 4),
                                   table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
+        # the paper page's Table 6 decode settings: SISO and MIMO, state size 64
+        # or 128, fp32 or bf16 state (128 sequences x 32 heads, P=64)
+        def dec(name, state_dtype=torch.float32, **kw):
+            wl = inputs.workload("decode", **kw)
+            rr = bench_decode(wl, 200, 30, state_dtype=state_dtype)
+            sec[name] = dict(state_updates_per_s=rr["updates_per_s"], us_per_step=round(rr["ms"] * 1e3, 1),
+                             us_per_launch=round(rr["ms_launch"] * 1e3, 1),
+                             hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
+                             state="bf16" if state_dtype == torch.bfloat16 else "fp32",
+                             dstate=wl.dstate, rank=wl.rank)
+        dec("mimo_decode_bf16_state", torch.bfloat16)
+        dec("mimo_decode_n64", dstate=64)
+        dec("siso_decode_n128", rank=1)
+        dec("siso_decode_n64", rank=1, dstate=64)
         out["secondary"] = sec
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -141,6 +141,23 @@ m3_status m3_decode_step(const m3_shape* s,
                          const float* theta,
                          void* y, void* stream);
 
+/* m3_decode_step with the state held in bf16 between steps: the pages' decode
+ * kernels are benchmarked with an FP32 or a BF16 state (paper page, Table 6).
+ * Each step reads the bf16 state, does the update in fp32, reads y from the
+ * updated fp32 values and stores the state rounded to nearest even bf16.
+ *
+ *   h      [b, H, N, P]      bf16    state, read and written in place
+ *
+ * Every other argument is as for m3_decode_step; s->dtype must be M3_BF16
+ * (M3_ERR_DTYPE otherwise).  The same aliasing rules apply (M3_ERR_ALIAS). */
+m3_status m3_decode_step_bf16_state(const m3_shape* s,
+                                    void* h,
+                                    const void* B_prev, const void* x_prev,
+                                    const void* x, const void* B, const void* C,
+                                    const float* dt, const float* A, const float* lam,
+                                    const float* theta,
+                                    void* y, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_str(m3_status st);
 

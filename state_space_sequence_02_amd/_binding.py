@@ -19,7 +19,7 @@ M3_FP32, M3_BF16 = 0, 1
 STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
           4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS"}
 EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_scan_prefill",
-           "m3_decode_step", "m3_status_str", "m3_version")
+           "m3_decode_step", "m3_decode_step_bf16_state", "m3_status_str", "m3_version")
 
 
 class M3Shape(ctypes.Structure):
@@ -57,6 +57,8 @@ def load_library(path: str = LIB_PATH):
     lib.m3_scan_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.m3_decode_step_bf16_state.restype = ctypes.c_int
+    lib.m3_decode_step_bf16_state.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.m3_status_str.restype = ctypes.c_char_p
     lib.m3_status_str.argtypes = [ctypes.c_int]
     lib.m3_version.restype = ctypes.c_int32
@@ -144,7 +146,8 @@ def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=N
 
 
 def decode_step(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=None):
-    """One decode step (m3_decode_step); updates h [b,H,N,P] in place, returns y."""
+    """One decode step; updates h [b,H,N,P] in place, returns y.  An fp32 h calls
+    m3_decode_step, a bf16 h m3_decode_step_bf16_state."""
     lib = load_library()
     b, H, R, P = x.shape
     N = B.shape[-1]
@@ -154,8 +157,10 @@ def decode_step(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=
     if y is None:
         y = torch.empty_like(x)
     f32 = torch.float32
-    code = lib.m3_decode_step(
-        ctypes.byref(shape), _ptr(h, f32, dev), _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+    fn = lib.m3_decode_step_bf16_state if h.dtype == torch.bfloat16 else lib.m3_decode_step
+    code = fn(
+        ctypes.byref(shape), _ptr(h, h.dtype if h.dtype == torch.bfloat16 else f32, dev),
+        _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
         _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
         _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
         _ptr(y, x.dtype, dev), _stream(dev))

@@ -152,15 +152,19 @@ m3_status m3_scan_prefill(const m3_shape* s,
   return M3_OK;
 }
 
-m3_status m3_decode_step(const m3_shape* s,
-                         float* h,
-                         const void* B_prev, const void* x_prev,
-                         const void* x, const void* B, const void* C,
-                         const float* dt, const float* A, const float* lam,
-                         const float* theta,
-                         void* y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both decode entry points: the state is fp32 or (state_bf16) bf16.
+m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
+                        const void* B_prev, const void* x_prev,
+                        const void* x, const void* B, const void* C,
+                        const float* dt, const float* A, const float* lam,
+                        const float* theta, void* y, void* stream) {
   m3_status st = check_common(s, false);
   if (st != M3_OK) return st;
+  if (state_bf16 && s->dtype != M3_BF16) return M3_ERR_DTYPE;
   const int b = s->batch, H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
   const size_t es = esize(s->dtype);
   const size_t bh = (size_t)b * H;
@@ -169,7 +173,7 @@ m3_status m3_decode_step(const m3_shape* s,
   if (!h || !x || !B || !C || !dt || !A || !lam || !y) return M3_ERR_NULL;
 
   const size_t ybytes = bh * R * P * es;
-  const size_t hbytes = bh * N * P * sizeof(float);
+  const size_t hbytes = bh * N * P * (state_bf16 ? 2 : sizeof(float));
   struct { const void* p; size_t n; } ins[] = {
       {x, bh * R * P * es}, {B, bh * R * N * es}, {C, bh * R * N * es},
       {dt, bh * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, bh * sizeof(float)},
@@ -185,11 +189,35 @@ m3_status m3_decode_step(const m3_shape* s,
     return M3_ERR_ALIAS;
 
   DecodeParams p;
-  p.h = h; p.Bp = B_prev; p.xp = x_prev; p.x = x; p.B = B; p.C = C;
+  p.h = h; p.state_bf16 = state_bf16; p.Bp = B_prev; p.xp = x_prev; p.x = x; p.B = B; p.C = C;
   p.dt = dt; p.A = A; p.lam = lam; p.theta = theta; p.y = y;
   p.batch = b; p.H = H; p.N = N; p.P = P; p.R = R;
   if (launch_decode(p, s->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_decode_step(const m3_shape* s,
+                         float* h,
+                         const void* B_prev, const void* x_prev,
+                         const void* x, const void* B, const void* C,
+                         const float* dt, const float* A, const float* lam,
+                         const float* theta,
+                         void* y, void* stream) {
+  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, y, stream);
+}
+
+m3_status m3_decode_step_bf16_state(const m3_shape* s,
+                                    void* h,
+                                    const void* B_prev, const void* x_prev,
+                                    const void* x, const void* B, const void* C,
+                                    const float* dt, const float* A, const float* lam,
+                                    const float* theta,
+                                    void* y, void* stream) {
+  return decode_common(s, h, 1, B_prev, x_prev, x, B, C, dt, A, lam, theta, y, stream);
 }
 
 const char* m3_status_str(m3_status st) {

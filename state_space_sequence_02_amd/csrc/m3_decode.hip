@@ -148,7 +148,24 @@ constexpr int decode_threads(int N, int P) {
 
 // N and P are template parameters: the index arithmetic then needs no integer
 // division at run time.
-template <typename T, int R, int N, int P>
+// State access: fp32, or bf16 (4 values in 8 bytes, rounded to nearest even
+// when stored).  Non-temporal: the state is touched once per step.
+__device__ __forceinline__ float4 ld_state(const float* p) { return ld_stream4(p); }
+__device__ __forceinline__ void st_state(float* p, float4 v) { st_stream4(p, v); }
+__device__ __forceinline__ float4 ld_state(const bf16* p) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+}
+__device__ __forceinline__ void st_state(bf16* p, float4 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  auto b = [](float f) { return (unsigned)__builtin_bit_cast(uint16_t, static_cast<bf16>(f)); };
+  const u32x2 w = {b(v.x) | (b(v.y) << 16), b(v.z) | (b(v.w) << 16)};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+
+template <typename T, typename S, int R, int N, int P>
 __global__ __launch_bounds__(decode_threads(N, P)) void decode_kernel(DecodeParams p) {
   constexpr int NT = decode_threads(N, P);
   constexpr int UPT = (decode_units(N, P) + NT - 1) / NT;
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(decode_threads(N, P)) void decode_kernel(DecodePara
 
   const int q = tid % QP;                // constant across this thread's units
   constexpr int units = (N >> 1) * QP;
-  float* hg = p.h + (size_t)bh * N * P;
+  S* hg = static_cast<S*>(p.h) + (size_t)bh * N * P;
 
   const T* Bg = static_cast<const T*>(p.B) + (size_t)bh * R * N;
   const T* Cg = static_cast<const T*>(p.C) + (size_t)bh * R * N;
@@ -193,8 +210,8 @@ __global__ __launch_bounds__(decode_threads(N, P)) void decode_kernel(DecodePara
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int k = min(tid + i * NT, units - 1) / QP;
-    h0v[i] = ld_stream4(hg + (size_t)(2 * k) * P + 4 * q);
-    h1v[i] = ld_stream4(hg + (size_t)(2 * k + 1) * P + 4 * q);
+    h0v[i] = ld_state(hg + (size_t)(2 * k) * P + 4 * q);
+    h1v[i] = ld_state(hg + (size_t)(2 * k + 1) * P + 4 * q);
   }
 
   const float alpha = __expf(d * Ah);
@@ -237,8 +254,8 @@ __global__ __launch_bounds__(decode_threads(N, P)) void decode_kernel(DecodePara
         n0.x += c0 * xx.x; n0.y += c0 * xx.y; n0.z += c0 * xx.z; n0.w += c0 * xx.w;
         n1.x += c1 * xx.x; n1.y += c1 * xx.y; n1.z += c1 * xx.z; n1.w += c1 * xx.w;
       }
-      st_stream4(hg + (size_t)(2 * k) * P + 4 * q, n0);
-      st_stream4(hg + (size_t)(2 * k + 1) * P + 4 * q, n1);
+      st_state(hg + (size_t)(2 * k) * P + 4 * q, n0);
+      st_state(hg + (size_t)(2 * k + 1) * P + 4 * q, n1);
       const float* c0 = sC + (2 * k) * R;
       const float* c1 = c0 + R;
 #pragma unroll
@@ -275,55 +292,57 @@ __global__ __launch_bounds__(decode_threads(N, P)) void decode_kernel(DecodePara
   }
 }
 
-template <typename T, int R, int N, int P>
+template <typename T, typename S, int R, int N, int P>
 hipError_t dispatch_shape(const DecodeParams& p, hipStream_t stream) {
   constexpr int nt = decode_threads(N, P);
   constexpr int nwaves = nt / 64;
   const size_t lds = sizeof(float) * (3 * (size_t)N * R + 2 * (size_t)R * P + N +
                                       (size_t)nwaves * R * P);   // sW, sC, sXX, sCS, sRed
-  hipLaunchKernelGGL((decode_kernel<T, R, N, P>), dim3(p.batch * p.H), dim3(nt), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<T, S, R, N, P>), dim3(p.batch * p.H), dim3(nt), lds, stream, p);
   return hipGetLastError();
 }
 
-template <typename T, int R, int N>
+template <typename T, typename S, int R, int N>
 hipError_t dispatch_p(const DecodeParams& p, hipStream_t stream) {
   switch (p.P) {
-    case 16: return dispatch_shape<T, R, N, 16>(p, stream);
-    case 32: return dispatch_shape<T, R, N, 32>(p, stream);
-    case 64: return dispatch_shape<T, R, N, 64>(p, stream);
-    case 128: return dispatch_shape<T, R, N, 128>(p, stream);
+    case 16: return dispatch_shape<T, S, R, N, 16>(p, stream);
+    case 32: return dispatch_shape<T, S, R, N, 32>(p, stream);
+    case 64: return dispatch_shape<T, S, R, N, 64>(p, stream);
+    case 128: return dispatch_shape<T, S, R, N, 128>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, int R>
+template <typename T, typename S, int R>
 hipError_t dispatch_n(const DecodeParams& p, hipStream_t stream) {
   switch (p.N) {
-    case 16: return dispatch_p<T, R, 16>(p, stream);
-    case 32: return dispatch_p<T, R, 32>(p, stream);
-    case 64: return dispatch_p<T, R, 64>(p, stream);
-    case 128: return dispatch_p<T, R, 128>(p, stream);
-    case 256: return dispatch_p<T, R, 256>(p, stream);
+    case 16: return dispatch_p<T, S, R, 16>(p, stream);
+    case 32: return dispatch_p<T, S, R, 32>(p, stream);
+    case 64: return dispatch_p<T, S, R, 64>(p, stream);
+    case 128: return dispatch_p<T, S, R, 128>(p, stream);
+    case 256: return dispatch_p<T, S, R, 256>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, typename S>
 hipError_t dispatch_rank(const DecodeParams& p, hipStream_t stream) {
   switch (p.R) {
-    case 1: return dispatch_n<T, 1>(p, stream);
-    case 2: return dispatch_n<T, 2>(p, stream);
-    case 4: return dispatch_n<T, 4>(p, stream);
-    case 8: return dispatch_n<T, 8>(p, stream);
+    case 1: return dispatch_n<T, S, 1>(p, stream);
+    case 2: return dispatch_n<T, S, 2>(p, stream);
+    case 4: return dispatch_n<T, S, 4>(p, stream);
+    case 8: return dispatch_n<T, S, 8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+// A bf16 state is supported with bf16 inputs (the API rejects other pairings).
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
   if (p.batch == 0 || p.H == 0) return hipSuccess;
-  return dtype == M3_BF16 ? dispatch_rank<bf16>(p, stream) : dispatch_rank<float>(p, stream);
+  if (p.state_bf16) return dtype == M3_BF16 ? dispatch_rank<bf16, bf16>(p, stream) : hipErrorInvalidValue;
+  return dtype == M3_BF16 ? dispatch_rank<bf16, float>(p, stream) : dispatch_rank<float, float>(p, stream);
 }
 
 }  // namespace m3

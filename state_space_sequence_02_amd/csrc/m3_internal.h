@@ -73,7 +73,8 @@ hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hip
 // ---------------------------------------------------------------------------
 // Decode: one workgroup per (sequence, head).
 struct DecodeParams {
-  float* h;
+  void* h;               // fp32 or (state_bf16) bf16 state
+  int state_bf16;
   const void* Bp; const void* xp;
   const void* x; const void* B; const void* C;
   const float* dt; const float* A; const float* lam; const float* theta;

@@ -89,6 +89,21 @@ def _decode(lib, shape, **over):
                               args["y"], None)
 
 
+def test_decode_bf16_state_validation_codes(lib):
+    def call(shape, **over):
+        args = dict(h=FAKE[0], Bp=None, xp=None, x=FAKE[1], B=FAKE[2], C=FAKE[3], dt=FAKE[4], A=FAKE[5],
+                    lam=FAKE[6], theta=None, y=FAKE[7])
+        args.update(over)
+        return lib.m3_decode_step_bf16_state(ctypes.byref(shape), args["h"], args["Bp"], args["xp"], args["x"],
+                                             args["B"], args["C"], args["dt"], args["A"], args["lam"],
+                                             args["theta"], args["y"], None)
+    ok = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
+    assert call(m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_FP32)) == 3     # bf16 state needs bf16 inputs
+    assert call(ok, h=None) == 1
+    assert call(ok, y=FAKE[0]) == 6                                        # y aliases the state
+    assert call(m3.make_shape(0, 1, 2, 64, 128, 4, 0, m3.M3_BF16), h=None) == 0
+
+
 def test_decode_validation_codes(lib):
     ok = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
     assert _decode(lib, m3.make_shape(4, 1, 2, 64, 128, 4, 0, 5)) == 3

@@ -205,6 +205,36 @@ def test_decode_several_pairs_per_workgroup():
     check_blocks(to64(h), hr, tol, (2, 3), "decode h")
 
 
+@pytest.mark.parametrize("shape", [
+    dict(batch=3, nheads=2, headdim=64, dstate=128, rank=4),
+    dict(batch=2, nheads=3, headdim=64, dstate=64, rank=1),
+    dict(batch=1, nheads=2, headdim=128, dstate=256, rank=8),
+    dict(batch=20, nheads=32, headdim=64, dstate=128, rank=4),
+])
+def test_decode_bf16_state(shape):
+    """The state kept in bf16 between steps, against the oracle's bf16-state
+    decode (the update in high precision, the stored state rounded to nearest
+    even bf16)."""
+    w = inputs.workload("decode", dtype="bf16", **shape)
+    steps = 12 if w.batch * w.nheads < 100 else 3
+    d = inputs.make_decode_inputs(w, seed=51, steps=steps)
+    dg = dev_inputs(d)
+    h0 = torch.randn((w.batch, w.nheads, w.dstate, w.headdim), generator=torch.Generator().manual_seed(52)) * 0.5
+    h = h0.to(torch.bfloat16).to("cuda")
+    note(f"decode bf16 state b={w.batch} H={w.nheads} N={w.dstate} P={w.headdim} R={w.rank} steps={steps}")
+    ys = []
+    for s in range(steps):
+        kw = dict(B_prev=dg["B"][s - 1], x_prev=dg["x"][s - 1]) if s else {}
+        ys.append(m3.decode_step(h, dg["x"][s], dg["B"][s], dg["C"][s], dg["dt"][s], dg["A"], dg["lam"][s],
+                                 dg["theta"][s], **kw))
+    torch.cuda.synchronize()
+    yr, hr = oracle.decode_steps_bf16_state(h0.to(torch.bfloat16).double().numpy(), d["x"], d["B"], d["C"],
+                                            d["dt"], d["A"], d["lam"], d["theta"])
+    check_blocks(to64(torch.stack(ys)), yr, TOL["bf16"], (3, 4), "decode bf16-state y")
+    check_blocks(to64(h), hr, TOL["bf16"], (2, 3), "decode bf16-state h")
+    assert h.dtype == torch.bfloat16
+
+
 def test_decode_graph_replay_matches_eager():
     """Decode steps captured in a HIP graph give the eager calls' bits on every
     replay, with unrelated eager work and synchronisations between replays."""
