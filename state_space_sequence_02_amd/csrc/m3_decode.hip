@@ -1,6 +1,7 @@
 // m3_decode.hip -- single-token Mamba-3 decode step for gfx950.
 //
-// Per (sequence, head) the N x P fp32 state is read once and written once:
+// Per (sequence, head) the N x P state (fp32, or bf16 between steps: the paper
+// page's Table 6 benchmarks decode with either) is read once and written once:
 //   H <- R(phi)[alpha H + beta B_prev X_prev^T] + gamma B X^T,   Y = H^T C
 // (Mamba-3 explainer, panel 3 physical-frame loop with the two-endpoint rule of
 // panel 1 and the rank-R write/readout of panel 4 / Eqs. 12-14).  Decode is
@@ -10,7 +11,8 @@
 //
 // Work unit = (pair k, quad q): rows 2k and 2k+1, columns 4q..4q+3.  Consecutive
 // lanes take consecutive quads of the same row pair, so every load/store
-// instruction covers whole 16-byte-aligned runs of a row.  The rotation of a
+// instruction covers whole 16-byte-aligned runs of a row (8-byte runs for a
+// bf16 state).  The rotation of a
 // pair is lane-local because both of its rows sit in the same unit.
 // The coefficients are folded into the small operands once per workgroup:
 //   H <- [alpha R(phi)] H + sum_r (beta R(phi) B_prev)[:, r] x_prev[r]^T + (gamma B)[:, r] x[r]^T

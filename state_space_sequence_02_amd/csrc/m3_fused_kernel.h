@@ -1,8 +1,9 @@
 // m3_fused_kernel.h -- single-pass chunked Mamba-3 prefill kernel for gfx950.
 //
-// One workgroup (8 waves) per (sequence, chunk).  Each input element is read
-// from HBM once; besides the outputs a chunk writes one N x P fp32 state (and,
-// only when its successor would otherwise wait, its own affine map).
+// One workgroup per (sequence, chunk): 8 waves for N <= 64, 16 for N >= 128
+// (where a chunk needs a whole CU's LDS).  Each input element is read from HBM
+// once; besides the outputs a chunk writes one N x P fp32 state (and, when its
+// predecessor's state was not yet published, its own affine map).
 //
 // The arithmetic is the exact chunked rearrangement of the recurrence
 //   H_t = alpha_t R(phi_t) H_{t-1} + beta_t R(phi_t) V_{t-1} + gamma_t V_t,
@@ -25,21 +26,25 @@
 // scan"): chunk c's map S -> a_c R(Psi_c) S + U_c is affine, so a chunk whose
 // predecessor has not finished composes the predecessors' maps itself
 // (decoupled look-back).  Flags per chunk: 1 = map published, 2 = S_out
-// published.  A chunk publishes its map only when its predecessor's state is
-// not yet there.  Workgroups take chunk-major tickets from an atomic counter,
-// so every chunk a workgroup looks back at holds a lower ticket and is already
-// running: every wait ends.  A bounded spin turns a wait that never ends into
-// NaN outputs.  Cross-workgroup data moves with device-scope relaxed atomic
-// loads/stores; a wave waits for its stores to complete (s_waitcnt 0) and the
-// last wave to finish raises the flag (an LDS counter), so no cache-wide
-// write-back/invalidate and no workgroup barrier is needed to publish.
+// published.  Wave 0 reads the predecessors' flags right after staging; a
+// chunk publishes its map only when its predecessor's state was not there.
+// Workgroups take chunk-major tickets from an atomic counter, so every chunk a
+// workgroup looks back at holds a lower ticket and is already running: every
+// wait ends.  A bounded spin turns a wait that never ends into NaN outputs.
+// Maps and states move as 16-byte buffer loads/stores with the cache policy of
+// device-scope atomics, each lane's values in register order; flags and the
+// per-chunk records are device-scope relaxed atomics.  A wave waits for its
+// stores to complete (s_waitcnt 0) and the last wave to finish raises the flag
+// (an LDS counter), so no cache-wide write-back/invalidate and no workgroup
+// barrier is needed to publish.
 //
 // Work order inside a workgroup:
-//   A  all global loads issued; chunk-local cumulative log decay and phases:
-//      each thread scans its own tokens in registers, lanes combine with
-//      shuffles, waves with one barrier; cos/sin table of Phi in LDS
+//   A  all global loads issued (raw buffer loads, rows past the sequence end
+//      read as zeros); chunk-local cumulative log decay and phases: each
+//      thread scans its own tokens in registers, lanes combine with shuffles,
+//      waves with one barrier; cos/sin table of Phi in LDS
 //   B  stage B~ (rotated) and X in LDS; the wave's C~ rows are kept in
-//      registers as MFMA operands
+//      registers as MFMA operands; wave 0 polls the predecessors' flags
 //   C  U = R(Psi) sum_s W_s B~_s^T X_s on MFMA (operands by LDS transpose reads);
 //      publish the map if needed
 //   D  look back for S_in; S_out = a R(Psi) S_in + U; stores issued
@@ -49,8 +54,8 @@
 //
 // Column order: X is staged in LDS with its columns permuted so that the
 // 16-column MFMA tile pt holds head columns TPt*l + pt (l = 0..15, TPt = P/16).
-// U, the chunk states in the workspace, S_in^T and the output accumulators all
-// follow that order; a lane then holds TPt consecutive head columns of each of
+// U, the chunk states in the workspace (stored in register order), S_in^T and
+// the output accumulators all follow that order; a lane then holds TPt consecutive head columns of each of
 // its output rows, and y leaves as full row segments.  h0, h_out, x_prev and y
 // are read/written in the head's own column order.
 #pragma once
