@@ -72,8 +72,11 @@ typedef struct {
 } m3_shape;
 
 /* Bytes of device workspace m3_scan_prefill needs for this shape (0 on an
- * invalid or unsupported shape).  The buffer holds per-chunk states and needs
- * no initialisation; it may be reused across calls on the same stream. */
+ * invalid or unsupported shape).  The buffer holds the call's ticket counter,
+ * per-chunk flags and per-chunk states; it needs no initialisation (each call
+ * resets what it uses) and may be reused across calls on the same stream, but
+ * calls that may run at the same time (other streams) need workspaces of their
+ * own. */
 size_t m3_prefill_workspace_bytes(const m3_shape* s);
 
 /* Tokens per chunk m3_scan_prefill will actually use for this shape (the
