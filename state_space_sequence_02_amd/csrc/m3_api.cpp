@@ -148,6 +148,7 @@ m3_status m3_scan_prefill(const m3_shape* s,
   f.states = reinterpret_cast<float*>(ws + plan.off_states);
   f.batch = b; f.L = L; f.H = H; f.N = N; f.P = P; f.R = R; f.logR = ilog2(R);
   f.Q = plan.Q; f.nc = plan.nc;
+  f.use_maps = 1;   // (the launch decides from the device's resident workgroups)
   if (launch_fused_prefill(f, plan.lds, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
 }

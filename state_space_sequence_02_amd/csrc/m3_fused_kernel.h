@@ -61,6 +61,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 
 #include "m3_device.h"
 
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   // Publish the map only if the predecessor's state was not there at the poll.
   if (wave == 0) {
     const bool pred_state = (__ballot(lane < W0 && fpoll == 2u) & 1ull) != 0;
-    const int need_map = c > 0 && !pred_state;
+    const int need_map = p.use_maps && c > 0 && !pred_state;
     if (lane == 0) {
       s_misc[2] = need_map;
       if (need_map) st_dev2(p.recs + chunk_id * (2 * NH + 2), a_c, 0.f);   // the record's decay
@@ -1040,7 +1041,34 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   hipLaunchKernelGGL(reset_kernel<0>, dim3(rblocks), dim3(256), 0, stream, p.counter, p.flags, nflags);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t grid = nflags;
-  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, p);
+  // Maps let a chunk finish before its predecessor's state exists; they pay off
+  // only when many chunks of one sequence are in flight at once (few sequences
+  // x heads for the workgroups resident on the device): then consecutive
+  // chunks start closer together than a state takes to pass from one to the
+  // next.  With at most 4 in flight the state chain keeps up, and the maps'
+  // stores and waits would only cost time.
+  // (resident workgroups per device, cached with the LDS size they were
+  // computed for: one 64-bit word per device, so concurrent callers never see
+  // half an update)
+  static std::atomic<unsigned long long> cache[64];
+  int dev = 0, resident = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  const unsigned long long hit = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0ull;
+  if (hit != 0 && (hit >> 32) == (unsigned long long)lds) {
+    resident = (int)(hit & 0xffffffffull);
+  } else {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT>), fused_threads(N), lds) == hipSuccess)
+      resident = cus * per;
+    if (dev >= 0 && resident > 0)
+      cache[dev].store(((unsigned long long)lds << 32) | (unsigned)resident, std::memory_order_relaxed);
+  }
+  FusedParams q = p;
+  const size_t nbh = (size_t)p.batch * p.H;
+  q.use_maps = !(resident > 0 && (size_t)resident <= 4 * nbh);
+  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, q);
   return hipGetLastError();
 }
 

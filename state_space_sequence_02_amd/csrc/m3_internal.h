@@ -50,6 +50,7 @@ struct FusedParams {
   void* y; float* h_out;
   unsigned* counter; unsigned* flags; float* recs; float* maps; float* states;
   int batch, L, H, N, P, R, logR, Q, nc;
+  int use_maps;          // publish chunk maps when the predecessor's state is late
 };
 // Threads per prefill workgroup: 1024 for N >= 128 (one workgroup fills a CU
 // there, and twice the waves share each chunk's work), 512 below.

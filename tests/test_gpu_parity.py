@@ -80,6 +80,13 @@ def test_prefill_small(case, carry):
     _prefill_case(w, seed=3, carry=carry, chunk=case["chunk"])
 
 
+def test_prefill_many_pairs_state_chain():
+    """128 (sequence, head) pairs: at most 4 chunks of a sequence are resident at
+    once, so chunks hand over states only (no maps)."""
+    w = inputs.workload("siso", batch=4, seqlen=300, nheads=32)
+    _prefill_case(w, seed=61, carry=True, chunk=64, heads=[0, 13, 31])
+
+
 def test_prefill_without_rotation():
     w = inputs.workload("mimo", batch=1, seqlen=150, nheads=2, rotation=False)
     _prefill_case(w, seed=4, carry=True, chunk=32)
