@@ -72,11 +72,14 @@ typedef struct {
 } m3_shape;
 
 /* Bytes of device workspace m3_scan_prefill needs for this shape (0 on an
- * invalid or unsupported shape).  The buffer holds the call's ticket counter,
- * per-chunk flags and per-chunk states; it needs no initialisation (each call
- * resets what it uses) and may be reused across calls on the same stream, but
- * calls that may run at the same time (other streams) need workspaces of their
- * own. */
+ * invalid or unsupported shape, including one of more than 2^26 - 1 chunks).
+ * The buffer holds a control word (ticket count and call epoch), per-chunk
+ * flags and per-chunk states.  Zero-fill it once before its first use (e.g.
+ * hipMemset); every call leaves it ready for the next one, whatever shape that
+ * has, so it may be reused across calls on the same stream with nothing done in
+ * between.  Calls that may run at the same time (other streams) need workspaces
+ * of their own.  A workspace that was not zero-filled before its first use
+ * gives wrong results (never an access outside the buffers) until it is. */
 size_t m3_prefill_workspace_bytes(const m3_shape* s);
 
 /* Tokens per chunk m3_scan_prefill will actually use for this shape (the
@@ -105,7 +108,8 @@ int32_t m3_prefill_chunk_used(const m3_shape* s);
  *   y      [b, L, H, R, P]   dtype   out: y[b,t,h,r,p] = Y_t[p, r]
  *   h_out  [b, H, N, P]      fp32    out: H_{L-1} (physical frame), or NULL
  *   workspace, workspace_bytes       device scratch of at least
- *                                    m3_prefill_workspace_bytes(s)
+ *                                    m3_prefill_workspace_bytes(s), zero-filled
+ *                                    before its first use (see above)
  * Aliasing: h_out may equal h0.  y must not alias any input (M3_ERR_ALIAS).
  * With L = 0 nothing is computed and h_out (if given) receives h0 (or zeros). */
 m3_status m3_scan_prefill(const m3_shape* s,

@@ -119,7 +119,9 @@ def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=N
     x [b,L,H,R,P], B/C [b,L,H,R,N] (fp32 or bf16, same dtype); dt/lam [b,L,H],
     A [H], theta [b,L,H,N/2] fp32 or None; h0 [b,H,N,P] fp32 or None; B_prev
     [b,H,R,N] / x_prev [b,H,R,P] or None.  Returns (y, h_out).  Output and
-    workspace tensors are allocated with torch when not given.
+    workspace tensors are allocated with torch when not given (the workspace
+    zero-filled); a workspace passed in must have been zero-filled before its
+    first use and may then be passed to every later call on the same stream.
     """
     lib = load_library()
     b, L, H, R, P = x.shape
@@ -133,7 +135,7 @@ def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=N
         h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
     need = int(lib.m3_prefill_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     f32 = torch.float32
     code = lib.m3_scan_prefill(
         ctypes.byref(shape), _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),

@@ -64,9 +64,10 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
   plan->Q = q;
   plan->nc = s.seqlen > 0 ? (s.seqlen + q - 1) / q : 0;
   const size_t bhc = (size_t)s.batch * s.nheads * plan->nc;
+  if (bhc > kMaxChunks) return false;
   const size_t map = (size_t)fused_slot_floats(s.dstate, s.headdim) * sizeof(float);
   plan->off_flags = 256;
-  plan->off_recs = align256(plan->off_flags + bhc * sizeof(unsigned));
+  plan->off_recs = align256(plan->off_flags + bhc * sizeof(unsigned long long));
   plan->off_maps = align256(plan->off_recs + bhc * (s.dstate + 2) * sizeof(float));
   plan->off_states = align256(plan->off_maps + bhc * map);
   plan->bytes = align256(plan->off_states + bhc * map);
@@ -141,8 +142,8 @@ m3_status m3_scan_prefill(const m3_shape* s,
   FusedParams f;
   f.x = x; f.B = B; f.C = C; f.dt = dt; f.A = A; f.lam = lam; f.theta = theta;
   f.h0 = h0; f.Bp = B_prev; f.xp = x_prev; f.y = y; f.h_out = h_out;
-  f.counter = reinterpret_cast<unsigned*>(ws);
-  f.flags = reinterpret_cast<unsigned*>(ws + plan.off_flags);
+  f.ctl = reinterpret_cast<unsigned long long*>(ws);
+  f.flags = reinterpret_cast<unsigned long long*>(ws + plan.off_flags);
   f.recs = reinterpret_cast<float*>(ws + plan.off_recs);
   f.maps = reinterpret_cast<float*>(ws + plan.off_maps);
   f.states = reinterpret_cast<float*>(ws + plan.off_states);

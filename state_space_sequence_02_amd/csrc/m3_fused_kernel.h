@@ -26,7 +26,7 @@
 // scan"): chunk c's map S -> a_c R(Psi_c) S + U_c is affine, so a chunk whose
 // predecessor has not finished composes the predecessors' maps itself
 // (decoupled look-back).  Flags per chunk: 1 = map published, 2 = S_out
-// published.  Wave 0 reads the predecessors' flags right after staging; a
+// published, tagged with the call's epoch (a flag of another call reads as 0).  Wave 0 reads the predecessors' flags right after staging; a
 // chunk publishes its map only when its predecessor's state was not there.
 // Workgroups take chunk-major tickets from an atomic counter, so every chunk a
 // workgroup looks back at holds a lower ticket and is already running: every
@@ -142,7 +142,7 @@ __device__ __forceinline__ void mem_done() {
 // Every one of the workgroup's `nwaves` waves calls this once after
 // mem_done(); the last one to arrive raises flag `f` to `val`.  `ctr` is an
 // LDS counter starting at 0.
-__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned* f, unsigned val, int nwaves) {
+__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned long long* f, unsigned long long val, int nwaves) {
   if ((threadIdx.x & 63) == 0) {
     const int n = atomicAdd(ctr, 1);
     if (n == nwaves - 1) __hip_atomic_store(f, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -373,10 +373,27 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   int* s_misc = reinterpret_cast<int*>(smem + lay.misc);
 
   // ---- ticket: chunk-major order over all sequences ----
+  // (the taker of the last ticket readies the control word for the next call:
+  // count 0, next epoch; the modulo only keeps a workspace that was not
+  // zero-filled in bounds)
   const int nbh = p.batch * p.H;
-  if (tid == 0) s_misc[0] = (int)atomicAdd(p.counter, 1u);
+  if (tid == 0) {
+    const unsigned total = (unsigned)(nbh * p.nc);
+    const unsigned long long w = atomicAdd(p.ctl, 1ull);
+    const unsigned cnt = (unsigned)(w & kTicketMask);
+    const unsigned long long epoch = w >> kTicketBits;
+    if (cnt == total - 1)
+      __hip_atomic_store(p.ctl, (epoch + 1) << kTicketBits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_misc[0] = (int)(cnt % total);
+    s_misc[6] = (int)(unsigned)(epoch + 1);
+    s_misc[7] = (int)(unsigned)((epoch + 1) >> 32);
+  }
   __syncthreads();
   const int ticket = s_misc[0];
+  // this call's flag tag; flag_state() reads a flag of another call as 0
+  const unsigned long long tag = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(s_misc[7]) << 32) |
+                                 (unsigned)__builtin_amdgcn_readfirstlane(s_misc[6]);
+  auto flag_state = [&](unsigned long long f) { return (f >> 2) == tag ? (unsigned)(f & 3u) : 0u; };
   const int QRp = round_up_i(Q * R, 32);
   const int MT = QRp / 16;
   const size_t tstride = (size_t)p.H;           // token step in [b, L, H] arrays
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   const int nt = min(Q, p.L - t0);
   const int rows = nt * R;
   const size_t tok0 = tok_index(p, b, t0, h);
-  unsigned* flags = p.flags + (size_t)bh * p.nc;
+  unsigned long long* flags = p.flags + (size_t)bh * p.nc;
   const T* Bg = static_cast<const T*>(p.B) + tok0 * R * N;
   const T* Xg = static_cast<const T*>(p.x) + tok0 * R * P;
   const float A = p.A[h];
@@ -611,7 +628,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   const int W0 = min(c, 64);
   unsigned fpoll = 1u;
   if (wave == 0 && lane < W0)
-    fpoll = __hip_atomic_load(flags + c - 1 - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    fpoll = flag_state(__hip_atomic_load(flags + c - 1 - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 
   // ---- C: U[n][p] = R(Psi) sum_k W_k B~[k][n] X[k][p] ----
   // Lane layout of a (state tile ntl, column tile pt): rows n = 16 ntl + 4 g4 + j
@@ -692,7 +709,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
       }
     }
     mem_done();
-    arrive_and_flag(&s_misc[3], flags + c, 1u, kWaves);
+    arrive_and_flag(&s_misc[3], flags + c, tag << 2 | 1u, kWaves);
   }
 
   // ---- D: S_in by look-back; S_out = a R(Psi) S_in + U ----
@@ -750,7 +767,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
         while (true) {
           unsigned f = 1u;
           if (first) f = lane < W ? fpoll : 1u;
-          else if (lane < W) f = __hip_atomic_load(flags + hi - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else if (lane < W) f = flag_state(__hip_atomic_load(flags + hi - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
           first = false;
           const unsigned long long m2 = __ballot(lane < W && f == 2u);
           const unsigned long long m0 = __ballot(lane < W && f == 0u);
@@ -922,7 +939,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   // raise the flag before the intra-chunk work
   if (publish) {
     mem_done();
-    arrive_and_flag(&s_misc[4], flags + c, 2u, kWaves);
+    arrive_and_flag(&s_misc[4], flags + c, tag << 2 | 2u, kWaves);
   }
   for (int sb = 0; sb <= sbmax; ++sb) {
     // S^T block = B~[32 rows of block sb] C~[tile]^T, for every tile of the wave
@@ -1016,15 +1033,6 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   }
 }
 
-// Resets the ticket counter and the per-chunk flags (a kernel, not a memset, so
-// the call stays correct inside a captured graph).
-template <int Unused = 0>
-__global__ void reset_kernel(unsigned* counter, unsigned* flags, size_t nflags) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i == 0) *counter = 0u;
-  for (size_t j = i; j < nflags; j += (size_t)gridDim.x * blockDim.x) flags[j] = 0u;
-}
-
 template <typename T, int N, int P, int R, int RT>
 hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   // LDS limit raised once per instantiation
@@ -1036,11 +1044,7 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
       return e;
     lds_set = true;
   }
-  const size_t nflags = (size_t)p.batch * p.H * p.nc;
-  const unsigned rblocks = (unsigned)std::min<size_t>((nflags + 255) / 256, 1024);
-  hipLaunchKernelGGL(reset_kernel<0>, dim3(rblocks), dim3(256), 0, stream, p.counter, p.flags, nflags);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t grid = nflags;
+  const size_t grid = (size_t)p.batch * p.H * p.nc;
   // Maps let a chunk finish before its predecessor's state exists; they pay off
   // only when many chunks of one sequence are in flight at once (few sequences
   // x heads for the workgroups resident on the device): then consecutive

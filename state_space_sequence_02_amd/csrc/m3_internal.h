@@ -27,12 +27,20 @@ inline bool supported_head(int P) { return P == 16 || P == 32 || P == 64 || P ==
 inline bool supported_rank(int R) { return R == 1 || R == 2 || R == 4 || R == 8; }
 
 // ---------------------------------------------------------------------------
-// Prefill: one launch per call (after a tiny reset of the ticket counter and
-// flags), one workgroup per (sequence, chunk); chunk states are handed from
-// chunk to chunk with decoupled look-back.
-// Workspace (each region 256-byte aligned): control block (ticket counter) |
-// flags [b*H*nc] u32 | recs [b*H*nc][N+2] fp32 (a_c, pad, cos/sin Psi_c per
-// pair) | maps [b*H*nc][fused_slot_floats] fp32 | states [b*H*nc][same] fp32.
+// Prefill: one launch per call, one workgroup per (sequence, chunk); chunk
+// states are handed from chunk to chunk with decoupled look-back.
+// Workspace (each region 256-byte aligned): control word | flags [b*H*nc] u64 |
+// recs [b*H*nc][N+2] fp32 (a_c, pad, cos/sin Psi_c per pair) |
+// maps [b*H*nc][fused_slot_floats] fp32 | states [b*H*nc][same] fp32.
+// The control word holds the call's ticket count (low kTicketBits bits) and an
+// epoch (the rest).  The workgroup that takes a call's last ticket sets the
+// count back to 0 and advances the epoch, and every flag carries the epoch of
+// the call that wrote it ((epoch + 1) << 2 | state), so a zero-filled
+// workspace stays ready for the next call with no reset between calls: flags
+// left by earlier calls never match.
+constexpr int kTicketBits = 26;
+constexpr unsigned long long kTicketMask = (1ull << kTicketBits) - 1;
+constexpr size_t kMaxChunks = (size_t)kTicketMask;   // chunks per call, at most
 struct PrefillPlan {
   int Q;              // tokens per chunk
   int nc;             // chunks per sequence
@@ -48,7 +56,7 @@ struct FusedParams {
   const float* dt; const float* A; const float* lam; const float* theta;
   const float* h0; const void* Bp; const void* xp;
   void* y; float* h_out;
-  unsigned* counter; unsigned* flags; float* recs; float* maps; float* states;
+  unsigned long long* ctl; unsigned long long* flags; float* recs; float* maps; float* states;
   int batch, L, H, N, P, R, logR, Q, nc;
   int use_maps;          // publish chunk maps when the predecessor's state is late
 };

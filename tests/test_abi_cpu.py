@@ -127,7 +127,7 @@ def test_workspace_size_matches_layout(lib, name):
     nc = -(-w.seqlen // q)
     bhc = w.batch * w.nheads * nc
     a = lambda v: (v + 255) // 256 * 256
-    # control block | flags | per-chunk records | maps | states; a map or state
+    # control word | flags (u64) | per-chunk records | maps | states; a map or state
     # slot holds each thread's NPW x PTW state tiles (16 x 16 tiles shared out
     # over the waves: 1024 threads for N >= 128, else 512), 4 floats per lane
     threads = 1024 if w.dstate >= 128 else 512
@@ -136,11 +136,19 @@ def test_workspace_size_matches_layout(lib, name):
     ngrp = min(tn, waves)
     slot = (tn // ngrp) * (-(-tp // (waves // ngrp))) * threads * 4
     assert slot >= w.dstate * w.headdim
-    recs = a(256 + bhc * 4)
+    recs = a(256 + bhc * 8)
     maps = a(recs + bhc * (w.dstate + 2) * 4)
     states = a(maps + bhc * slot * 4)
     expect = a(states + bhc * slot * 4)
     assert m3.prefill_workspace_bytes(shape) == expect
+
+
+def test_chunk_count_cap(lib):
+    # a call takes at most 2^26 - 1 chunk tickets (the control word's count field)
+    s = lambda H: m3.make_shape(64, 65536, H, 16, 16, 1, 16, m3.M3_BF16)
+    assert 64 * 255 * (65536 // 16) < 2 ** 26 - 1 < 64 * 256 * (65536 // 16)
+    assert m3.prefill_chunk_used(s(255)) == 16 and m3.prefill_workspace_bytes(s(255)) > 0
+    assert m3.prefill_chunk_used(s(256)) == 0 and m3.prefill_workspace_bytes(s(256)) == 0
 
 
 def test_chunk_request_rounding(lib):

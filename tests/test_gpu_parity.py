@@ -130,6 +130,68 @@ def test_run_twice_bit_exact():
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
+def _shape_of(w, chunk):
+    dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+    return m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, chunk, dcode)
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """One workspace, zero-filled once, serves successive calls of different
+    shapes with nothing done in between; the last call repeats the first shape
+    with other inputs, so a flag left by the first call that still counted would
+    hand it a stale state."""
+    cases = [(inputs.workload("siso", batch=2, seqlen=600, nheads=3), 32),
+             (inputs.workload("siso", batch=1, seqlen=70, nheads=2), 16),
+             (inputs.workload("mimo", batch=1, seqlen=200, nheads=2), 32),
+             (inputs.workload("siso", batch=2, seqlen=600, nheads=3), 32)]
+    need = max(m3.prefill_workspace_bytes(_shape_of(w, q)) for w, q in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (w, q) in enumerate(cases):
+        d = inputs.make_prefill_inputs(w, seed=70 + i)
+        dg = dev_inputs(d)
+        note(f"prefill call {i} on a shared workspace: {w.name} b={w.batch} L={w.seqlen} H={w.nheads} chunk={q}")
+        y, h = m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS}, chunk=q, workspace=ws)
+        torch.cuda.synchronize()
+        yr, hr = oracle.scan(**oracle_inputs(d))
+        check_blocks(to64(y), yr, TOL[w.dtype], (1, 3, 4), f"y call {i}", elem_axes=(3, 4))
+        check_blocks(to64(h), hr, TOL[w.dtype], (2, 3), f"h_out call {i}")
+
+
+def test_prefill_graph_replay():
+    """A prefill captured in a HIP graph is right on every replay, with eager
+    calls on the same workspace between the replays."""
+    w = inputs.workload("mimo", batch=2, seqlen=300, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=81)
+    dg = dev_inputs(d)
+    kw = {k: dg[k] for k in PREFILL_KEYS}
+    yr, hr = oracle.scan(**oracle_inputs(d))
+    ws = torch.zeros(m3.prefill_workspace_bytes(_shape_of(w, 32)), dtype=torch.uint8, device="cuda")
+    y, h = torch.empty_like(dg["x"]), torch.empty((w.batch, w.nheads, w.dstate, w.headdim), device="cuda")
+    note("prefill graph capture")
+    m3.scan_prefill(**kw, y=y, h_out=h, chunk=32, workspace=ws)   # eager, before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            m3.scan_prefill(**kw, y=y, h_out=h, chunk=32, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.zero_()
+        h.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_blocks(to64(y), yr, TOL[w.dtype], (1, 3, 4), f"y replay {rep}", elem_axes=(3, 4))
+        check_blocks(to64(h), hr, TOL[w.dtype], (2, 3), f"h_out replay {rep}")
+        ye, he = m3.scan_prefill(**kw, chunk=32, workspace=ws)   # eager, same workspace
+        torch.cuda.synchronize()
+        check_blocks(to64(ye), yr, TOL[w.dtype], (1, 3, 4), f"y eager after replay {rep}", elem_axes=(3, 4))
+        check_blocks(to64(he), hr, TOL[w.dtype], (2, 3), f"h_out eager after replay {rep}")
+
+
 def test_state_in_place_and_empty_and_single():
     w = inputs.workload("siso", batch=2, seqlen=1, nheads=3)
     d = inputs.make_prefill_inputs(w, seed=9)
