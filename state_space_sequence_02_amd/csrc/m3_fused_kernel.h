@@ -413,7 +413,12 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   auto hcol = [&](int pt) { return l16 * TPt + pt; };
   // output row tiles of this wave, paired (w, MT-1-w) for balance
   const int ntiles_w = (MT + kWaves - 1 - wave) / kWaves;
+  // (one tile per wave: the second half of the waves takes the tiles in reverse
+  // order, so waves w and w + 4 -- one SIMD when waves go round-robin over the
+  // four -- hold a light and a heavy tile)
+  const bool rev = RT == 1 && MT == kWaves && wave >= kWaves / 2;
   auto tile_of = [&](int k) {
+    if (rev) return MT - 1 - (wave - kWaves / 2);
     const int pair = k >> 1;
     return (k & 1) ? MT - 1 - (wave + 2 * kWaves * pair) : wave + 2 * kWaves * pair;
   };
