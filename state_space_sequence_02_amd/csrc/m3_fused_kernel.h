@@ -26,8 +26,10 @@
 // scan"): chunk c's map S -> a_c R(Psi_c) S + U_c is affine, so a chunk whose
 // predecessor has not finished composes the predecessors' maps itself
 // (decoupled look-back).  Flags per chunk: 1 = map published, 2 = S_out
-// published, tagged with the call's epoch (a flag of another call reads as 0).  Wave 0 reads the predecessors' flags right after staging; a
-// chunk publishes its map only when its predecessor's state was not there.
+// published, tagged with the call's epoch (a flag of another call reads as 0).
+// Wave 0 reads the predecessors' flags once before the look-back proper (at
+// the start when maps are in use, else after staging); a chunk publishes its
+// map only when maps are in use and its predecessor's state was not there.
 // Workgroups take chunk-major tickets from an atomic counter, so every chunk a
 // workgroup looks back at holds a lower ticket and is already running: every
 // wait ends.  A bounded spin turns a wait that never ends into NaN outputs.
@@ -45,6 +47,7 @@
 //      waves with one barrier; cos/sin table of Phi in LDS
 //   B  stage B~ (rotated) and X in LDS; the wave's C~ rows are kept in
 //      registers as MFMA operands; wave 0 polls the predecessors' flags
+//      (when maps are in use, this poll is issued with the loads in A)
 //   C  U = R(Psi) sum_s W_s B~_s^T X_s on MFMA (operands by LDS transpose reads);
 //      publish the map if needed
 //   D  look back for S_in; S_out = a R(Psi) S_in + U; stores issued
@@ -497,6 +500,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   const int rows = nt * R;
   const size_t tok0 = tok_index(p, b, t0, h);
   unsigned long long* flags = p.flags + (size_t)bh * p.nc;
+  // With maps, wave 0 reads the predecessors' flags right away: the answer
+  // (whether the predecessor's state is there, i.e. whether to publish a map)
+  // is then in before the map is done, and serves as the look-back's first step.
+  const int W0 = min(c, 64);
+  unsigned fpoll = 1u;
+  if (p.use_maps && wave == 0 && lane < W0)
+    fpoll = flag_state(__hip_atomic_load(flags + c - 1 - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   const T* Bg = static_cast<const T*>(p.B) + tok0 * R * N;
   const T* Xg = static_cast<const T*>(p.x) + tok0 * R * P;
   const float A = p.A[h];
@@ -627,12 +637,10 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     }
   }
   __syncthreads();
-  // Wave 0 reads the flags of up to 64 predecessors (lane k: chunk c-1-k) now;
-  // the answer arrives during the map's MFMAs and serves both the choice of
-  // publishing the map and the first step of the look-back.
-  const int W0 = min(c, 64);
-  unsigned fpoll = 1u;
-  if (wave == 0 && lane < W0)
+  // Without maps, wave 0 reads the flags of up to 64 predecessors (lane k:
+  // chunk c-1-k) now, for the first step of the look-back (with maps this
+  // was done at the start, see there).
+  if (!p.use_maps && wave == 0 && lane < W0)
     fpoll = flag_state(__hip_atomic_load(flags + c - 1 - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 
   // ---- C: U[n][p] = R(Psi) sum_k W_k B~[k][n] X[k][p] ----
@@ -689,8 +697,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   const size_t chunk_id = (size_t)bh * p.nc + c;
   // Publish the map only if the predecessor's state was not there at the poll.
   if (wave == 0) {
-    const bool pred_state = (__ballot(lane < W0 && fpoll == 2u) & 1ull) != 0;
-    const int need_map = p.use_maps && c > 0 && !pred_state;
+    int need_map = 0;
+    if (p.use_maps) need_map = c > 0 && (__ballot(lane < W0 && fpoll == 2u) & 1ull) == 0;
     if (lane == 0) {
       s_misc[2] = need_map;
       if (need_map) st_dev2(p.recs + chunk_id * (2 * NH + 2), a_c, 0.f);   // the record's decay
