@@ -84,7 +84,11 @@ size_t m3_prefill_workspace_bytes(const m3_shape* s);
 
 /* Tokens per chunk m3_scan_prefill will actually use for this shape (the
  * requested value rounded to a supported power of two and capped so that one
- * chunk's tiles fit on a compute unit), or 0 on an invalid shape. */
+ * chunk's tiles fit on a compute unit), or 0 on an invalid shape.  A few
+ * supported (N, P, R) do not fit a compute unit's LDS even at 16 tokens per
+ * chunk and get 0 here and M3_ERR_SHAPE from m3_scan_prefill (the decode step
+ * takes them): bf16 N=256 P=128 R=8; fp32 N=128 P=128 R=8; fp32 N=256 with
+ * P=128 or R=8. */
 int32_t m3_prefill_chunk_used(const m3_shape* s);
 
 /* Chunked prefill over a whole sequence (the recurrence above for t = 0..L-1).

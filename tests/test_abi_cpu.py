@@ -151,6 +151,24 @@ def test_chunk_count_cap(lib):
     assert m3.prefill_chunk_used(s(256)) == 0 and m3.prefill_workspace_bytes(s(256)) == 0
 
 
+def test_prefill_shapes_too_big_for_a_cu(lib):
+    # every chunk's tiles must fit one compute unit's 160 KB of LDS; these
+    # supported (N, P, R) do not even at 16 tokens per chunk
+    too_big = {("bf16", 256, 128, 8), ("fp32", 128, 128, 8), ("fp32", 256, 16, 8), ("fp32", 256, 32, 8),
+               ("fp32", 256, 64, 8), ("fp32", 256, 128, 1), ("fp32", 256, 128, 2), ("fp32", 256, 128, 4),
+               ("fp32", 256, 128, 8)}
+    for dt, code in (("bf16", m3.M3_BF16), ("fp32", m3.M3_FP32)):
+        for N in (16, 32, 64, 128, 256):
+            for P in (16, 32, 64, 128):
+                for R in (1, 2, 4, 8):
+                    s = m3.make_shape(1, 100, 2, P, N, R, 0, code)
+                    q, ws = m3.prefill_chunk_used(s), m3.prefill_workspace_bytes(s)
+                    if (dt, N, P, R) in too_big:
+                        assert q == 0 and ws == 0, (dt, N, P, R)
+                    else:
+                        assert q >= 16 and ws > 0, (dt, N, P, R)
+
+
 def test_chunk_request_rounding(lib):
     s = lambda c, R=1, N=64: m3.make_shape(1, 1000, 1, 64, N, R, c, m3.M3_BF16)
     assert m3.prefill_chunk_used(s(64)) == 64

@@ -1,0 +1,100 @@
+"""GPU parity over every compiled shape: each (dtype, N, P, R) the library
+instantiates, for the chunked prefill (at the library's default chunk and at
+the largest chunk the shape allows, which puts two or four 16-row output tiles
+on a wave) and for the decode step (fp32 state, and bf16 state with bf16
+inputs), against the float64 oracle.  Sizes are small: a prefill spans two
+whole chunks and a ragged third, with an incoming state and previous write.
+"""
+import pytest
+import torch
+
+import oracle
+import state_space_sequence_02_amd as m3
+from state_space_sequence_02_amd import inputs
+
+from _parity import TOL, check_blocks, dev_inputs, note, oracle_inputs, to64
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("bf16", "fp32")
+STATES = (16, 32, 64, 128, 256)
+HEADS = (16, 32, 64, 128)
+RANKS = (1, 2, 4, 8)
+GRID = [(dt, n, p, r) for dt in DTYPES for n in STATES for p in HEADS for r in RANKS]
+KEYS = ("x", "B", "C", "dt", "A", "lam", "theta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m3.load_library()
+
+
+def _code(dtype):
+    return m3.M3_BF16 if dtype == "bf16" else m3.M3_FP32
+
+
+# shapes whose chunk tiles do not fit a compute unit's LDS even at 16 tokens
+# per chunk: the prefill rejects them (the decode takes them)
+NO_PREFILL = {("bf16", 256, 128, 8), ("fp32", 128, 128, 8), ("fp32", 256, 16, 8), ("fp32", 256, 32, 8),
+              ("fp32", 256, 64, 8), ("fp32", 256, 128, 1), ("fp32", 256, 128, 2), ("fp32", 256, 128, 4),
+              ("fp32", 256, 128, 8)}
+
+
+@pytest.mark.parametrize("chunk", ["default", "max"])
+@pytest.mark.parametrize("dtype,N,P,R", GRID, ids=lambda v: str(v))
+def test_prefill_grid(dtype, N, P, R, chunk):
+    request = 0 if chunk == "default" else 4096
+    q = m3.prefill_chunk_used(m3.make_shape(1, 1, 2, P, N, R, request, _code(dtype)))
+    if (dtype, N, P, R) in NO_PREFILL:
+        assert q == 0
+        w = inputs.workload("mimo", batch=1, seqlen=20, nheads=2, headdim=P, dstate=N, rank=R, dtype=dtype)
+        dg = dev_inputs(inputs.make_prefill_inputs(w, seed=1))
+        note(f"prefill grid {dtype} N={N} P={P} R={R}: rejected")
+        with pytest.raises(m3.M3Error, match="M3_ERR_SHAPE"):
+            m3.scan_prefill(**{k: dg[k] for k in KEYS}, chunk=request)
+        return
+    assert q >= 16
+    L = 2 * q + q // 2 + 3
+    w = inputs.workload("mimo", batch=1, seqlen=L, nheads=2, headdim=P, dstate=N, rank=R,
+                        chunk=q, dtype=dtype)
+    seed = 1000 + N + P + R
+    d = inputs.make_prefill_inputs(w, seed=seed)
+    c = inputs.random_carry(w, seed=seed + 1)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note(f"prefill grid {dtype} N={N} P={P} R={R} chunk={q} L={L}")
+    y, h = m3.scan_prefill(**{k: dg[k] for k in KEYS}, **cg, chunk=q)
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
+    check_blocks(to64(y), yr, TOL[dtype], (1, 3, 4), "y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL[dtype], (2, 3), "h_out")
+
+
+DECODE = [(dt, st, n, p, r) for dt, st in (("bf16", "fp32"), ("fp32", "fp32"), ("bf16", "bf16"))
+          for n in STATES for p in HEADS for r in RANKS]
+
+
+@pytest.mark.parametrize("dtype,state,N,P,R", DECODE, ids=lambda v: str(v))
+def test_decode_grid(dtype, state, N, P, R):
+    w = inputs.workload("decode", batch=2, nheads=3, headdim=P, dstate=N, rank=R, dtype=dtype)
+    steps, seed = 3, 2000 + N + P + R
+    d = inputs.make_decode_inputs(w, seed=seed, steps=steps)
+    dg = dev_inputs(d)
+    h0 = torch.randn((w.batch, w.nheads, N, P), generator=torch.Generator().manual_seed(seed + 1)) * 0.5
+    h = (h0.to(torch.bfloat16) if state == "bf16" else h0).to("cuda").contiguous()
+    note(f"decode grid {dtype} inputs, {state} state, N={N} P={P} R={R}")
+    ys = []
+    for s in range(steps):
+        kw = dict(B_prev=dg["B"][s - 1], x_prev=dg["x"][s - 1]) if s else {}
+        ys.append(m3.decode_step(h, dg["x"][s], dg["B"][s], dg["C"][s], dg["dt"][s], dg["A"],
+                                 dg["lam"][s], dg["theta"][s], **kw))
+    torch.cuda.synchronize()
+    if state == "bf16":
+        yr, hr = oracle.decode_steps_bf16_state(h0.to(torch.bfloat16).double().numpy(), d["x"], d["B"],
+                                                d["C"], d["dt"], d["A"], d["lam"], d["theta"])
+    else:
+        yr, hr = oracle.decode_steps(h0, d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"])
+    tol = TOL[dtype]
+    check_blocks(to64(torch.stack(ys)), yr, tol, (3, 4), "decode y")
+    check_blocks(to64(h), hr, tol, (2, 3), "decode h")
