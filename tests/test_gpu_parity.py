@@ -263,9 +263,9 @@ def test_decode_small(shape):
 
 
 def test_decode_several_pairs_per_workgroup():
-    """640 (sequence, head) pairs at N=128, P=64, R=4: more than the 512
-    workgroups of this shape that fit on the chip at once, so workgroups take
-    several pairs each and every pair after the first is prefetched."""
+    """640 (sequence, head) pairs at N=128, P=64, R=4: more workgroups (one
+    per pair) than fit on the chip at once, so later ones start on compute
+    units that earlier ones free."""
     w = inputs.workload("decode", batch=20, nheads=32, headdim=64, dstate=128, rank=4, dtype="bf16")
     d, h0, y, h = _decode_case(w, steps=3, seed=21)
     yr, hr = oracle.decode_steps(h0, d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"])
