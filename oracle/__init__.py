@@ -158,3 +158,39 @@ def decode_steps_bf16_state(h0, x, B, C, dt, A, lam, theta=None, B_prev=None, x_
         ys.append(y[:, 0])
         h = round_bf16(h_new)
     return np.stack(ys), h
+
+
+def silu(v) -> np.ndarray:
+    """v * sigmoid(v) = v / (1 + exp(-v)), in float64."""
+    v = _as64(v)
+    return v / (1.0 + np.exp(-v))
+
+
+def gated_readout(y, z=None, w_y=None, w_z=None) -> np.ndarray:
+    """Rank contraction of the outputs with an elementwise rank-expanded gate.
+
+    The explainer's remark on MIMO training cost (its sec. 3.3 / 4.1.1 note)
+    says the architecture replaces dense rank projections of x, y and the gate
+    by learned elementwise rank expansion, printing no formula; the paper page's
+    Tables 11 and 12 fuse the gate into the SSM kernel (prefill and decode).
+    Reading used here: the gate z_t (one value per head column p) is expanded to
+    Z_t[p, r] = w_z[h, r, p] z_t[p], applied to each rank's output through SiLU,
+    and the ranks are contracted with w_y:
+        out_t[p] = sum_r w_y[h, r, p] * Y_t[p, r] * silu(Z_t[p, r]).
+    y [..., H, R, P]; z [..., H, P] or None (no gate); w_y, w_z [H, R, P] or
+    None (all ones).  Returns out [..., H, P] in float64."""
+    y = _as64(y)
+    H, R, P = y.shape[-3:]
+    wy = np.ones((H, R, P)) if w_y is None else _as64(w_y)
+    g = np.ones(y.shape)
+    if z is not None:
+        wz = np.ones((H, R, P)) if w_z is None else _as64(w_z)
+        g = silu(wz * _as64(z)[..., None, :])
+    return (wy * y * g).sum(axis=-2)
+
+
+def scan_gated(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
+               z=None, w_y=None, w_z=None, nthreads: int = 0):
+    """`scan` followed by `gated_readout` of its outputs: (out [b,L,H,P], h)."""
+    y, h = scan(x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, nthreads=nthreads)
+    return gated_readout(y, z, w_y, w_z), h

@@ -406,3 +406,54 @@ def test_bf16_state_first_step_and_representable_states():
     scale = max(np.abs(hr).max(), np.abs(h0).max())
     assert np.abs(hb - hr).max() <= 24 * 2.0 ** -9 * scale * 2
     assert np.abs(hb - hr).max() > 0          # the rounding is really applied
+
+
+def test_silu_closed_form_values():
+    # silu(v) = v * sigmoid(v); sigmoid(1) = e/(e+1), sigmoid(2) = e^2/(e^2+1)
+    e = math.e
+    want = [0.0, e / (e + 1), -1.0 / (e + 1), 2 * e * e / (e * e + 1), -2.0 / (e * e + 1)]
+    got = oracle.silu(np.array([0.0, 1.0, -1.0, 2.0, -2.0]))
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=1e-300)
+    v = np.linspace(-30, 30, 121)
+    # v sigmoid(v) - (-v) sigmoid(-v) = v (sigmoid(v) + sigmoid(-v)) = v
+    np.testing.assert_allclose(oracle.silu(v) - oracle.silu(-v), v, rtol=1e-12, atol=1e-12)
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-15 and abs(oracle.silu(-40.0)) < 1e-15
+
+
+def test_gated_readout_special_cases():
+    rng = np.random.default_rng(5)
+    b, L, H, R, P = 2, 3, 2, 4, 8
+    y = rng.standard_normal((b, L, H, R, P))
+    z = rng.standard_normal((b, L, H, P))
+    wy = rng.standard_normal((H, R, P))
+    wz = rng.standard_normal((H, R, P))
+    # no gate, unit weights: the plain sum over ranks
+    np.testing.assert_allclose(oracle.gated_readout(y), y.sum(axis=3), rtol=1e-14, atol=1e-14)
+    # a one-hot w_y picks one rank; a zero gate input gives silu(0) = 0
+    onehot = np.zeros((H, R, P))
+    onehot[:, 2, :] = 1.0
+    np.testing.assert_allclose(oracle.gated_readout(y, w_y=onehot), y[:, :, :, 2, :], rtol=0, atol=0)
+    assert not oracle.gated_readout(y, np.zeros_like(z), wy, wz).any()
+    # the odd part of the gate: out(z) - out(-z) = sum_r w_y y w_z z
+    d = oracle.gated_readout(y, z, wy, wz) - oracle.gated_readout(y, -z, wy, wz)
+    np.testing.assert_allclose(d, (wy * y * wz * z[:, :, :, None, :]).sum(axis=3), rtol=1e-12, atol=1e-12)
+    # brute force on one element, rank by rank
+    t, h, p = 1, 1, 5
+    s = 0.0
+    for r in range(R):
+        zz = wz[h, r, p] * z[0, t, h, p]
+        s += wy[h, r, p] * y[0, t, h, r, p] * zz / (1.0 + math.exp(-zz))
+    assert abs(oracle.gated_readout(y, z, wy, wz)[0, t, h, p] - s) < 1e-13
+
+
+def test_scan_gated_is_scan_then_readout():
+    w = inputs.workload("mimo", batch=1, seqlen=40, nheads=2, headdim=16, dstate=16)
+    d = inputs.make_prefill_inputs(w, seed=3)
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((1, 40, 2, 16))
+    wy = rng.standard_normal((2, 4, 16))
+    o = {k: d[k].double().numpy() for k in ("x", "B", "C", "dt", "A", "lam", "theta")}
+    out, h = oracle.scan_gated(**o, z=z, w_y=wy)
+    y, h2 = oracle.scan(**o)
+    assert np.array_equal(h, h2)
+    np.testing.assert_allclose(out, oracle.gated_readout(y, z, wy), rtol=0, atol=0)
