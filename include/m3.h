@@ -84,11 +84,11 @@ size_t m3_prefill_workspace_bytes(const m3_shape* s);
 
 /* Tokens per chunk m3_scan_prefill will actually use for this shape (the
  * requested value rounded to a supported power of two and capped so that one
- * chunk's tiles fit on a compute unit), or 0 on an invalid shape.  A few
- * supported (N, P, R) do not fit a compute unit's LDS even at 16 tokens per
- * chunk and get 0 here and M3_ERR_SHAPE from m3_scan_prefill (the decode step
- * takes them): bf16 N=256 P=128 R=8; fp32 N=128 P=128 R=8; fp32 N=256 with
- * P=128 or R=8. */
+ * chunk's tiles fit on a compute unit), or 0 on an invalid shape.  The prefill
+ * takes N = 16..128 (N = 256 is decode-only) and every P and R with them
+ * except fp32 N=128 P=128 R=8, whose tiles do not fit a compute unit's LDS even
+ * at 16 tokens per chunk; those get 0 here and M3_ERR_SHAPE from
+ * m3_scan_prefill. */
 int32_t m3_prefill_chunk_used(const m3_shape* s);
 
 /* Chunked prefill over a whole sequence (the recurrence above for t = 0..L-1).
@@ -168,6 +168,44 @@ m3_status m3_decode_step_bf16_state(const m3_shape* s,
                                     const float* dt, const float* A, const float* lam,
                                     const float* theta,
                                     void* y, void* stream);
+
+/* The two calls above with the gated readout fused into their output stage:
+ * instead of y [.., H, R, P] they write
+ *   out[.., h, p] = sum_r w_y[h, r, p] * Y[p, r] * silu(w_z[h, r, p] * z[.., h, p]),
+ *   silu(v) = v / (1 + exp(-v)),
+ * from the fp32 outputs before any rounding (one value per head column: the
+ * ranks are contracted).  Defined by: the explainer's note that the
+ * architecture uses learned elementwise rank expansion for x, y and the gate
+ * instead of dense rank projections (no formula printed; this is the reading
+ * adopted: the gate is expanded per rank, applied to that rank's output, and
+ * the ranks are summed with weights w_y), and the paper page's Tables 11 and 12,
+ * which fuse the gate into the SSM kernel for prefill and decode.
+ *   z     [b, L, H, P] (prefill) / [b, H, P] (decode)  dtype  gate input, or
+ *                                         NULL = no gate (factor 1)
+ *   w_y   [H, R, P]  fp32   rank contraction weights, or NULL = all ones
+ *   w_z   [H, R, P]  fp32   rank expansion of the gate, or NULL = all ones
+ *                           (unused without z)
+ *   out   [b, L, H, P] (prefill) / [b, H, P] (decode)  dtype  out
+ * Every other argument, the workspace and the error codes as in
+ * m3_scan_prefill / m3_decode_step (fp32 state).  out must not alias any input,
+ * the state or the workspace (M3_ERR_ALIAS). */
+m3_status m3_scan_prefill_gated(const m3_shape* s,
+                                const void* x, const void* B, const void* C,
+                                const float* dt, const float* A, const float* lam,
+                                const float* theta,
+                                const float* h0, const void* B_prev, const void* x_prev,
+                                const void* z, const float* w_y, const float* w_z,
+                                void* out, float* h_out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+m3_status m3_decode_step_gated(const m3_shape* s,
+                               float* h,
+                               const void* B_prev, const void* x_prev,
+                               const void* x, const void* B, const void* C,
+                               const float* dt, const float* A, const float* lam,
+                               const float* theta,
+                               const void* z, const float* w_y, const float* w_z,
+                               void* out, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_str(m3_status st);

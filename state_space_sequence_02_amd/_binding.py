@@ -19,7 +19,8 @@ M3_FP32, M3_BF16 = 0, 1
 STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
           4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS"}
 EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_scan_prefill",
-           "m3_decode_step", "m3_decode_step_bf16_state", "m3_status_str", "m3_version")
+           "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
+           "m3_decode_step_gated", "m3_status_str", "m3_version")
 
 
 class M3Shape(ctypes.Structure):
@@ -59,6 +60,10 @@ def load_library(path: str = LIB_PATH):
     lib.m3_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.m3_decode_step_bf16_state.restype = ctypes.c_int
     lib.m3_decode_step_bf16_state.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.m3_scan_prefill_gated.restype = ctypes.c_int
+    lib.m3_scan_prefill_gated.argtypes = [sp] + [vp] * 16 + [sz, vp]
+    lib.m3_decode_step_gated.restype = ctypes.c_int
+    lib.m3_decode_step_gated.argtypes = [sp] + [vp] * 15
     lib.m3_status_str.restype = ctypes.c_char_p
     lib.m3_status_str.argtypes = [ctypes.c_int]
     lib.m3_version.restype = ctypes.c_int32
@@ -145,6 +150,62 @@ def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=N
         _ptr(workspace, None, dev), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(code)
     return y, h_out
+
+
+def scan_prefill_gated(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
+                       z=None, w_y=None, w_z=None, out=None, h_out=None, chunk: int = 0,
+                       workspace=None, want_state: bool = True):
+    """Chunked prefill with the gated readout fused (m3_scan_prefill_gated):
+    out[b,t,h,p] = sum_r w_y[h,r,p] y[b,t,h,r,p] silu(w_z[h,r,p] z[b,t,h,p]).
+    z [b,L,H,P] (x's dtype) or None; w_y, w_z [H,R,P] fp32 or None.  Other
+    arguments as scan_prefill.  Returns (out, h_out)."""
+    lib = load_library()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    dcode = _dtype_code(x)
+    shape = make_shape(b, L, H, P, N, R, chunk, dcode)
+    if out is None:
+        out = torch.empty((b, L, H, P), dtype=x.dtype, device=dev)
+    if h_out is None and want_state:
+        h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    need = int(lib.m3_prefill_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    code = lib.m3_scan_prefill_gated(
+        ctypes.byref(shape), _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
+        _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
+        _ptr(h0, f32, dev), _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(z, x.dtype, dev), _ptr(w_y, f32, dev), _ptr(w_z, f32, dev),
+        _ptr(out, x.dtype, dev), _ptr(h_out, f32, dev),
+        _ptr(workspace, None, dev), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code)
+    return out, h_out
+
+
+def decode_step_gated(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None,
+                      z=None, w_y=None, w_z=None, out=None):
+    """One decode step (fp32 state h, updated in place) with the gated readout
+    fused (m3_decode_step_gated); z [b,H,P] or None, w_y/w_z [H,R,P] or None.
+    Returns out [b,H,P]."""
+    lib = load_library()
+    b, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    shape = make_shape(b, 1, H, P, N, R, 0, _dtype_code(x))
+    if out is None:
+        out = torch.empty((b, H, P), dtype=x.dtype, device=dev)
+    f32 = torch.float32
+    code = lib.m3_decode_step_gated(
+        ctypes.byref(shape), _ptr(h, f32, dev),
+        _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
+        _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
+        _ptr(z, x.dtype, dev), _ptr(w_y, f32, dev), _ptr(w_z, f32, dev),
+        _ptr(out, x.dtype, dev), _stream(dev))
+    _check(code)
+    return out
 
 
 def decode_step(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=None):

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libm3.so")
 SOURCES = (["m3_api.cpp", "m3_decode.hip", "m3_util.hip", "m3_fused.hip"] +
-           [f"m3_fused_{t}_n{n}.hip" for t in ("bf16", "f32") for n in (16, 32, 64, 128, 256)])
+           [f"m3_fused_{t}_n{n}.hip" for t in ("bf16", "f32") for n in (16, 32, 64, 128)])
 ARCH = "gfx950"
 
 

@@ -59,6 +59,10 @@ int choose_chunk(const m3_shape& s) {
 }  // namespace
 
 bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
+  // N = 256 is decode-only: its prefill kernels spill 76-708 bytes per lane to
+  // scratch, and a memory fault was seen in one of them whose cause is not
+  // established, so that path is not built.
+  if (s.dstate > 128) return false;
   const int q = choose_chunk(s);
   if (q == 0) return false;
   plan->Q = q;
@@ -95,14 +99,26 @@ int32_t m3_prefill_chunk_used(const m3_shape* s) {
   return plan.Q;
 }
 
-m3_status m3_scan_prefill(const m3_shape* s,
-                          const void* x, const void* B, const void* C,
-                          const float* dt, const float* A, const float* lam,
-                          const float* theta,
-                          const float* h0, const void* B_prev, const void* x_prev,
-                          void* y, float* h_out,
-                          void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The gated readout's operands (gated = false: plain y output).
+struct Gate {
+  bool gated;
+  const void* z; const float* w_y; const float* w_z;
+};
+
+// Shared by both prefill entry points: `y` is y [b,L,H,R,P], or with a gate
+// out [b,L,H,P].
+m3_status prefill_common(const m3_shape* s,
+                         const void* x, const void* B, const void* C,
+                         const float* dt, const float* A, const float* lam,
+                         const float* theta,
+                         const float* h0, const void* B_prev, const void* x_prev,
+                         const Gate& g, void* y, float* h_out,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream) {
   m3_status st = check_common(s, true);
   if (st != M3_OK) return st;
   const int b = s->batch, L = s->seqlen, H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
@@ -122,15 +138,17 @@ m3_status m3_scan_prefill(const m3_shape* s,
   if (!plan_prefill(*s, &plan)) return M3_ERR_SHAPE;
   if (!workspace || workspace_bytes < plan.bytes) return M3_ERR_WORKSPACE;
 
-  // y must not alias any input, the final state or the workspace; h_out may be
-  // exactly h0 but must not overlap anything else.
-  const size_t ybytes = tok * R * P * es;
+  // y (or out) must not alias any input, the final state or the workspace;
+  // h_out may be exactly h0 but must not overlap anything else.
+  const size_t ybytes = tok * (g.gated ? 1 : R) * P * es;
   const size_t sbytes = bh * N * P * sizeof(float);
+  const size_t wbytes = (size_t)H * R * P * sizeof(float);
   struct { const void* p; size_t n; } ins[] = {
       {x, tok * R * P * es}, {B, tok * R * N * es}, {C, tok * R * N * es},
       {dt, tok * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, tok * sizeof(float)},
       {theta, theta ? tok * (N / 2) * sizeof(float) : 0}, {h0, h0 ? sbytes : 0},
-      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es}, {workspace, plan.bytes}};
+      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es}, {workspace, plan.bytes},
+      {g.z, g.z ? tok * P * es : 0}, {g.w_y, g.w_y ? wbytes : 0}, {g.w_z, g.w_z ? wbytes : 0}};
   for (const auto& in : ins) {
     if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
     if (h_out && in.p != h0 && overlaps(h_out, sbytes, in.p, in.n)) return M3_ERR_ALIAS;
@@ -141,7 +159,10 @@ m3_status m3_scan_prefill(const m3_shape* s,
   char* ws = static_cast<char*>(workspace);
   FusedParams f;
   f.x = x; f.B = B; f.C = C; f.dt = dt; f.A = A; f.lam = lam; f.theta = theta;
-  f.h0 = h0; f.Bp = B_prev; f.xp = x_prev; f.y = y; f.h_out = h_out;
+  f.h0 = h0; f.Bp = B_prev; f.xp = x_prev; f.h_out = h_out;
+  f.y = g.gated ? nullptr : y;
+  f.out = g.gated ? y : nullptr;
+  f.z = g.z; f.wy = g.w_y; f.wz = g.z ? g.w_z : nullptr;
   f.ctl = reinterpret_cast<unsigned long long*>(ws);
   f.flags = reinterpret_cast<unsigned long long*>(ws + plan.off_flags);
   f.recs = reinterpret_cast<float*>(ws + plan.off_recs);
@@ -154,16 +175,13 @@ m3_status m3_scan_prefill(const m3_shape* s,
   return M3_OK;
 }
 
-}  // extern "C"
-
-namespace {
-
 // Shared by both decode entry points: the state is fp32 or (state_bf16) bf16.
+// `y` is y [b,H,R,P], or with a gate out [b,H,P].
 m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
                         const void* B_prev, const void* x_prev,
                         const void* x, const void* B, const void* C,
                         const float* dt, const float* A, const float* lam,
-                        const float* theta, void* y, void* stream) {
+                        const float* theta, const Gate& g, void* y, void* stream) {
   m3_status st = check_common(s, false);
   if (st != M3_OK) return st;
   if (state_bf16 && s->dtype != M3_BF16) return M3_ERR_DTYPE;
@@ -174,13 +192,15 @@ m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
   if (bh == 0) return M3_OK;
   if (!h || !x || !B || !C || !dt || !A || !lam || !y) return M3_ERR_NULL;
 
-  const size_t ybytes = bh * R * P * es;
+  const size_t ybytes = bh * (g.gated ? 1 : R) * P * es;
   const size_t hbytes = bh * N * P * (state_bf16 ? 2 : sizeof(float));
+  const size_t wbytes = (size_t)H * R * P * sizeof(float);
   struct { const void* p; size_t n; } ins[] = {
       {x, bh * R * P * es}, {B, bh * R * N * es}, {C, bh * R * N * es},
       {dt, bh * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, bh * sizeof(float)},
       {theta, theta ? bh * (N / 2) * sizeof(float) : 0},
-      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es}};
+      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es},
+      {g.z, g.z ? bh * P * es : 0}, {g.w_y, g.w_y ? wbytes : 0}, {g.w_z, g.w_z ? wbytes : 0}};
   for (const auto& in : ins) {
     if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
     if (overlaps(h, hbytes, in.p, in.n)) return M3_ERR_ALIAS;
@@ -192,7 +212,10 @@ m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
 
   DecodeParams p;
   p.h = h; p.state_bf16 = state_bf16; p.Bp = B_prev; p.xp = x_prev; p.x = x; p.B = B; p.C = C;
-  p.dt = dt; p.A = A; p.lam = lam; p.theta = theta; p.y = y;
+  p.dt = dt; p.A = A; p.lam = lam; p.theta = theta;
+  p.y = g.gated ? nullptr : y;
+  p.out = g.gated ? y : nullptr;
+  p.z = g.z; p.wy = g.w_y; p.wz = g.z ? g.w_z : nullptr;
   p.batch = b; p.H = H; p.N = N; p.P = P; p.R = R;
   if (launch_decode(p, s->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
@@ -209,7 +232,19 @@ m3_status m3_decode_step(const m3_shape* s,
                          const float* dt, const float* A, const float* lam,
                          const float* theta,
                          void* y, void* stream) {
-  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, y, stream);
+  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{false, nullptr, nullptr, nullptr},
+                       y, stream);
+}
+
+m3_status m3_decode_step_gated(const m3_shape* s,
+                               float* h,
+                               const void* B_prev, const void* x_prev,
+                               const void* x, const void* B, const void* C,
+                               const float* dt, const float* A, const float* lam,
+                               const float* theta,
+                               const void* z, const float* w_y, const float* w_z,
+                               void* out, void* stream) {
+  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{true, z, w_y, w_z}, out, stream);
 }
 
 m3_status m3_decode_step_bf16_state(const m3_shape* s,
@@ -219,7 +254,33 @@ m3_status m3_decode_step_bf16_state(const m3_shape* s,
                                     const float* dt, const float* A, const float* lam,
                                     const float* theta,
                                     void* y, void* stream) {
-  return decode_common(s, h, 1, B_prev, x_prev, x, B, C, dt, A, lam, theta, y, stream);
+  return decode_common(s, h, 1, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{false, nullptr, nullptr, nullptr},
+                       y, stream);
+}
+
+m3_status m3_scan_prefill(const m3_shape* s,
+                          const void* x, const void* B, const void* C,
+                          const float* dt, const float* A, const float* lam,
+                          const float* theta,
+                          const float* h0, const void* B_prev, const void* x_prev,
+                          void* y, float* h_out,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{false, nullptr, nullptr, nullptr},
+                        y, h_out, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_scan_prefill_gated(const m3_shape* s,
+                                const void* x, const void* B, const void* C,
+                                const float* dt, const float* A, const float* lam,
+                                const float* theta,
+                                const float* h0, const void* B_prev, const void* x_prev,
+                                const void* z, const float* w_y, const float* w_z,
+                                void* out, float* h_out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{true, z, w_y, w_z},
+                        out, h_out, workspace, workspace_bytes, stream);
 }
 
 const char* m3_status_str(m3_status st) {

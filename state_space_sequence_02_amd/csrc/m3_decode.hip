@@ -19,7 +19,9 @@
 // so each state element costs one 2x2 rotation and one 2R-long FMA chain.  The
 // small operands are staged in LDS as fp32; the readout Y = H^T C is reduced
 // across lanes that share a quad (xor shuffles within the wave, then LDS
-// across waves).
+// across waves).  The gated entry point contracts the ranks of Y with the
+// rank-expanded SiLU gate in the same final pass and writes one value per
+// head column instead of R.
 #include "m3_device.h"
 
 namespace m3 {
@@ -297,6 +299,30 @@ __global__ __launch_bounds__((decode_threads<S, R>(N, P))) void decode_kernel(De
       *reinterpret_cast<float4*>(sRed + (wave * R + r) * P + 4 * q) = acc[r];
   }
   __syncthreads();
+  if (p.out) {
+    // gated readout: out[c] = sum_r w_y[r][c] Y[c][r] silu(w_z[r][c] z[c])
+    T* og = static_cast<T*>(p.out) + (size_t)bh * P;
+    const T* zg = p.z ? static_cast<const T*>(p.z) + (size_t)bh * P : nullptr;
+    const float* wyh = p.wy ? p.wy + (size_t)h_idx * R * P : nullptr;
+    const float* wzh = p.wz ? p.wz + (size_t)h_idx * R * P : nullptr;
+    for (int c = tid; c < P; c += NT) {
+      const float zc = zg ? to_f(zg[c]) : 0.f;
+      float o = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float s = 0.f;
+        for (int w = 0; w < nwaves; ++w) s += sRed[(w * R + r) * P + c];
+        if (wyh) s *= wyh[r * P + c];
+        if (zg) {
+          const float v = (wzh ? wzh[r * P + c] : 1.f) * zc;
+          s *= v / (1.f + __expf(-v));
+        }
+        o += s;
+      }
+      og[c] = from_f<T>(o);
+    }
+    return;
+  }
   T* yg = static_cast<T*>(p.y) + (size_t)bh * R * P;
   for (int i = tid; i < R * P; i += NT) {
     float s = 0.f;

@@ -1,5 +1,7 @@
 // m3_fused.hip -- host-side dispatch of the single-pass prefill (kernels in
-// m3_fused_kernel.h, instantiated per (dtype, state size) in m3_fused_*_n*.hip).
+// m3_fused_kernel.h, instantiated per (dtype, state size) in m3_fused_*_n*.hip;
+// N = 16..128: a 256-state chunk does not fit the register budget without
+// spilling, and the prefill rejects that size).
 #include "m3_fused_kernel.h"
 
 namespace m3 {
@@ -8,12 +10,10 @@ hipError_t launch_fused_bf16_16(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_bf16_32(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_bf16_64(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_bf16_128(const FusedParams&, size_t, hipStream_t);
-hipError_t launch_fused_bf16_256(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_f32_16(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_f32_32(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_f32_64(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_f32_128(const FusedParams&, size_t, hipStream_t);
-hipError_t launch_fused_f32_256(const FusedParams&, size_t, hipStream_t);
 
 size_t fused_lds_bytes(int Q, int R, int N, int P, int esize) {
   return fused::lds_layout(Q, R, N, P, esize).total;
@@ -26,7 +26,6 @@ hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hip
     case 32: return bf ? launch_fused_bf16_32(p, lds, s) : launch_fused_f32_32(p, lds, s);
     case 64: return bf ? launch_fused_bf16_64(p, lds, s) : launch_fused_f32_64(p, lds, s);
     case 128: return bf ? launch_fused_bf16_128(p, lds, s) : launch_fused_f32_128(p, lds, s);
-    case 256: return bf ? launch_fused_bf16_256(p, lds, s) : launch_fused_f32_256(p, lds, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -334,7 +334,8 @@ __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
 template <int N, int RT>
 constexpr int prefill_waves_per_simd() { return (fused_threads(N) == 1024 || (N <= 64 && RT <= 2)) ? 4 : 2; }
 
-template <typename T, int N, int P, int R, int RT>
+// G: the gated readout (out [b,L,H,P]) replaces the y store.
+template <typename T, int N, int P, int R, int RT, bool G>
 __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())) void prefill_kernel(FusedParams p) {
   constexpr int kThreads = fused_threads(N);
   constexpr int kWaves = kThreads / 64;
@@ -903,7 +904,6 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   __syncthreads();   // S_in^T complete in LDS
 
   // ---- E: outputs of this wave's 16-row tiles (up to RTW), all together ----
-  T* Yg = static_cast<T*>(p.y) + tok0 * R * P;
   int itk[RTW], sbm[RTW];
   bool vk[RTW];
 #pragma unroll
@@ -1030,29 +1030,81 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     }
   }
   // y: a lane holds head columns TPt*l16 .. TPt*l16+TPt-1 of 4 rows per tile
+  if constexpr (!G) {
+    T* Yg = static_cast<T*>(p.y) + tok0 * R * P;
 #pragma unroll
-  for (int k = 0; k < RTW; ++k) {
-    if (!vk[k]) continue;
+    for (int k = 0; k < RTW; ++k) {
+      if (!vk[k]) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = itk[k] * 16 + 4 * g4 + j;
-      if (row < rows) {
-        float v[TPt];
+      for (int j = 0; j < 4; ++j) {
+        const int row = itk[k] * 16 + 4 * g4 + j;
+        if (row < rows) {
+          float v[TPt];
 #pragma unroll
-        for (int pn = 0; pn < TPt; ++pn) v[pn] = chain_ok ? yacc[k][pn][j] : nanv;
-        store_row<T, TPt>(Yg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + TPt * l16, v);
+          for (int pn = 0; pn < TPt; ++pn) v[pn] = chain_ok ? yacc[k][pn][j] : nanv;
+          store_row<T, TPt>(Yg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + TPt * l16, v);
+        }
+      }
+    }
+  } else {
+    // gated readout out[t][c] = sum_r w_y[r][c] y[(t, r)][c] silu(w_z[r][c] z[t][c]):
+    // a lane's 4 rows are whole tokens' ranks for R <= 4 (RG rows per token);
+    // at R = 8 they are half a token's, and the lane 16 apart holds the rest
+    const size_t rowstepO = tstride * P;
+    T* Og = static_cast<T*>(p.out) + tok0 * P;
+    const T* Zg = p.z ? static_cast<const T*>(p.z) + tok0 * P : nullptr;
+    const float* wyh = p.wy ? p.wy + (size_t)h * R * P + TPt * l16 : nullptr;
+    const float* wzh = p.wz ? p.wz + (size_t)h * R * P + TPt * l16 : nullptr;
+    constexpr int RG = R < 4 ? R : 4;
+#pragma unroll
+    for (int k = 0; k < RTW; ++k) {
+      if (!vk[k]) continue;
+#pragma unroll
+      for (int q = 0; q < 4; q += RG) {
+        const int row0 = itk[k] * 16 + 4 * g4 + q;
+        const bool valid = row0 < rows;
+        const int tk = row0 >> LOGR;
+        float zv[TPt], o[TPt];
+#pragma unroll
+        for (int pn = 0; pn < TPt; ++pn) {
+          zv[pn] = (Zg && valid) ? to_f(Zg[tk * rowstepO + TPt * l16 + pn]) : 0.f;
+          o[pn] = 0.f;
+        }
+#pragma unroll
+        for (int j = q; j < q + RG; ++j) {
+          const int r = (row0 + j - q) & (R - 1);
+#pragma unroll
+          for (int pn = 0; pn < TPt; ++pn) {
+            float v = yacc[k][pn][j];
+            if (wyh) v *= wyh[r * P + pn];
+            if (Zg) {
+              const float gz = (wzh ? wzh[r * P + pn] : 1.f) * zv[pn];
+              v *= gz / (1.f + __expf(-gz));
+            }
+            o[pn] += v;
+          }
+        }
+        if constexpr (R == 8) {
+#pragma unroll
+          for (int pn = 0; pn < TPt; ++pn) o[pn] += __shfl_xor(o[pn], 16);
+        }
+        if (valid && (R != 8 || (g4 & 1) == 0)) {
+#pragma unroll
+          for (int pn = 0; pn < TPt; ++pn) o[pn] = chain_ok ? o[pn] : nanv;
+          store_row<T, TPt>(Og + tk * rowstepO + TPt * l16, o);
+        }
       }
     }
   }
 }
 
-template <typename T, int N, int P, int R, int RT>
+template <typename T, int N, int P, int R, int RT, bool G>
 hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   // LDS limit raised once per instantiation
   static bool lds_set = false;
   hipError_t e;
   if (!lds_set && lds > 64 * 1024) {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT>),
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)) != hipSuccess)
       return e;
     lds_set = true;
@@ -1077,7 +1129,7 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT>), fused_threads(N), lds) == hipSuccess)
+            &per, reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G>), fused_threads(N), lds) == hipSuccess)
       resident = cus * per;
     if (dev >= 0 && resident > 0)
       cache[dev].store(((unsigned long long)lds << 32) | (unsigned)resident, std::memory_order_relaxed);
@@ -1085,7 +1137,7 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   FusedParams q = p;
   const size_t nbh = (size_t)p.batch * p.H;
   q.use_maps = !(resident > 0 && (size_t)resident <= 4 * nbh);
-  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT, G>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, q);
   return hipGetLastError();
 }
 
@@ -1101,9 +1153,15 @@ hipError_t launch_rt(const FusedParams& p, size_t lds, hipStream_t s) {
   const int rt = row_tiles_per_wave(p.Q, R, N);
   constexpr int kWaves = fused_threads(N) / 64;
   constexpr int kMaxRT = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;
-  if (rt <= 1) return launch<T, N, P, R, 1>(p, lds, s);
-  if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1)>(p, lds, s);
-  if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1)>(p, lds, s);
+  if (p.out) {
+    if (rt <= 1) return launch<T, N, P, R, 1, true>(p, lds, s);
+    if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), true>(p, lds, s);
+    if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), true>(p, lds, s);
+    return hipErrorInvalidValue;
+  }
+  if (rt <= 1) return launch<T, N, P, R, 1, false>(p, lds, s);
+  if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), false>(p, lds, s);
+  if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), false>(p, lds, s);
   return hipErrorInvalidValue;
 }
 

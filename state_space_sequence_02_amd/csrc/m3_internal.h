@@ -55,7 +55,9 @@ struct FusedParams {
   const void* x; const void* B; const void* C;
   const float* dt; const float* A; const float* lam; const float* theta;
   const float* h0; const void* Bp; const void* xp;
-  void* y; float* h_out;
+  void* y; float* h_out;   // y is NULL when `out` is given
+  void* out;               // gated readout out [b,L,H,P], or NULL
+  const void* z; const float* wy; const float* wz;   // gate input and weights (each may be NULL)
   unsigned long long* ctl; unsigned long long* flags; float* recs; float* maps; float* states;
   int batch, L, H, N, P, R, logR, Q, nc;
   int use_maps;          // publish chunk maps when the predecessor's state is late
@@ -87,7 +89,9 @@ struct DecodeParams {
   const void* Bp; const void* xp;
   const void* x; const void* B; const void* C;
   const float* dt; const float* A; const float* lam; const float* theta;
-  void* y;
+  void* y;               // y [b,H,R,P], or NULL when `out` is given
+  void* out;             // gated readout out [b,H,P], or NULL
+  const void* z; const float* wy; const float* wz;   // gate input and weights (each may be NULL)
   int batch, H, N, P, R;
 };
 

@@ -116,6 +116,44 @@ def test_decode_validation_codes(lib):
     assert _decode(lib, m3.make_shape(0, 1, 2, 64, 128, 4, 0, 1), h=None) == 0
 
 
+FAR = [(i + 1) << 36 for i in range(20)]   # 64 GiB apart: no two fakes overlap
+
+
+def test_gated_validation_codes(lib):
+    ok = m3.make_shape(2, 128, 3, 64, 64, 4, 64, m3.M3_BF16)
+
+    def prefill(shape, **over):
+        a = dict(x=FAR[0], B=FAR[1], C=FAR[2], dt=FAR[3], A=FAR[4], lam=FAR[5], theta=None, h0=None,
+                 Bp=None, xp=None, z=FAR[6], wy=FAR[7], wz=FAR[8], out=FAR[9], h_out=None, ws=FAR[10],
+                 wsb=1 << 40)
+        a.update(over)
+        return lib.m3_scan_prefill_gated(ctypes.byref(shape), a["x"], a["B"], a["C"], a["dt"], a["A"], a["lam"],
+                                         a["theta"], a["h0"], a["Bp"], a["xp"], a["z"], a["wy"], a["wz"],
+                                         a["out"], a["h_out"], a["ws"], a["wsb"], None)
+
+    def decode(shape, **over):
+        a = dict(h=FAR[0], Bp=None, xp=None, x=FAR[1], B=FAR[2], C=FAR[3], dt=FAR[4], A=FAR[5], lam=FAR[6],
+                 theta=None, z=FAR[7], wy=FAR[8], wz=FAR[9], out=FAR[10])
+        a.update(over)
+        return lib.m3_decode_step_gated(ctypes.byref(shape), a["h"], a["Bp"], a["xp"], a["x"], a["B"], a["C"],
+                                        a["dt"], a["A"], a["lam"], a["theta"], a["z"], a["wy"], a["wz"],
+                                        a["out"], None)
+
+    assert prefill(ok, out=None) == 1
+    assert prefill(ok, out=FAR[6]) == 6          # out aliases z
+    assert prefill(ok, out=FAR[7] + 64) == 6     # out overlaps w_y
+    assert prefill(ok, out=FAR[10]) == 6         # out overlaps the workspace
+    assert prefill(ok, ws=None) == 4
+    assert prefill(m3.make_shape(2, 128, 3, 64, 64, 3, 64, 1)) == 2
+    assert prefill(m3.make_shape(0, 128, 3, 64, 64, 4, 64, 1), x=None, out=None, ws=None) == 0
+    dec = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
+    assert decode(dec, h=None) == 1
+    assert decode(dec, out=FAR[7]) == 6          # out aliases z
+    assert decode(dec, out=FAR[0]) == 6          # out aliases the state
+    assert decode(dec, out=FAR[9] + 4) == 6      # out overlaps w_z
+    assert decode(m3.make_shape(0, 1, 2, 64, 128, 4, 0, 1), h=None) == 0
+
+
 @pytest.mark.parametrize("name", ["tiny", "siso", "mimo", "long"])
 def test_workspace_size_matches_layout(lib, name):
     from state_space_sequence_02_amd import inputs
@@ -151,12 +189,11 @@ def test_chunk_count_cap(lib):
     assert m3.prefill_chunk_used(s(256)) == 0 and m3.prefill_workspace_bytes(s(256)) == 0
 
 
-def test_prefill_shapes_too_big_for_a_cu(lib):
-    # every chunk's tiles must fit one compute unit's 160 KB of LDS; these
-    # supported (N, P, R) do not even at 16 tokens per chunk
-    too_big = {("bf16", 256, 128, 8), ("fp32", 128, 128, 8), ("fp32", 256, 16, 8), ("fp32", 256, 32, 8),
-               ("fp32", 256, 64, 8), ("fp32", 256, 128, 1), ("fp32", 256, 128, 2), ("fp32", 256, 128, 4),
-               ("fp32", 256, 128, 8)}
+def test_prefill_unsupported_shapes(lib):
+    # the prefill takes N <= 128 (N = 256 is decode-only); fp32 N=128 P=128 R=8
+    # does not fit one compute unit's 160 KB of LDS even at 16 tokens per chunk
+    too_big = {("fp32", 128, 128, 8)} | {(dt, 256, P, R) for dt in ("bf16", "fp32")
+                                          for P in (16, 32, 64, 128) for R in (1, 2, 4, 8)}
     for dt, code in (("bf16", m3.M3_BF16), ("fp32", m3.M3_FP32)):
         for N in (16, 32, 64, 128, 256):
             for P in (16, 32, 64, 128):

@@ -37,14 +37,18 @@ def _code(dtype):
 
 # shapes whose chunk tiles do not fit a compute unit's LDS even at 16 tokens
 # per chunk: the prefill rejects them (the decode takes them)
-NO_PREFILL = {("bf16", 256, 128, 8), ("fp32", 128, 128, 8), ("fp32", 256, 16, 8), ("fp32", 256, 32, 8),
-              ("fp32", 256, 64, 8), ("fp32", 256, 128, 1), ("fp32", 256, 128, 2), ("fp32", 256, 128, 4),
-              ("fp32", 256, 128, 8)}
+NO_PREFILL = {("fp32", 128, 128, 8)}
+# N = 256 is decode-only: its prefill kernels spilled heavily to scratch and one
+# of them (bf16 P=64 R=4) made a GPU memory fault whose cause was not found, so
+# the path was taken out of the library
+N256_SKIP = "N=256 prefill is not built (heavy scratch spills; one unexplained GPU memory fault)"
 
 
 @pytest.mark.parametrize("chunk", ["default", "max"])
 @pytest.mark.parametrize("dtype,N,P,R", GRID, ids=lambda v: str(v))
 def test_prefill_grid(dtype, N, P, R, chunk):
+    if N == 256:
+        pytest.skip(N256_SKIP)
     request = 0 if chunk == "default" else 4096
     q = m3.prefill_chunk_used(m3.make_shape(1, 1, 2, P, N, R, request, _code(dtype)))
     if (dtype, N, P, R) in NO_PREFILL:
