@@ -42,6 +42,20 @@ def prefill_bytes_per_token_head(w) -> int:
     return R * P * es + 2 * R * N * es + 8 + (N // 2) * 4 * (1 if w.rotation else 0) + R * P * es
 
 
+def gated_bytes_per_token_head(w) -> int:
+    """Algorithmic bytes of the gated call: y [R x P] is replaced by the gate
+    input z [P] read and out [P] written."""
+    es, R, P = esize(w), w.rank, w.headdim
+    return prefill_bytes_per_token_head(w) - R * P * es + 2 * P * es
+
+
+def gated_readout_torch(y, z, w_y, w_z):
+    """The gated readout as plain torch ops (the unfused alternative):
+    sum_r w_y y silu(w_z z) over the rank axis, in fp32."""
+    g = torch.nn.functional.silu(w_z * z.float().unsqueeze(-2))
+    return (w_y * y.float() * g).sum(dim=-2).to(y.dtype)
+
+
 def prefill_flops_per_token_head(w, q) -> float:
     """Algorithmic flops of the chunked form with q tokens/chunk (causal blocks only)."""
     R, N, P = w.rank, w.dstate, w.headdim
@@ -127,12 +141,23 @@ def _timed(step, steps, warmup):
     return out
 
 
-def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
+def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None):
     """One step = one m3_scan_prefill over the whole layer (all heads), with the
     final state exported; `nsets` input sets alternate so a step cannot be served
-    from the last-level cache left warm by the previous one."""
+    from the last-level cache left warm by the previous one.  gate="fused": one
+    m3_scan_prefill_gated (z, w_y, w_z) per step; gate="torch": m3_scan_prefill
+    then the same readout in torch ops."""
     dev = torch.device("cuda")
     sets = [inputs.make_prefill_inputs(w, seed=s, device=dev) for s in range(nsets)]
+    if gate:
+        g = torch.Generator(device=dev)
+        g.manual_seed(77)
+        for s in sets:
+            s["z"] = torch.randn((w.batch, w.seqlen, w.nheads, w.headdim), generator=g, device=dev).to(w.torch_dtype)
+        wy = torch.randn((w.nheads, w.rank, w.headdim), generator=g, device=dev)
+        wz = torch.rand((w.nheads, w.rank, w.headdim), generator=g, device=dev) + 0.5
+        outs = [torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=w.torch_dtype, device=dev)
+                for _ in sets]
     dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
     shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, chunk, dcode)
     ws = torch.zeros(m3.prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
@@ -143,13 +168,20 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
 
     def step(i):
         d = sets[i % nsets]
+        if gate == "fused":
+            m3.scan_prefill_gated(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], z=d["z"],
+                                  w_y=wy, w_z=wz, out=outs[i % nsets], h_out=hs[i % nsets], chunk=chunk,
+                                  workspace=ws)
+            return
         m3.scan_prefill(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"],
                         y=ys[i % nsets], h_out=hs[i % nsets], chunk=chunk, workspace=ws)
+        if gate == "torch":
+            outs[i % nsets].copy_(gated_readout_torch(ys[i % nsets], d["z"], wy, wz))
 
     r = _timed(step, steps, warmup)
     ms = r["ms"]
     tok = w.batch * w.seqlen
-    bpt = prefill_bytes_per_token_head(w)
+    bpt = gated_bytes_per_token_head(w) if gate else prefill_bytes_per_token_head(w)
     nbytes = tok * w.nheads * bpt + w.batch * w.nheads * w.dstate * w.headdim * 4
     flops = tok * w.nheads * prefill_flops_per_token_head(w, q_used)
     del sets, ys, hs, ws
@@ -159,13 +191,21 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2):
                 gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
 
-def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32):
+def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=False):
     """One step = one m3_decode_step over all (sequence, head) pairs; >= 3 state
     buffers (384 MiB at the 128-sequence shape) rotate so a step cannot be served
-    from the 256 MB last-level cache left warm by the previous step."""
+    from the 256 MB last-level cache left warm by the previous step.  gated:
+    m3_decode_step_gated with a gate input per step and rank weights."""
     dev = torch.device("cuda")
     S = w.steps
     d = inputs.make_decode_inputs(w, seed=0, device=dev)
+    if gated:
+        g = torch.Generator(device=dev)
+        g.manual_seed(78)
+        zs = torch.randn((S, w.batch, w.nheads, w.headdim), generator=g, device=dev).to(w.torch_dtype)
+        wy = torch.randn((w.nheads, w.rank, w.headdim), generator=g, device=dev)
+        wz = torch.rand((w.nheads, w.rank, w.headdim), generator=g, device=dev) + 0.5
+        out = torch.empty((w.batch, w.nheads, w.headdim), dtype=w.torch_dtype, device=dev)
     hs = [torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=state_dtype, device=dev)
           for _ in range(nstate)]
     y = torch.empty_like(d["x"][0])
@@ -173,6 +213,10 @@ def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32):
     def step(i):
         s = i % S
         kw = dict(B_prev=d["B"][s - 1], x_prev=d["x"][s - 1]) if s else {}
+        if gated:
+            m3.decode_step_gated(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
+                                 d["lam"][s], d["theta"][s], z=zs[s], w_y=wy, w_z=wz, out=out, **kw)
+            return
         m3.decode_step(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
                        d["lam"][s], d["theta"][s], y=y, **kw)
 
@@ -180,6 +224,8 @@ def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32):
     ms = r["ms"]
     upd = w.batch * w.nheads
     nbytes = upd * decode_bytes_per_update(w, 2 if state_dtype == torch.bfloat16 else 4)
+    if gated:   # y [R x P] replaced by z [P] read and out [P] written
+        nbytes += upd * (2 * w.headdim - w.rank * w.headdim) * esize(w)
     del d, hs
     return dict(r, updates_per_s=upd / (ms * 1e-3), tokens_per_s=w.batch / (ms * 1e-3),
                 bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
@@ -341,6 +387,19 @@ def main():
         dec("mimo_decode_n64", dstate=64)
         dec("siso_decode_n128", rank=1)
         dec("siso_decode_n64", rank=1, dstate=64)
+        # the gated readout (rank contraction + rank-expanded SiLU gate) fused
+        # into the kernels, and the prefill's unfused alternative
+        wm = inputs.WORKLOADS["mimo"]
+        rf = bench_prefill(wm, args.steps, max(2, args.warmup // 5), gate="fused")
+        rt = bench_prefill(wm, args.steps, max(2, args.warmup // 5), gate="torch")
+        sec["mimo_prefill_gated"] = dict(tokens_per_s_layer=rf["tokens_per_s"], us=round(rf["ms"] * 1e3, 1),
+                                         us_per_launch=round(rf["ms_launch"] * 1e3, 1),
+                                         hbm_frac=round(rf["gbs_launch"] / HBM_PEAK_GBS, 4),
+                                         us_unfused_torch_readout=round(rt["ms"] * 1e3, 1))
+        rg = bench_decode(wd, 200, 30, gated=True)
+        sec["mimo_decode_gated"] = dict(state_updates_per_s=rg["updates_per_s"], us_per_step=round(rg["ms"] * 1e3, 1),
+                                        us_per_launch=round(rg["ms_launch"] * 1e3, 1),
+                                        hbm_frac=round(rg["gbs_launch"] / HBM_PEAK_GBS, 4))
         out["secondary"] = sec
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
