@@ -644,6 +644,53 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   if (!p.use_maps && wave == 0 && lane < W0)
     fpoll = flag_state(__hip_atomic_load(flags + c - 1 - lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 
+  // Gated readout: the gate operands (w_y, w_z [R][P] fp32, this chunk's z
+  // [nt][P]) go to LDS behind S_in^T in the cos/sin region when they fit.  One
+  // round of loads is issued here and arrives during C's products; it is
+  // written to LDS once the cos/sin table is dead (after the map decision),
+  // together with any remaining rounds.  Otherwise the output stage reads them
+  // from global memory.
+  constexpr uint32_t kSinTB = (uint32_t)round_up_i((int)(sizeof(T) * P * NS), 16);
+  constexpr uint32_t kGwB = 2u * R * P * 4u;
+  constexpr int kWi = R * P / 4;                          // float4 items per weight table
+  constexpr int kZi = P / 8;                              // 8-element items per z row
+  const bool gate_lds = G && (uint32_t)(lay.B - lay.csH) >= kSinTB + kGwB + (uint32_t)(Q * P * sizeof(T));
+  float* s_gw = reinterpret_cast<float*>(smem + lay.csH + kSinTB);
+  T* s_gz = reinterpret_cast<T*>(smem + lay.csH + kSinTB + kGwB);
+  const int gnz = (G && p.z) ? nt * kZi : 0;
+  const size_t gzstep = tstride * P;
+  const Rsrc rWy = buf_rsrc((G && p.wy) ? p.wy + (size_t)h * R * P : nullptr, (G && p.wy) ? R * P * 4 : 0);
+  const Rsrc rWz = buf_rsrc((G && p.wz) ? p.wz + (size_t)h * R * P : nullptr, (G && p.wz) ? R * P * 4 : 0);
+  const Rsrc rZ = buf_rsrc((G && p.z) ? static_cast<const T*>(p.z) + tok0 * P : nullptr,
+                           (G && p.z) ? (uint32_t)(((nt - 1) * gzstep + P) * sizeof(T)) : 0);
+  float4 gwa, gwb;
+  Raw8<T> gzv[2];
+  auto gate_load = [&](int rd) {       // round rd: weight item tid + rd*kThreads, z items 2 per thread
+    const int iw = tid + rd * kThreads;
+    gwa = buf_load_f32x4(rWy, iw < kWi ? 16u * iw : kOff);
+    gwb = buf_load_f32x4(rWz, iw < kWi ? 16u * iw : kOff);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + (2 * rd + u) * kThreads, t = i / kZi, cc = (i - t * kZi) * 8;
+      raw_load_buf(gzv[u], rZ, i < gnz ? (uint32_t)((t * gzstep + cc) * sizeof(T)) : kOff);
+    }
+  };
+  auto gate_store = [&](int rd) {
+    const int iw = tid + rd * kThreads;
+    if (iw < kWi) {
+      *reinterpret_cast<float4*>(s_gw + 4 * iw) = gwa;
+      *reinterpret_cast<float4*>(s_gw + R * P + 4 * iw) = gwb;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + (2 * rd + u) * kThreads, t = i / kZi, cc = (i - t * kZi) * 8;
+      if (i < gnz) *reinterpret_cast<Raw8<T>*>(s_gz + t * P + cc) = gzv[u];
+    }
+  };
+  if constexpr (G) {
+    if (gate_lds) gate_load(0);
+  }
+
   // ---- C: U[n][p] = R(Psi) sum_k W_k B~[k][n] X[k][p] ----
   // Lane layout of a (state tile ntl, column tile pt): rows n = 16 ntl + 4 g4 + j
   // (two whole rotation pairs), column p = 16 pt + l16.
@@ -706,6 +753,16 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     }
   }
   __syncthreads();   // s_misc[2] visible; every read of the cos/sin table is done
+  if constexpr (G) {
+    if (gate_lds) {
+      gate_store(0);
+      const int nround = max((kWi + kThreads - 1) / kThreads, (gnz + 2 * kThreads - 1) / (2 * kThreads));
+      for (int rd = 1; rd < nround; ++rd) {
+        gate_load(rd);
+        gate_store(rd);
+      }
+    }
+  }
   if (s_misc[2]) {
     const Rsrc rU = buf_rsrc(p.maps + chunk_id * SLOT, SLOT * 4);
 #pragma unroll
@@ -1055,6 +1112,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     const T* Zg = p.z ? static_cast<const T*>(p.z) + tok0 * P : nullptr;
     const float* wyh = p.wy ? p.wy + (size_t)h * R * P + TPt * l16 : nullptr;
     const float* wzh = p.wz ? p.wz + (size_t)h * R * P + TPt * l16 : nullptr;
+    const float* swy = s_gw + TPt * l16;
+    const float* swz = s_gw + R * P + TPt * l16;
     constexpr int RG = R < 4 ? R : 4;
 #pragma unroll
     for (int k = 0; k < RTW; ++k) {
@@ -1067,7 +1126,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
         float zv[TPt], o[TPt];
 #pragma unroll
         for (int pn = 0; pn < TPt; ++pn) {
-          zv[pn] = (Zg && valid) ? to_f(Zg[tk * rowstepO + TPt * l16 + pn]) : 0.f;
+          zv[pn] = !(Zg && valid) ? 0.f
+                   : gate_lds ? to_f(s_gz[tk * P + TPt * l16 + pn]) : to_f(Zg[tk * rowstepO + TPt * l16 + pn]);
           o[pn] = 0.f;
         }
 #pragma unroll
@@ -1076,9 +1136,9 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
 #pragma unroll
           for (int pn = 0; pn < TPt; ++pn) {
             float v = yacc[k][pn][j];
-            if (wyh) v *= wyh[r * P + pn];
+            if (wyh) v *= gate_lds ? swy[r * P + pn] : wyh[r * P + pn];
             if (Zg) {
-              const float gz = (wzh ? wzh[r * P + pn] : 1.f) * zv[pn];
+              const float gz = (wzh ? (gate_lds ? swz[r * P + pn] : wzh[r * P + pn]) : 1.f) * zv[pn];
               v *= gz / (1.f + __expf(-gz));
             }
             o[pn] += v;

@@ -72,10 +72,12 @@ def test_prefill_gated(case):
     tol = TOL[w.dtype]
     check_blocks(to64(out), ref, tol, (1, 3), "gated out")
     check_blocks(to64(h), href, tol, (2, 3), "h_out")
-    # the state path is the ungated call's
+    # the state path is the ungated call's (equal up to rounding: with few
+    # sequences a chunk may compose its predecessors' maps, an order of the
+    # products that depends on timing)
     _, h2 = m3.scan_prefill(**{k: dg[k] for k in KEYS}, **cg, chunk=chunk)
     torch.cuda.synchronize()
-    assert torch.equal(h, h2)
+    torch.testing.assert_close(h, h2, rtol=1e-5, atol=1e-5)
 
 
 @pytest.mark.parametrize("shape", [

@@ -124,7 +124,12 @@ def test_chunk_size_invariance(dtype):
 
 
 def test_run_twice_bit_exact():
-    w = inputs.workload("mimo", batch=2, seqlen=257, nheads=2)
+    """64 (sequence, head) pairs at N=128: one workgroup per compute unit fits, so
+    at most 4 chunks of a sequence are in flight and chunks hand over states
+    only, in a fixed order: two runs give the same bits.  (With fewer pairs a
+    chunk may compose its predecessors' maps instead, whose products associate
+    differently, so runs agree to rounding only; the parity tests cover that.)"""
+    w = inputs.workload("mimo", batch=4, seqlen=257, nheads=16)
     dg = dev_inputs(inputs.make_prefill_inputs(w, seed=8))
     note("prefill run twice")
     y1, h1 = _run_prefill(dg, chunk=32)
