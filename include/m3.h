@@ -16,7 +16,9 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor arguments are DEVICE pointers into memory the caller owns; the
- *    library allocates nothing and keeps no state between calls.
+ *    library allocates nothing and keeps no data between calls (it caches only
+ *    per-device launch properties).  The prefill's workspace carries a call
+ *    epoch from one call to the next (see m3_prefill_workspace_bytes).
  *  - Tensors are dense and row-major in the layouts given below.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
  *    call returns without waiting.  Shape, pointer and dtype checks run on the
