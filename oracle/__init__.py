@@ -194,3 +194,30 @@ def scan_gated(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=Non
     """`scan` followed by `gated_readout` of its outputs: (out [b,L,H,P], h)."""
     y, h = scan(x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, nthreads=nthreads)
     return gated_readout(y, z, w_y, w_z), h
+
+
+def prologue(B, C, dt, theta_raw=None, B_prev=None, eps: float = 1e-6, bias_B=None, bias_C=None):
+    """The inputs' pre-processing the explainer describes for Mamba-3 (its
+    sec. 3.4 note: B and C get RMS normalization, then learned head-specific
+    channel biases) and the per-step angle as dt times a raw angle.  Reading:
+    each (token, head, rank) column of B and C (N values) is divided by
+    sqrt(mean of its squares + eps), then bias [H, R, N] is added; B_prev (the
+    token before the sequence, [b, H, R, N]) is treated as a B column; the
+    angle of pair k at step t is dt_t * theta_raw[t, k].
+    B, C [b, L, H, R, N]; dt [b, L, H]; theta_raw [b, L, H, N/2] or None.
+    Returns (B_hat, C_hat, phi, B_prev_hat) in float64."""
+    def norm(v, bias):
+        v = _as64(v)
+        out = v / np.sqrt((v * v).mean(axis=-1, keepdims=True) + eps)
+        return out if bias is None else out + _as64(bias)
+    Bh, Ch = norm(B, bias_B), norm(C, bias_C)
+    phi = None if theta_raw is None else _as64(dt)[..., None] * _as64(theta_raw)
+    Bp = None if B_prev is None else norm(B_prev, bias_B)
+    return Bh, Ch, phi, Bp
+
+
+def scan_prologue(x, B, C, dt, A, lam, theta_raw=None, h0=None, B_prev=None, x_prev=None,
+                  eps: float = 1e-6, bias_B=None, bias_C=None, nthreads: int = 0):
+    """`prologue` followed by `scan`: (y, h)."""
+    Bh, Ch, phi, Bp = prologue(B, C, dt, theta_raw, B_prev, eps, bias_B, bias_C)
+    return scan(x, Bh, Ch, dt, A, lam, phi, h0, Bp, x_prev, nthreads=nthreads)

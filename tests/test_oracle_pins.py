@@ -457,3 +457,46 @@ def test_scan_gated_is_scan_then_readout():
     y, h2 = oracle.scan(**o)
     assert np.array_equal(h, h2)
     np.testing.assert_allclose(out, oracle.gated_readout(y, z, wy), rtol=0, atol=0)
+
+
+def test_prologue_norm_bias_and_angles():
+    rng = np.random.default_rng(11)
+    b, L, H, R, N = 2, 5, 3, 2, 8
+    B = rng.standard_normal((b, L, H, R, N)) * rng.uniform(0.1, 3.0, (b, L, H, R, 1))
+    C = rng.standard_normal((b, L, H, R, N))
+    dt = rng.uniform(0.01, 0.2, (b, L, H))
+    th = rng.uniform(-np.pi, np.pi, (b, L, H, N // 2))
+    Bp = rng.standard_normal((b, H, R, N))
+    # eps = 0, no bias: every column has unit RMS, and scaling a column changes nothing
+    Bh, Ch, phi, Bph = oracle.prologue(B, C, dt, th, Bp, eps=0.0)
+    np.testing.assert_allclose(np.sqrt((Bh ** 2).mean(axis=-1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(np.sqrt((Bph ** 2).mean(axis=-1)), 1.0, rtol=1e-13)
+    Bh2, _, _, _ = oracle.prologue(B * 7.5, C, dt, eps=0.0)
+    np.testing.assert_allclose(Bh2, Bh, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(phi, dt[..., None] * th, rtol=0, atol=0)
+    # one element by hand, with eps and bias
+    bb = rng.standard_normal((H, R, N))
+    bc = rng.standard_normal((H, R, N))
+    Bh, Ch, _, _ = oracle.prologue(B, C, dt, eps=0.25, bias_B=bb, bias_C=bc)
+    i, t, h, r, n = 1, 3, 2, 1, 6
+    ms = sum(B[i, t, h, r, k] ** 2 for k in range(N)) / N
+    assert abs(Bh[i, t, h, r, n] - (B[i, t, h, r, n] / math.sqrt(ms + 0.25) + bb[h, r, n])) < 1e-13
+    ms = sum(C[i, t, h, r, k] ** 2 for k in range(N)) / N
+    assert abs(Ch[i, t, h, r, n] - (C[i, t, h, r, n] / math.sqrt(ms + 0.25) + bc[h, r, n])) < 1e-13
+    # a zero column becomes the bias
+    Z = np.zeros((1, 1, H, R, N))
+    Zh, _, _, _ = oracle.prologue(Z, Z, np.ones((1, 1, H)), eps=1e-6, bias_B=bb)
+    np.testing.assert_allclose(Zh[0, 0], bb, rtol=0, atol=0)
+
+
+def test_scan_prologue_scale_invariance():
+    # with the norm (eps = 0) the outputs do not depend on the scale of B or C columns
+    w = inputs.workload("mimo", batch=1, seqlen=30, nheads=2, headdim=16, dstate=16)
+    d = {k: v.double().numpy() for k, v in inputs.make_prefill_inputs(w, seed=21).items()}
+    rng = np.random.default_rng(22)
+    s = rng.uniform(0.2, 5.0, d["B"].shape[:-1] + (1,))
+    base = dict(x=d["x"], dt=d["dt"], A=d["A"], lam=d["lam"], theta_raw=d["theta"], eps=0.0)
+    y1, h1 = oracle.scan_prologue(B=d["B"], C=d["C"], **base)
+    y2, h2 = oracle.scan_prologue(B=d["B"] * s, C=d["C"] / s, **base)
+    np.testing.assert_allclose(y2, y1, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(h2, h1, rtol=1e-10, atol=1e-10)
