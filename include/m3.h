@@ -209,6 +209,36 @@ m3_status m3_decode_step_gated(const m3_shape* s,
                                const void* z, const float* w_y, const float* w_z,
                                void* out, void* stream);
 
+/* The fused prologue: the pre-processing of B, C and the angles done inside
+ * the kernels' load stage.  Defined by: the explainer's note that Mamba-3's B
+ * and C receive RMS normalization followed by learned head-specific channel
+ * biases (its sec. 3.4 and Table 5(a) remark), and its complex transition
+ * generator (Prop. 2: each complex entry a decayed rotation of a pair), whose
+ * discretization over a step dt turns the generator's angle theta into the
+ * rotation dt * theta as it turns A into the decay exp(dt A).  Reading adopted: every
+ * (token, head, rank) column of B, of C and of B_prev (N values) is divided by
+ * sqrt(mean of its squares + eps) and then gets bias[h, r, :] added (B_prev
+ * takes B's bias; a NULL B_prev stays a zero previous write); `theta` holds raw
+ * angles and the step's angle of pair k is dt_t * theta[.., k]. */
+typedef struct {
+    float eps;              /* added to the mean square before the square root (>= 0;
+                               a zero column with eps = 0 gives NaN) */
+    const float* bias_B;    /* [H, R, N] fp32 added to B and B_prev after the norm, or NULL */
+    const float* bias_C;    /* [H, R, N] fp32 added to C after the norm, or NULL */
+} m3_prologue;
+
+/* m3_decode_step (fp32 state) with the fused prologue applied to B, C, B_prev
+ * and theta.  pro must not be NULL (M3_ERR_NULL); the bias tables are inputs
+ * (they must not overlap y or h, M3_ERR_ALIAS).  Everything else as
+ * m3_decode_step. */
+m3_status m3_decode_step_prologue(const m3_shape* s, const m3_prologue* pro,
+                                  float* h,
+                                  const void* B_prev, const void* x_prev,
+                                  const void* x, const void* B, const void* C,
+                                  const float* dt, const float* A, const float* lam,
+                                  const float* theta,
+                                  void* y, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_str(m3_status st);
 

@@ -199,7 +199,9 @@ def scan_gated(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=Non
 def prologue(B, C, dt, theta_raw=None, B_prev=None, eps: float = 1e-6, bias_B=None, bias_C=None):
     """The inputs' pre-processing the explainer describes for Mamba-3 (its
     sec. 3.4 note: B and C get RMS normalization, then learned head-specific
-    channel biases) and the per-step angle as dt times a raw angle.  Reading:
+    channel biases) and the per-step angle as dt times a raw angle (the
+    complex transition generator of its Prop. 2 discretized over the step, as
+    A becomes exp(dt A)).  Reading:
     each (token, head, rank) column of B and C (N values) is divided by
     sqrt(mean of its squares + eps), then bias [H, R, N] is added; B_prev (the
     token before the sequence, [b, H, R, N]) is treated as a B column; the

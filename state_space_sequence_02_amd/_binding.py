@@ -20,7 +20,7 @@ STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
           4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS"}
 EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_scan_prefill",
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
-           "m3_decode_step_gated", "m3_status_str", "m3_version")
+           "m3_decode_step_gated", "m3_decode_step_prologue", "m3_status_str", "m3_version")
 
 
 class M3Shape(ctypes.Structure):
@@ -28,6 +28,10 @@ class M3Shape(ctypes.Structure):
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class M3Prologue(ctypes.Structure):
+    _fields_ = [("eps", ctypes.c_float), ("bias_B", ctypes.c_void_p), ("bias_C", ctypes.c_void_p)]
 
 
 class M3Error(RuntimeError):
@@ -64,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.m3_scan_prefill_gated.argtypes = [sp] + [vp] * 16 + [sz, vp]
     lib.m3_decode_step_gated.restype = ctypes.c_int
     lib.m3_decode_step_gated.argtypes = [sp] + [vp] * 15
+    lib.m3_decode_step_prologue.restype = ctypes.c_int
+    lib.m3_decode_step_prologue.argtypes = [sp, ctypes.POINTER(M3Prologue)] + [vp] * 12
     lib.m3_status_str.restype = ctypes.c_char_p
     lib.m3_status_str.argtypes = [ctypes.c_int]
     lib.m3_version.restype = ctypes.c_int32
@@ -206,6 +212,35 @@ def decode_step_gated(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=No
         _ptr(out, x.dtype, dev), _stream(dev))
     _check(code)
     return out
+
+
+def _prologue(eps, bias_B, bias_C, dev):
+    return M3Prologue(float(eps), _ptr(bias_B, torch.float32, dev), _ptr(bias_C, torch.float32, dev))
+
+
+def decode_step_prologue(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=None,
+                         eps: float = 1e-6, bias_B=None, bias_C=None):
+    """One decode step (fp32 state h, in place) with the fused prologue
+    (m3_decode_step_prologue): B, C, B_prev RMS-normalised per column over N
+    (+ eps) plus bias_B / bias_C [H,R,N] fp32 (or None); theta holds raw angles,
+    the step angle being dt * theta.  Returns y."""
+    lib = load_library()
+    b, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    shape = make_shape(b, 1, H, P, N, R, 0, _dtype_code(x))
+    if y is None:
+        y = torch.empty_like(x)
+    f32 = torch.float32
+    pro = _prologue(eps, bias_B, bias_C, dev)
+    code = lib.m3_decode_step_prologue(
+        ctypes.byref(shape), ctypes.byref(pro), _ptr(h, f32, dev),
+        _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
+        _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
+        _ptr(y, x.dtype, dev), _stream(dev))
+    _check(code)
+    return y
 
 
 def decode_step(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=None):

@@ -109,6 +109,13 @@ struct Gate {
   const void* z; const float* w_y; const float* w_z;
 };
 
+// The prologue's options (on = false: inputs used as given).
+struct Pro {
+  bool on;
+  float eps; const float* bias_B; const float* bias_C;
+};
+constexpr Pro kNoPro{false, 0.f, nullptr, nullptr};
+
 // Shared by both prefill entry points: `y` is y [b,L,H,R,P], or with a gate
 // out [b,L,H,P].
 m3_status prefill_common(const m3_shape* s,
@@ -181,7 +188,7 @@ m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
                         const void* B_prev, const void* x_prev,
                         const void* x, const void* B, const void* C,
                         const float* dt, const float* A, const float* lam,
-                        const float* theta, const Gate& g, void* y, void* stream) {
+                        const float* theta, const Gate& g, const Pro& pro, void* y, void* stream) {
   m3_status st = check_common(s, false);
   if (st != M3_OK) return st;
   if (state_bf16 && s->dtype != M3_BF16) return M3_ERR_DTYPE;
@@ -200,7 +207,9 @@ m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
       {dt, bh * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, bh * sizeof(float)},
       {theta, theta ? bh * (N / 2) * sizeof(float) : 0},
       {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es},
-      {g.z, g.z ? bh * P * es : 0}, {g.w_y, g.w_y ? wbytes : 0}, {g.w_z, g.w_z ? wbytes : 0}};
+      {g.z, g.z ? bh * P * es : 0}, {g.w_y, g.w_y ? wbytes : 0}, {g.w_z, g.w_z ? wbytes : 0},
+      {pro.bias_B, pro.bias_B ? (size_t)H * R * N * sizeof(float) : 0},
+      {pro.bias_C, pro.bias_C ? (size_t)H * R * N * sizeof(float) : 0}};
   for (const auto& in : ins) {
     if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
     if (overlaps(h, hbytes, in.p, in.n)) return M3_ERR_ALIAS;
@@ -216,6 +225,7 @@ m3_status decode_common(const m3_shape* s, void* h, int state_bf16,
   p.y = g.gated ? nullptr : y;
   p.out = g.gated ? y : nullptr;
   p.z = g.z; p.wy = g.w_y; p.wz = g.z ? g.w_z : nullptr;
+  p.pro = pro.on ? 1 : 0; p.eps = pro.eps; p.biasB = pro.bias_B; p.biasC = pro.bias_C;
   p.batch = b; p.H = H; p.N = N; p.P = P; p.R = R;
   if (launch_decode(p, s->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
@@ -233,7 +243,7 @@ m3_status m3_decode_step(const m3_shape* s,
                          const float* theta,
                          void* y, void* stream) {
   return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{false, nullptr, nullptr, nullptr},
-                       y, stream);
+                       kNoPro, y, stream);
 }
 
 m3_status m3_decode_step_gated(const m3_shape* s,
@@ -244,7 +254,7 @@ m3_status m3_decode_step_gated(const m3_shape* s,
                                const float* theta,
                                const void* z, const float* w_y, const float* w_z,
                                void* out, void* stream) {
-  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{true, z, w_y, w_z}, out, stream);
+  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{true, z, w_y, w_z}, kNoPro, out, stream);
 }
 
 m3_status m3_decode_step_bf16_state(const m3_shape* s,
@@ -255,7 +265,19 @@ m3_status m3_decode_step_bf16_state(const m3_shape* s,
                                     const float* theta,
                                     void* y, void* stream) {
   return decode_common(s, h, 1, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{false, nullptr, nullptr, nullptr},
-                       y, stream);
+                       kNoPro, y, stream);
+}
+
+m3_status m3_decode_step_prologue(const m3_shape* s, const m3_prologue* pro,
+                                  float* h,
+                                  const void* B_prev, const void* x_prev,
+                                  const void* x, const void* B, const void* C,
+                                  const float* dt, const float* A, const float* lam,
+                                  const float* theta,
+                                  void* y, void* stream) {
+  if (!pro) return M3_ERR_NULL;
+  return decode_common(s, h, 0, B_prev, x_prev, x, B, C, dt, A, lam, theta, Gate{false, nullptr, nullptr, nullptr},
+                       Pro{true, pro->eps, pro->bias_B, pro->bias_C}, y, stream);
 }
 
 m3_status m3_scan_prefill(const m3_shape* s,

@@ -60,7 +60,7 @@ __device__ __forceinline__ void raw_unpack(const Raw<float>& r, float (&v)[8]) {
 // (Pointers are passed one by one: a struct of them selected by a run-time
 // index would be placed in private memory.)
 template <typename T>
-struct Item { Raw<T> raw; uint4 th; bool ok, tok; };   // masks applied when staged
+struct Item { Raw<T> raw; uint4 th; uint4 b0, b1; bool ok, tok, bok; };   // masks applied when staged
 
 // Branch-free on purpose: every item issues its loads unconditionally from a
 // clamped address (B stands in for a missing source) and masks the result, so
@@ -74,7 +74,8 @@ __device__ __forceinline__ uint4 mask4(uint4 v, bool ok) {
 template <typename T>
 __device__ __forceinline__ Item<T> load_item(const T* B, const T* C, const T* Bp, const T* X,
                                              const T* Xp, const float* theta, int N,
-                                             int nb8, int nx8, int nitems, int i) {
+                                             int nb8, int nx8, int nitems, int i,
+                                             const float* biasB = nullptr, const float* biasC = nullptr) {
   const int nbB = 3 * nb8, nbX = nbB + 2 * nx8;
   const bool isB = i < nbB, isX = !isB && i < nbX, isT = !isB && !isX && i < nitems;
   const int wb = isB ? i / nb8 : 0;
@@ -89,27 +90,59 @@ __device__ __forceinline__ Item<T> load_item(const T* B, const T* C, const T* Bp
   const bool tok = tb || (isT && theta != nullptr);
   const int toff = tb ? (8 * j - ((8 * j) / N) * N) / 2 : 4 * (i - nbX);
   it.th = *reinterpret_cast<const uint4*>(tok ? theta + toff : reinterpret_cast<const float*>(B));
+  // prologue biases of a B / C / B_prev item (B_prev takes B's)
+  const float* bsrc = isB ? (wb == 1 ? biasC : biasB) : nullptr;
+  const bool bok = ok && bsrc != nullptr;
+  const uint4* bp = reinterpret_cast<const uint4*>(bok ? bsrc + 8 * j : reinterpret_cast<const float*>(B));
+  it.b0 = bp[0];
+  it.b1 = bp[1];
   it.ok = ok;
   it.tok = tok;
+  it.bok = bok;
   return it;
+}
+
+// Prologue: the RMS-norm factor of a B / C / B_prev item's column (the N/8
+// items of one (rank, tensor) column sit in consecutive lanes), computed by
+// every lane; items of other kinds get a factor they do not use.
+template <typename T>
+__device__ __forceinline__ float item_norm(const Item<T>& it, int N, float eps) {
+  Raw<T> raw = it.raw;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(raw.v) / sizeof(uint4)); ++k) raw.v[k] = mask4(raw.v[k], it.ok);
+  float v[8];
+  raw_unpack(raw, v);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off);
+  return rsqrtf(ss / (float)N + eps);
 }
 
 // Widens an item to fp32 into LDS:
 //   sW [N][2R]: (beta R(phi) B_prev) in slots 0..R-1, (gamma B) in R..2R-1
 //   sC [N][R], sXX [2R][P]: x_prev rows then x rows, sCS [N/2]: alpha (cos, sin).
+// scale, tsc: the prologue's norm factor of the item's column and the angle
+// multiplier (dt); 1 without the prologue.
 template <typename T, int R>
 __device__ __forceinline__ void stage_item(float* sW, float* sC, float* sXX, float2* sCS,
                                            int N, int P, int nb8, int nx8, int nitems,
                                            float alpha, float beta, float gamma,
-                                           int i, const Item<T>& it) {
+                                           int i, const Item<T>& it, float scale = 1.f, float tsc = 1.f) {
   Raw<T> raw = it.raw;
 #pragma unroll
   for (int k = 0; k < (int)(sizeof(raw.v) / sizeof(uint4)); ++k) raw.v[k] = mask4(raw.v[k], it.ok);
   const uint4 tm = mask4(it.th, it.tok);
-  const float4 th = make_float4(__uint_as_float(tm.x), __uint_as_float(tm.y), __uint_as_float(tm.z), __uint_as_float(tm.w));
+  const float4 th = make_float4(tsc * __uint_as_float(tm.x), tsc * __uint_as_float(tm.y),
+                                tsc * __uint_as_float(tm.z), tsc * __uint_as_float(tm.w));
   float v[8];
   raw_unpack(raw, v);
   if (i < 3 * nb8) {
+    const uint4 b0 = mask4(it.b0, it.bok), b1 = mask4(it.b1, it.bok);
+    const float bias[8] = {__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
+                           __uint_as_float(b1.x), __uint_as_float(b1.y), __uint_as_float(b1.z), __uint_as_float(b1.w)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * scale + bias[e];
     const int which = i / nb8, j = i - which * nb8;
     const int rr = (8 * j) / N, n0 = 8 * j - rr * N;
     if (which == 0) {
@@ -216,8 +249,10 @@ __global__ __launch_bounds__((decode_threads<S, R>(N, P))) void decode_kernel(De
   const int nth4 = thg ? (N >> 3) : 0;
   const int nitems = 3 * nb8 + 2 * nx8 + nth4;
   const float d = p.dt[bh], lm = p.lam[bh], Ah = p.A[h_idx];
-  const Item<T> it0 = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, tid);
-  const Item<T> it1 = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, tid + NT);
+  const float* bBh = p.pro && p.biasB ? p.biasB + (size_t)h_idx * R * N : nullptr;
+  const float* bCh = p.pro && p.biasC ? p.biasC + (size_t)h_idx * R * N : nullptr;
+  const Item<T> it0 = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, tid, bBh, bCh);
+  const Item<T> it1 = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, tid + NT, bBh, bCh);
 
   // (unconditional, from a clamped unit: a load under a branch would make the
   // compiler wait for everything at the merge)
@@ -232,12 +267,24 @@ __global__ __launch_bounds__((decode_threads<S, R>(N, P))) void decode_kernel(De
   const float alpha = __expf(d * Ah);
   const float beta = (1.f - lm) * d * alpha;
   const float gamma = lm * d;
-  stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, tid, it0);
-  stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, tid + NT, it1);
-  // large shapes (more than two items per thread): the rest, loaded and staged here
-  for (int i = tid + 2 * NT; i < nitems; i += NT)
-    stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, i,
-                     load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, i));
+  // prologue: column norm factors (lane shuffles: every lane takes part) and
+  // angles scaled by dt
+  float sc0 = 1.f, sc1 = 1.f;
+  if (p.pro) {
+    sc0 = item_norm(it0, N, p.eps);
+    sc1 = item_norm(it1, N, p.eps);
+  }
+  const float tsc = p.pro ? d : 1.f;
+  stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, tid, it0, sc0, tsc);
+  stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, tid + NT, it1, sc1, tsc);
+  // large shapes (more than two items per thread): the rest, loaded and staged
+  // here, every lane through every round
+  for (int base = 2 * NT; base < nitems; base += NT) {
+    const int i = base + tid;
+    const Item<T> it = load_item(Bg, Cg, Bpg, Xg, Xpg, thg, N, nb8, nx8, nitems, i, bBh, bCh);
+    const float sc = p.pro ? item_norm(it, N, p.eps) : 1.f;
+    if (i < nitems) stage_item<T, R>(sW, sC, sXX, sCS, N, P, nb8, nx8, nitems, alpha, beta, gamma, i, it, sc, tsc);
+  }
   if (!thg)
     for (int k = tid; k < (N >> 1); k += NT) sCS[k] = make_float2(alpha, 0.f);
   __syncthreads();

@@ -92,6 +92,8 @@ struct DecodeParams {
   void* y;               // y [b,H,R,P], or NULL when `out` is given
   void* out;             // gated readout out [b,H,P], or NULL
   const void* z; const float* wy; const float* wz;   // gate input and weights (each may be NULL)
+  int pro; float eps;    // prologue: B/C/B_prev column RMS norm (+ eps), angle = dt x theta
+  const float* biasB; const float* biasC;             // prologue biases [H][R][N] (each may be NULL)
   int batch, H, N, P, R;
 };
 
