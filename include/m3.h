@@ -227,6 +227,21 @@ typedef struct {
     const float* bias_C;    /* [H, R, N] fp32 added to C after the norm, or NULL */
 } m3_prologue;
 
+/* m3_scan_prefill with the fused prologue applied to B, C, B_prev and theta
+ * inside the kernel's load stage.  pro must not be NULL (M3_ERR_NULL).  The
+ * bias tables take 2 x R x N x 4 bytes of LDS per workgroup beside the chunk's
+ * tiles; a shape whose tiles leave too little room gets M3_ERR_SHAPE.  The
+ * workspace is the one m3_prefill_workspace_bytes gives for the shape.
+ * Everything else as m3_scan_prefill. */
+m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,
+                                   const void* x, const void* B, const void* C,
+                                   const float* dt, const float* A, const float* lam,
+                                   const float* theta,
+                                   const float* h0, const void* B_prev, const void* x_prev,
+                                   void* y, float* h_out,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* m3_decode_step (fp32 state) with the fused prologue applied to B, C, B_prev
  * and theta.  pro must not be NULL (M3_ERR_NULL); the bias tables are inputs
  * (they must not overlap y or h, M3_ERR_ALIAS).  Everything else as

@@ -5,5 +5,5 @@ Python binding plus the seeded synthetic input generators.
 """
 from ._binding import (  # noqa: F401
     M3Error, M3Prologue, M3Shape, M3_BF16, M3_FP32, EXPORTS, LIB_PATH, decode_step, decode_step_gated, decode_step_prologue, load_library,
-    make_shape, prefill_chunk_used, prefill_workspace_bytes, scan_prefill, scan_prefill_gated,
+    make_shape, prefill_chunk_used, prefill_workspace_bytes, scan_prefill, scan_prefill_gated, scan_prefill_prologue,
 )

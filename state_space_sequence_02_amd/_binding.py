@@ -20,7 +20,8 @@ STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
           4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS"}
 EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_scan_prefill",
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
-           "m3_decode_step_gated", "m3_decode_step_prologue", "m3_status_str", "m3_version")
+           "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
+           "m3_status_str", "m3_version")
 
 
 class M3Shape(ctypes.Structure):
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH):
     lib.m3_scan_prefill_gated.argtypes = [sp] + [vp] * 16 + [sz, vp]
     lib.m3_decode_step_gated.restype = ctypes.c_int
     lib.m3_decode_step_gated.argtypes = [sp] + [vp] * 15
+    lib.m3_scan_prefill_prologue.restype = ctypes.c_int
+    lib.m3_scan_prefill_prologue.argtypes = [sp, ctypes.POINTER(M3Prologue)] + [vp] * 13 + [sz, vp]
     lib.m3_decode_step_prologue.restype = ctypes.c_int
     lib.m3_decode_step_prologue.argtypes = [sp, ctypes.POINTER(M3Prologue)] + [vp] * 12
     lib.m3_status_str.restype = ctypes.c_char_p
@@ -216,6 +219,37 @@ def decode_step_gated(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=No
 
 def _prologue(eps, bias_B, bias_C, dev):
     return M3Prologue(float(eps), _ptr(bias_B, torch.float32, dev), _ptr(bias_C, torch.float32, dev))
+
+
+def scan_prefill_prologue(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
+                          y=None, h_out=None, chunk: int = 0, workspace=None, want_state: bool = True,
+                          eps: float = 1e-6, bias_B=None, bias_C=None):
+    """Chunked prefill with the fused prologue (m3_scan_prefill_prologue): B, C
+    and B_prev RMS-normalised per column over N (+ eps) plus bias_B / bias_C
+    [H,R,N] fp32 (or None); theta holds raw angles, the step angle being
+    dt * theta.  Other arguments as scan_prefill.  Returns (y, h_out)."""
+    lib = load_library()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    shape = make_shape(b, L, H, P, N, R, chunk, _dtype_code(x))
+    if y is None:
+        y = torch.empty_like(x)
+    if h_out is None and want_state:
+        h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    need = int(lib.m3_prefill_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    pro = _prologue(eps, bias_B, bias_C, dev)
+    code = lib.m3_scan_prefill_prologue(
+        ctypes.byref(shape), ctypes.byref(pro), _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev),
+        _ptr(C, x.dtype, dev), _ptr(dt, f32, dev), _ptr(A, f32, dev), _ptr(lam, f32, dev), _ptr(theta, f32, dev),
+        _ptr(h0, f32, dev), _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(y, x.dtype, dev), _ptr(h_out, f32, dev),
+        _ptr(workspace, None, dev), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code)
+    return y, h_out
 
 
 def decode_step_prologue(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=None,

@@ -123,7 +123,7 @@ m3_status prefill_common(const m3_shape* s,
                          const float* dt, const float* A, const float* lam,
                          const float* theta,
                          const float* h0, const void* B_prev, const void* x_prev,
-                         const Gate& g, void* y, float* h_out,
+                         const Gate& g, const Pro& pro, void* y, float* h_out,
                          void* workspace, size_t workspace_bytes,
                          void* stream) {
   m3_status st = check_common(s, true);
@@ -155,10 +155,18 @@ m3_status prefill_common(const m3_shape* s,
       {dt, tok * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, tok * sizeof(float)},
       {theta, theta ? tok * (N / 2) * sizeof(float) : 0}, {h0, h0 ? sbytes : 0},
       {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es}, {workspace, plan.bytes},
-      {g.z, g.z ? tok * P * es : 0}, {g.w_y, g.w_y ? wbytes : 0}, {g.w_z, g.w_z ? wbytes : 0}};
+      {g.z, g.z ? tok * P * es : 0}, {g.w_y, g.w_y ? wbytes : 0}, {g.w_z, g.w_z ? wbytes : 0},
+      {pro.bias_B, pro.bias_B ? (size_t)H * R * N * sizeof(float) : 0},
+      {pro.bias_C, pro.bias_C ? (size_t)H * R * N * sizeof(float) : 0}};
   for (const auto& in : ins) {
     if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
     if (h_out && in.p != h0 && overlaps(h_out, sbytes, in.p, in.n)) return M3_ERR_ALIAS;
+  }
+  // the prologue's bias tables take LDS of their own
+  size_t lds = plan.lds;
+  if (pro.on) {
+    lds = fused_lds_bytes(plan.Q, R, N, P, (int)es, 1);
+    if (lds > (size_t)kLdsBudget) return M3_ERR_SHAPE;
   }
   if (h_out && overlaps(h_out, sbytes, y, ybytes)) return M3_ERR_ALIAS;
   if (h_out && h0 && h_out != h0 && overlaps(h_out, sbytes, h0, sbytes)) return M3_ERR_ALIAS;
@@ -170,6 +178,7 @@ m3_status prefill_common(const m3_shape* s,
   f.y = g.gated ? nullptr : y;
   f.out = g.gated ? y : nullptr;
   f.z = g.z; f.wy = g.w_y; f.wz = g.z ? g.w_z : nullptr;
+  f.pro = pro.on ? 1 : 0; f.eps = pro.eps; f.biasB = pro.bias_B; f.biasC = pro.bias_C;
   f.ctl = reinterpret_cast<unsigned long long*>(ws);
   f.flags = reinterpret_cast<unsigned long long*>(ws + plan.off_flags);
   f.recs = reinterpret_cast<float*>(ws + plan.off_recs);
@@ -178,7 +187,7 @@ m3_status prefill_common(const m3_shape* s,
   f.batch = b; f.L = L; f.H = H; f.N = N; f.P = P; f.R = R; f.logR = ilog2(R);
   f.Q = plan.Q; f.nc = plan.nc;
   f.use_maps = 1;   // (the launch decides from the device's resident workgroups)
-  if (launch_fused_prefill(f, plan.lds, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
+  if (launch_fused_prefill(f, lds, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
 }
 
@@ -289,7 +298,7 @@ m3_status m3_scan_prefill(const m3_shape* s,
                           void* workspace, size_t workspace_bytes,
                           void* stream) {
   return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{false, nullptr, nullptr, nullptr},
-                        y, h_out, workspace, workspace_bytes, stream);
+                        kNoPro, y, h_out, workspace, workspace_bytes, stream);
 }
 
 m3_status m3_scan_prefill_gated(const m3_shape* s,
@@ -302,7 +311,20 @@ m3_status m3_scan_prefill_gated(const m3_shape* s,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream) {
   return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{true, z, w_y, w_z},
-                        out, h_out, workspace, workspace_bytes, stream);
+                        kNoPro, out, h_out, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,
+                                   const void* x, const void* B, const void* C,
+                                   const float* dt, const float* A, const float* lam,
+                                   const float* theta,
+                                   const float* h0, const void* B_prev, const void* x_prev,
+                                   void* y, float* h_out,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!pro) return M3_ERR_NULL;
+  return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{false, nullptr, nullptr, nullptr},
+                        Pro{true, pro->eps, pro->bias_B, pro->bias_C}, y, h_out, workspace, workspace_bytes, stream);
 }
 
 const char* m3_status_str(m3_status st) {

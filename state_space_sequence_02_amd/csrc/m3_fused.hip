@@ -15,8 +15,8 @@ hipError_t launch_fused_f32_32(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_f32_64(const FusedParams&, size_t, hipStream_t);
 hipError_t launch_fused_f32_128(const FusedParams&, size_t, hipStream_t);
 
-size_t fused_lds_bytes(int Q, int R, int N, int P, int esize) {
-  return fused::lds_layout(Q, R, N, P, esize).total;
+size_t fused_lds_bytes(int Q, int R, int N, int P, int esize, int pro) {
+  return fused::lds_layout(Q, R, N, P, esize, pro).total;
 }
 
 hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hipStream_t s) {

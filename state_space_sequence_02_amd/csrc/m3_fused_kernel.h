@@ -85,7 +85,7 @@ __host__ __device__ constexpr int round_up_i(int a, int b) { return (a + b - 1) 
 __host__ __device__ inline size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 
 struct Lds {
-  size_t row, rw, W, csH, B, X, misc, total;
+  size_t row, rw, W, csH, B, X, misc, pb, total;
   size_t segl, sega;   // scan scratch, inside B (used only before B~ is staged)
 };
 // LDS row stride (elements) of the X tile.  bf16 X is read with 8-byte
@@ -104,7 +104,8 @@ __host__ __device__ constexpr int x_stride(int P, int esize) {
 //      access that take consecutive groups g of one row read consecutive entries.
 // B: B~ [QRp][N+8];  X: X [QRp][P+8] (permuted columns)
 // segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
-__host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize) {
+// pb: the prologue's bias tables [2][R][N] fp32 (B's, then C's), only when pro.
+__host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize, int pro = 0) {
   const int QRp = round_up_i(Q * R, 32);
   const int kWaves = fused_threads(N) / 64;
   const size_t scan = sizeof(float) * kWaves + sizeof(float4) * (size_t)kWaves * (N / 8);
@@ -116,7 +117,8 @@ __host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize)
   o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2 + 1), (size_t)esize * P * (N + 8)), 16);
   o.X = o.B + round_up_i((int)max_sz((size_t)esize * QRp * (N + 8), scan), 16);
   o.misc = o.X + (size_t)esize * QRp * x_stride(P, esize);
-  o.total = o.misc + 32;
+  o.pb = o.misc + 32;
+  o.total = o.pb + (pro ? sizeof(float) * 2 * (size_t)R * N : 0);
   o.segl = o.B;
   o.sega = o.B + sizeof(float) * kWaves;
   return o;
@@ -334,8 +336,9 @@ __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
 template <int N, int RT>
 constexpr int prefill_waves_per_simd() { return (fused_threads(N) == 1024 || (N <= 64 && RT <= 2)) ? 4 : 2; }
 
-// G: the gated readout (out [b,L,H,P]) replaces the y store.
-template <typename T, int N, int P, int R, int RT, bool G>
+// G: the gated readout (out [b,L,H,P]) replaces the y store.  PRO: the fused
+// prologue (B, C, B_prev column RMS norm + biases; angle = dt x raw angle).
+template <typename T, int N, int P, int R, int RT, bool G, bool PRO>
 __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())) void prefill_kernel(FusedParams p) {
   constexpr int kThreads = fused_threads(N);
   constexpr int kWaves = kThreads / 64;
@@ -364,7 +367,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int Q = p.Q;
-  const Lds lay = lds_layout(Q, R, N, P, sizeof(T));
+  const Lds lay = lds_layout(Q, R, N, P, sizeof(T), PRO ? 1 : 0);
+  float* s_pb = reinterpret_cast<float*>(smem + lay.pb);   // prologue biases (PRO)
   float4* s_row = reinterpret_cast<float4*>(smem + lay.row);
   float* s_rw = reinterpret_cast<float*>(smem + lay.rw);
   float* s_W = reinterpret_cast<float*>(smem + lay.W);
@@ -408,6 +412,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   const uint32_t rsB = (uint32_t)rowstepB * esz, rsX = (uint32_t)rowstepX * esz;
   float dv, lmv, dnv, lmnv_raw;
   float4 th4[4];
+  float thdt[4];          // PRO: dt of the angle tokens
+  float4 pbv0, pbv1;      // PRO: this thread's bias items (B's, C's)
   Raw8<T> raw[kBatch];
   Raw8<T> craw[RTW][NK];
   const int lane = tid & 63, wave = tid >> 6;
@@ -467,6 +473,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     const int nnext = min(nt, p.L - t0 - 1);    // tokens whose successor exists
     const Rsrc rDn = buf_rsrc(p.dt + tok0 + tstride, nnext > 0 ? (nnext - 1) * tsb + 4 : 0);
     const Rsrc rLn = buf_rsrc(p.lam + tok0 + tstride, nnext > 0 ? (nnext - 1) * tsb + 4 : 0);
+    if constexpr (PRO) {   // first, so they are back before the rest
+      constexpr int kPb = R * N / 4;                      // float4 items per bias table
+      const Rsrc rBB = buf_rsrc(p.biasB ? p.biasB + (size_t)h * R * N : nullptr, p.biasB ? R * N * 4 : 0);
+      const Rsrc rBC = buf_rsrc(p.biasC ? p.biasC + (size_t)h * R * N : nullptr, p.biasC ? R * N * 4 : 0);
+      pbv0 = buf_load_f32x4(rBB, tid < kPb ? 16u * tid : kOff);
+      pbv1 = buf_load_f32x4(rBC, tid < kPb ? 16u * tid : kOff);
+    }
     const uint32_t toff = tid < Q ? tid * tsb : kOff;
     dv = buf_load_f32(rD, toff);
     lmv = buf_load_f32(rL, toff);
@@ -477,6 +490,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     for (int j = 0; j < 4; ++j) {
       const bool ok = j < ALEN && sg < NSEG;
       th4[j] = buf_load_f32x4(rT, ok ? (uint32_t)(sg * ALEN + j) * tsb * NH + 16 * cg : kOff);
+    }
+    if constexpr (PRO) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = j < ALEN && sg < NSEG;
+        thdt[j] = buf_load_f32(rD, ok ? (uint32_t)(sg * ALEN + j) * tsb : kOff);
+      }
     }
     const uint32_t extB = (uint32_t)(nt - 1) * rsB + R * N * esz;
     batch_loads(buf_rsrc(static_cast<const T*>(p.B) + tok0 * R * N, extB),
@@ -515,6 +535,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     s_misc[3] = 0;      // wave counter: map published
     s_misc[4] = 0;      // wave counter: state published
   }
+  if constexpr (PRO) {
+    constexpr int kPb = R * N / 4;
+    if (tid < kPb) {
+      *reinterpret_cast<float4*>(s_pb + 4 * tid) = pbv0;
+      *reinterpret_cast<float4*>(s_pb + R * N + 4 * tid) = pbv1;
+    }
+  }
   const float lmnv = (t0 + tid + 1 < p.L && tid < nt) ? lmnv_raw : 1.f;   // (only multiplies dnv = 0 otherwise)
 
   // chunk-local cumulative log decay (token tid) and phases (this thread's
@@ -529,6 +556,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   for (int off = 1; off < 64; off <<= 1) {
     const float u = __shfl_up(lsc, off);
     if (lane >= off) lsc += u;
+  }
+  if constexpr (PRO) {   // raw angles: the step's angle is dt x theta
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d = thdt[j];
+      th4[j] = make_float4(d * th4[j].x, d * th4[j].y, d * th4[j].z, d * th4[j].w);
+    }
   }
 #pragma unroll
   for (int j = 1; j < 4; ++j)
@@ -608,10 +642,28 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = base + u * kThreads;
+      float pscale = 1.f;
+      if constexpr (PRO) {   // every lane: a B row's N/8 items sit in consecutive lanes
+        float v[8];
+        raw_unpack(raw[u], v);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+#pragma unroll
+        for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off);
+        pscale = rsqrtf(ss / (float)N + p.eps);
+      }
       if (i < nbi) {
         const int row = i / (N / 8), ng = i - row * (N / 8);
         float v[8];
         raw_unpack(raw[u], v);
+        if constexpr (PRO) {
+          if (row < rows) {
+            const float* bb = s_pb + (row & (R - 1)) * N + ng * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * pscale + bb[e];
+          }
+        }
         if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * CSS + ng, NG);
         store8<T>(s_B + row * NS + ng * 8, v);
       } else if (i >= nbp && i < ntot) {
@@ -627,11 +679,32 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   for (int k = 0; k < RTW; ++k) {
     const int row_a = (k < ntiles_w ? tile_of(k) : 0) * 16 + l16;
     const int ta = row_a < rows ? row_a >> LOGR : 0;
+    float cscale = 1.f;
+    if constexpr (PRO) {   // a C row: NK slices in this lane, 4 lane groups (g4)
+      float ss = 0.f;
+#pragma unroll
+      for (int kn = 0; kn < NK; ++kn) {
+        float v[8];
+        raw_unpack(craw[k][kn], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      cscale = rsqrtf(ss / (float)N + p.eps);
+    }
 #pragma unroll
     for (int kn = 0; kn < NK; ++kn) {
       const int n0 = kn * 32 + 8 * g4;
       float v[8];
       raw_unpack(craw[k][kn], v);
+      if constexpr (PRO) {
+        if (n0 < N && row_a < rows) {
+          const float* bc = s_pb + R * N + (row_a & (R - 1)) * N + n0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * cscale + bc[e];
+        }
+      }
       if (n0 < N) rotate_neg(v, s_cs + ta * CSS + n0 / 8, NG);
 #pragma unroll
       for (int e = 0; e < 8; ++e) frag_set(cf[k][kn], e, v[e]);
@@ -800,6 +873,24 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
     if (p.Bp) kappa0 = (1.f - p.lam[tok0]) * p.dt[tok0];
     const T* Bp = p.Bp ? static_cast<const T*>(p.Bp) + (size_t)bh * R * N : nullptr;
     const T* xp = p.xp ? static_cast<const T*>(p.xp) + (size_t)bh * R * P : nullptr;
+    float bps[R];   // PRO: B_prev column norm factors (every wave reduces over its lanes)
+#pragma unroll
+    for (int r = 0; r < R; ++r) bps[r] = 1.f;
+    if constexpr (PRO) {
+      if (Bp) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float ss = 0.f;
+          for (int n = lane; n < N; n += 64) {
+            const float t = to_f(Bp[r * N + n]);
+            ss += t * t;
+          }
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+          bps[r] = rsqrtf(ss / (float)N + p.eps);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
       const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
@@ -814,7 +905,11 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
             if (Bp) {
               float acc = 0.f;
 #pragma unroll
-              for (int r = 0; r < R; ++r) acc += to_f(Bp[r * N + n0 + e]) * to_f(xp[r * P + hc]);
+              for (int r = 0; r < R; ++r) {
+                float bv = to_f(Bp[r * N + n0 + e]);
+                if constexpr (PRO) bv = bv * bps[r] + s_pb[r * N + n0 + e];
+                acc += bv * to_f(xp[r * P + hc]);
+              }
               v += kappa0 * acc;
             }
             FU[i][j][e] = v;
@@ -1158,13 +1253,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())
   }
 }
 
-template <typename T, int N, int P, int R, int RT, bool G>
+template <typename T, int N, int P, int R, int RT, bool G, bool PRO>
 hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   // LDS limit raised once per instantiation
   static bool lds_set = false;
   hipError_t e;
   if (!lds_set && lds > 64 * 1024) {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G>),
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G, PRO>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)) != hipSuccess)
       return e;
     lds_set = true;
@@ -1189,7 +1284,7 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G>), fused_threads(N), lds) == hipSuccess)
+            &per, reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G, PRO>), fused_threads(N), lds) == hipSuccess)
       resident = cus * per;
     if (dev >= 0 && resident > 0)
       cache[dev].store(((unsigned long long)lds << 32) | (unsigned)resident, std::memory_order_relaxed);
@@ -1197,7 +1292,7 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   FusedParams q = p;
   const size_t nbh = (size_t)p.batch * p.H;
   q.use_maps = !(resident > 0 && (size_t)resident <= 4 * nbh);
-  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT, G>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<T, N, P, R, RT, G, PRO>), dim3((unsigned)grid), dim3(fused_threads(N)), lds, stream, q);
   return hipGetLastError();
 }
 
@@ -1213,15 +1308,23 @@ hipError_t launch_rt(const FusedParams& p, size_t lds, hipStream_t s) {
   const int rt = row_tiles_per_wave(p.Q, R, N);
   constexpr int kWaves = fused_threads(N) / 64;
   constexpr int kMaxRT = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;
+  // variants: plain, gated readout, prologue (not both)
+  if (p.out && p.pro) return hipErrorInvalidValue;
   if (p.out) {
-    if (rt <= 1) return launch<T, N, P, R, 1, true>(p, lds, s);
-    if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), true>(p, lds, s);
-    if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), true>(p, lds, s);
+    if (rt <= 1) return launch<T, N, P, R, 1, true, false>(p, lds, s);
+    if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), true, false>(p, lds, s);
+    if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), true, false>(p, lds, s);
     return hipErrorInvalidValue;
   }
-  if (rt <= 1) return launch<T, N, P, R, 1, false>(p, lds, s);
-  if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), false>(p, lds, s);
-  if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), false>(p, lds, s);
+  if (p.pro) {
+    if (rt <= 1) return launch<T, N, P, R, 1, false, true>(p, lds, s);
+    if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), false, true>(p, lds, s);
+    if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), false, true>(p, lds, s);
+    return hipErrorInvalidValue;
+  }
+  if (rt <= 1) return launch<T, N, P, R, 1, false, false>(p, lds, s);
+  if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), false, false>(p, lds, s);
+  if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), false, false>(p, lds, s);
   return hipErrorInvalidValue;
 }
 

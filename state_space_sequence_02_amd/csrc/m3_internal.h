@@ -61,6 +61,8 @@ struct FusedParams {
   unsigned long long* ctl; unsigned long long* flags; float* recs; float* maps; float* states;
   int batch, L, H, N, P, R, logR, Q, nc;
   int use_maps;          // publish chunk maps when the predecessor's state is late
+  int pro; float eps;    // prologue: B/C/B_prev column RMS norm (+ eps), angle = dt x theta
+  const float* biasB; const float* biasC;             // prologue biases [H][R][N] (each may be NULL)
 };
 // Threads per prefill workgroup: 1024 for N >= 128 (one workgroup fills a CU
 // there, and twice the waves share each chunk's work), 512 below.
@@ -78,7 +80,7 @@ __host__ __device__ constexpr int fused_slot_floats(int N, int P) {
 // angles (tokens x N/2) per chunk; they bound the per-thread prefetch registers.
 inline int fused_max_rows(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
 constexpr int kFusedAngleCap = 8192;
-size_t fused_lds_bytes(int Q, int R, int N, int P, int esize);
+size_t fused_lds_bytes(int Q, int R, int N, int P, int esize, int pro = 0);
 hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

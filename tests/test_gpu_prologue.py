@@ -67,3 +67,67 @@ def test_decode_prologue(shape, biases):
     tol = TOL[w.dtype]
     check_blocks(to64(torch.stack(ys)), yr, tol, (3, 4), "decode prologue y")
     check_blocks(to64(h), hr, tol, (2, 3), "decode prologue h")
+
+
+PREFILL = [
+    # (workload, overrides, chunk, biases, carry)
+    ("siso", dict(batch=2, seqlen=300, nheads=3), 64, True, True),
+    ("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),          # two tiles per wave
+    ("siso", dict(batch=2, seqlen=200, nheads=2), 128, False, False),
+    ("mimo", dict(batch=2, seqlen=130, nheads=2), 64, True, True),
+    ("mimo", dict(batch=1, seqlen=97, nheads=2), 32, False, True),
+    ("mimo", dict(batch=1, seqlen=70, nheads=2, rank=2, dstate=64), 64, True, True),
+    ("mimo", dict(batch=1, seqlen=90, nheads=2, rank=8, dstate=32), 16, True, True),
+    ("mimo", dict(batch=1, seqlen=90, nheads=1, rank=8, headdim=128, dstate=128), 16, True, True),
+    ("tiny", dict(batch=1, seqlen=100, nheads=2, rank=4, headdim=32, dstate=32), 32, True, True),   # fp32
+    ("tiny", dict(batch=2, seqlen=77, nheads=1), 16, True, True),                                    # fp32 R=1
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: f"{c[0]}-{c[1]}-q{c[2]}-b{int(c[3])}c{int(c[4])}")
+def test_prefill_prologue(case):
+    name, kw, chunk, biases, carry = case
+    w = inputs.workload(name, **kw)
+    seed, eps = 700 + chunk + w.rank, 1e-5
+    d = inputs.make_prefill_inputs(w, seed=seed)
+    c = inputs.random_carry(w, seed=seed + 1) if carry else {}
+    th, bb, bc = _pro_inputs(w, seed + 2, (w.batch, w.seqlen), biases)
+    dg, cg = dev_inputs(d), (dev_inputs(c) if c else {})
+    note(f"prefill prologue {name} {kw} {w.dtype} chunk={chunk} biases={biases} carry={carry}")
+    y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
+                                    chunk=chunk, eps=eps, bias_B=None if bb is None else bb.cuda(),
+                                    bias_C=None if bc is None else bc.cuda())
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_prologue(_np(d["x"]), _np(d["B"]), _np(d["C"]), _np(d["dt"]), _np(d["A"]), _np(d["lam"]),
+                                  _np(th), h0=_np(c.get("h0")), B_prev=_np(c.get("B_prev")),
+                                  x_prev=_np(c.get("x_prev")), eps=eps, bias_B=_np(bb), bias_C=_np(bc))
+    tol = TOL[w.dtype]
+    check_blocks(to64(y), yr, tol, (1, 3, 4), "prologue y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, tol, (2, 3), "prologue h_out")
+
+
+def test_prologue_prefill_then_decode():
+    """prefill with the prologue over L - 2 tokens, then two decode steps with
+    it, equals the prologue's recurrence over the whole sequence."""
+    w = inputs.workload("mimo", batch=2, seqlen=70, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=801)
+    th, bb, bc = _pro_inputs(w, 802, (w.batch, w.seqlen), True)
+    dg = dev_inputs(d)
+    thg, bbg, bcg = th.cuda(), bb.cuda(), bc.cuda()
+    L0 = w.seqlen - 2
+    note("prologue prefill then prologue decode")
+    cut = lambda t: t[:, :L0].contiguous()
+    y0, h = m3.scan_prefill_prologue(cut(dg["x"]), cut(dg["B"]), cut(dg["C"]), cut(dg["dt"]), dg["A"], cut(dg["lam"]),
+                                     cut(thg), chunk=32, eps=1e-5, bias_B=bbg, bias_C=bcg)
+    ys = [y0]
+    for t in (L0, L0 + 1):
+        at = lambda k: dg[k][:, t].contiguous()
+        yt = m3.decode_step_prologue(h, at("x"), at("B"), at("C"), at("dt"), dg["A"], at("lam"),
+                                     thg[:, t].contiguous(), B_prev=dg["B"][:, t - 1].contiguous(),
+                                     x_prev=dg["x"][:, t - 1].contiguous(), eps=1e-5, bias_B=bbg, bias_C=bcg)
+        ys.append(yt[:, None])
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_prologue(_np(d["x"]), _np(d["B"]), _np(d["C"]), _np(d["dt"]), _np(d["A"]), _np(d["lam"]),
+                                  _np(th), eps=1e-5, bias_B=_np(bb), bias_C=_np(bc))
+    check_blocks(to64(torch.cat(ys, dim=1)), yr, TOL[w.dtype], (1, 3, 4), "y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL[w.dtype], (2, 3), "h")
