@@ -56,6 +56,16 @@ def gated_readout_torch(y, z, w_y, w_z):
     return (w_y * y.float() * g).sum(dim=-2).to(y.dtype)
 
 
+def prologue_torch(B, C, dt, theta_raw, bias_B, bias_C, eps):
+    """The prologue as plain torch ops (the unfused alternative): RMS norm of
+    B and C over N in fp32 plus the biases, rounded back to the input dtype,
+    and the angle dt * theta_raw."""
+    def norm(v, bias):
+        f = v.float()
+        return (f * torch.rsqrt(f.square().mean(dim=-1, keepdim=True) + eps) + bias).to(v.dtype)
+    return norm(B, bias_B), norm(C, bias_C), dt.unsqueeze(-1) * theta_raw
+
+
 def prefill_flops_per_token_head(w, q) -> float:
     """Algorithmic flops of the chunked form with q tokens/chunk (causal blocks only)."""
     R, N, P = w.rank, w.dstate, w.headdim
@@ -141,14 +151,23 @@ def _timed(step, steps, warmup):
     return out
 
 
-def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None):
+def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None):
     """One step = one m3_scan_prefill over the whole layer (all heads), with the
     final state exported; `nsets` input sets alternate so a step cannot be served
     from the last-level cache left warm by the previous one.  gate="fused": one
     m3_scan_prefill_gated (z, w_y, w_z) per step; gate="torch": m3_scan_prefill
-    then the same readout in torch ops."""
+    then the same readout in torch ops.  prologue="fused": one
+    m3_scan_prefill_prologue (raw angles, B/C biases) per step; "torch": the
+    prologue in torch ops, then m3_scan_prefill."""
     dev = torch.device("cuda")
     sets = [inputs.make_prefill_inputs(w, seed=s, device=dev) for s in range(nsets)]
+    if prologue:
+        g = torch.Generator(device=dev)
+        g.manual_seed(79)
+        for s in sets:
+            s["theta"] = (torch.rand(s["theta"].shape, generator=g, device=dev) * 2 - 1) * math.pi
+        pbB = torch.randn((w.nheads, w.rank, w.dstate), generator=g, device=dev) * 0.5
+        pbC = torch.randn((w.nheads, w.rank, w.dstate), generator=g, device=dev) * 0.5
     if gate:
         g = torch.Generator(device=dev)
         g.manual_seed(77)
@@ -168,6 +187,16 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None):
 
     def step(i):
         d = sets[i % nsets]
+        if prologue == "fused":
+            m3.scan_prefill_prologue(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"],
+                                     y=ys[i % nsets], h_out=hs[i % nsets], chunk=chunk, workspace=ws,
+                                     eps=1e-6, bias_B=pbB, bias_C=pbC)
+            return
+        if prologue == "torch":
+            Bh, Ch, phi = prologue_torch(d["B"], d["C"], d["dt"], d["theta"], pbB, pbC, 1e-6)
+            m3.scan_prefill(d["x"], Bh, Ch, d["dt"], d["A"], d["lam"], phi,
+                            y=ys[i % nsets], h_out=hs[i % nsets], chunk=chunk, workspace=ws)
+            return
         if gate == "fused":
             m3.scan_prefill_gated(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], z=d["z"],
                                   w_y=wy, w_z=wz, out=outs[i % nsets], h_out=hs[i % nsets], chunk=chunk,
@@ -191,11 +220,12 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None):
                 gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
 
-def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=False):
+def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=False, prologue=False):
     """One step = one m3_decode_step over all (sequence, head) pairs; >= 3 state
     buffers (384 MiB at the 128-sequence shape) rotate so a step cannot be served
     from the 256 MB last-level cache left warm by the previous step.  gated:
-    m3_decode_step_gated with a gate input per step and rank weights."""
+    m3_decode_step_gated with a gate input per step and rank weights.  prologue:
+    m3_decode_step_prologue with raw angles and B/C biases."""
     dev = torch.device("cuda")
     S = w.steps
     d = inputs.make_decode_inputs(w, seed=0, device=dev)
@@ -206,6 +236,12 @@ def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=Fa
         wy = torch.randn((w.nheads, w.rank, w.headdim), generator=g, device=dev)
         wz = torch.rand((w.nheads, w.rank, w.headdim), generator=g, device=dev) + 0.5
         out = torch.empty((w.batch, w.nheads, w.headdim), dtype=w.torch_dtype, device=dev)
+    if prologue:
+        g = torch.Generator(device=dev)
+        g.manual_seed(80)
+        d["theta"] = (torch.rand(d["theta"].shape, generator=g, device=dev) * 2 - 1) * math.pi
+        pbB = torch.randn((w.nheads, w.rank, w.dstate), generator=g, device=dev) * 0.5
+        pbC = torch.randn((w.nheads, w.rank, w.dstate), generator=g, device=dev) * 0.5
     hs = [torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=state_dtype, device=dev)
           for _ in range(nstate)]
     y = torch.empty_like(d["x"][0])
@@ -213,6 +249,10 @@ def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=Fa
     def step(i):
         s = i % S
         kw = dict(B_prev=d["B"][s - 1], x_prev=d["x"][s - 1]) if s else {}
+        if prologue:
+            m3.decode_step_prologue(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
+                                    d["lam"][s], d["theta"][s], y=y, eps=1e-6, bias_B=pbB, bias_C=pbC, **kw)
+            return
         if gated:
             m3.decode_step_gated(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
                                  d["lam"][s], d["theta"][s], z=zs[s], w_y=wy, w_z=wz, out=out, **kw)
@@ -407,6 +447,18 @@ def main():
         sec["mimo_decode_gated"] = dict(state_updates_per_s=rg["updates_per_s"], us_per_step=round(rg["ms"] * 1e3, 1),
                                         us_per_launch=round(rg["ms_launch"] * 1e3, 1),
                                         hbm_frac=round(rg["gbs_launch"] / HBM_PEAK_GBS, 4))
+        # the fused prologue (BCNorm + B/C biases + angle = dt x raw angle), and
+        # the prefill's unfused alternative (the prologue in torch ops first)
+        pf = bench_prefill(wm, args.steps, max(2, args.warmup // 5), prologue="fused")
+        pt = bench_prefill(wm, args.steps, max(2, args.warmup // 5), prologue="torch")
+        sec["mimo_prefill_prologue"] = dict(tokens_per_s_layer=pf["tokens_per_s"], us=round(pf["ms"] * 1e3, 1),
+                                            us_per_launch=round(pf["ms_launch"] * 1e3, 1),
+                                            hbm_frac=round(pf["gbs_launch"] / HBM_PEAK_GBS, 4),
+                                            us_unfused_torch_prologue=round(pt["ms"] * 1e3, 1))
+        rp = bench_decode(wd, 200, 30, prologue=True)
+        sec["mimo_decode_prologue"] = dict(state_updates_per_s=rp["updates_per_s"], us_per_step=round(rp["ms"] * 1e3, 1),
+                                           us_per_launch=round(rp["ms_launch"] * 1e3, 1),
+                                           hbm_frac=round(rp["gbs_launch"] / HBM_PEAK_GBS, 4))
         out["secondary"] = sec
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

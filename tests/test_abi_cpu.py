@@ -154,6 +154,37 @@ def test_gated_validation_codes(lib):
     assert decode(m3.make_shape(0, 1, 2, 64, 128, 4, 0, 1), h=None) == 0
 
 
+def test_prologue_validation_codes(lib):
+    ok = m3.make_shape(2, 128, 3, 64, 64, 4, 64, m3.M3_BF16)
+    pro = m3.M3Prologue(1e-6, FAR[11], FAR[12])
+
+    def prefill(shape, p=pro, **over):
+        a = dict(x=FAR[0], B=FAR[1], C=FAR[2], dt=FAR[3], A=FAR[4], lam=FAR[5], theta=None, h0=None,
+                 Bp=None, xp=None, y=FAR[9], h_out=None, ws=FAR[10], wsb=1 << 40)
+        a.update(over)
+        return lib.m3_scan_prefill_prologue(ctypes.byref(shape), None if p is None else ctypes.byref(p),
+                                            a["x"], a["B"], a["C"], a["dt"], a["A"], a["lam"], a["theta"],
+                                            a["h0"], a["Bp"], a["xp"], a["y"], a["h_out"], a["ws"], a["wsb"], None)
+
+    def decode(shape, p=pro, **over):
+        a = dict(h=FAR[0], Bp=None, xp=None, x=FAR[1], B=FAR[2], C=FAR[3], dt=FAR[4], A=FAR[5], lam=FAR[6],
+                 theta=None, y=FAR[9])
+        a.update(over)
+        return lib.m3_decode_step_prologue(ctypes.byref(shape), None if p is None else ctypes.byref(p),
+                                           a["h"], a["Bp"], a["xp"], a["x"], a["B"], a["C"], a["dt"], a["A"],
+                                           a["lam"], a["theta"], a["y"], None)
+
+    assert prefill(ok, p=None) == 1
+    assert prefill(ok, y=FAR[11] + 8) == 6       # y overlaps the B bias table
+    assert prefill(ok, ws=None) == 4
+    assert prefill(m3.make_shape(2, 128, 3, 64, 256, 4, 64, 1)) == 2      # N = 256: decode only
+    dec = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
+    assert decode(dec, p=None) == 1
+    assert decode(dec, y=FAR[12]) == 6           # y aliases the C bias table
+    assert decode(dec, h=FAR[11] + 4) == 6       # the state overlaps a bias table
+    assert decode(m3.make_shape(0, 1, 2, 64, 128, 4, 0, 1), h=None) == 0
+
+
 @pytest.mark.parametrize("name", ["tiny", "siso", "mimo", "long"])
 def test_workspace_size_matches_layout(lib, name):
     from state_space_sequence_02_amd import inputs
