@@ -12,8 +12,8 @@
 // Work unit = (pair k, quad q): rows 2k and 2k+1, columns 4q..4q+3.  Consecutive
 // lanes take consecutive quads of the same row pair, so every load/store
 // instruction covers whole 16-byte-aligned runs of a row (8-byte runs for a
-// bf16 state).  The rotation of a
-// pair is lane-local because both of its rows sit in the same unit.
+// bf16 state).  The rotation of a pair is lane-local because both of its rows
+// sit in the same unit.
 // The coefficients are folded into the small operands once per workgroup:
 //   H <- [alpha R(phi)] H + sum_r (beta R(phi) B_prev)[:, r] x_prev[r]^T + (gamma B)[:, r] x[r]^T
 // so each state element costs one 2x2 rotation and one 2R-long FMA chain.  The
@@ -21,7 +21,9 @@
 // across lanes that share a quad (xor shuffles within the wave, then LDS
 // across waves).  The gated entry point contracts the ranks of Y with the
 // rank-expanded SiLU gate in the same final pass and writes one value per
-// head column instead of R.
+// head column instead of R.  The prologue entry point normalises the B, C and
+// B_prev columns (with their biases) and scales the raw angles by dt while
+// the small operands are staged.
 #include "m3_device.h"
 
 namespace m3 {

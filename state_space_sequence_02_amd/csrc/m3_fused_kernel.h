@@ -55,12 +55,20 @@
 //      source block the masked intra-chunk products on MFMA (each B~ / X read
 //      serves every tile of the wave); flag 2 raised; y stored.
 //
+// Variants (template flags): G, the gated readout, replaces the y store by the
+// rank contraction with the rank-expanded SiLU gate (its operands loaded
+// during phase C and written to the free tail of the cos/sin region once the
+// table is dead); PRO, the prologue,
+// normalises B and C rows (and B_prev) with their biases while they are
+// staged and scales the raw angles by dt before the phase scan.
+//
 // Column order: X is staged in LDS with its columns permuted so that the
 // 16-column MFMA tile pt holds head columns TPt*l + pt (l = 0..15, TPt = P/16).
 // U, the chunk states in the workspace (stored in register order), S_in^T and
-// the output accumulators all follow that order; a lane then holds TPt consecutive head columns of each of
-// its output rows, and y leaves as full row segments.  h0, h_out, x_prev and y
-// are read/written in the head's own column order.
+// the output accumulators all follow that order; a lane then holds TPt
+// consecutive head columns of each of its output rows, and y leaves as full
+// row segments.  h0, h_out, x_prev and y are read/written in the head's own
+// column order.
 #pragma once
 
 #include <algorithm>
