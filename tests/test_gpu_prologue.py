@@ -131,3 +131,34 @@ def test_prologue_prefill_then_decode():
                                   _np(th), eps=1e-5, bias_B=_np(bb), bias_C=_np(bc))
     check_blocks(to64(torch.cat(ys, dim=1)), yr, TOL[w.dtype], (1, 3, 4), "y", elem_axes=(3, 4))
     check_blocks(to64(h), hr, TOL[w.dtype], (2, 3), "h")
+
+
+def test_fused_entry_points_edges():
+    """L = 0 (h_out receives h0), L = 1 with h_out aliasing h0, for the gated
+    and prologue prefill entry points."""
+    w = inputs.workload("mimo", batch=2, seqlen=1, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=901)
+    c = inputs.random_carry(w, seed=902)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    th, bb, bc = _pro_inputs(w, 903, (w.batch, w.seqlen), True)
+    note("fused entry points: L=1 in place, L=0")
+    h_io = cg["h0"].clone()
+    y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(),
+                                    h0=h_io, B_prev=cg["B_prev"], x_prev=cg["x_prev"], h_out=h_io, chunk=16,
+                                    eps=1e-5, bias_B=bb.cuda(), bias_C=bc.cuda())
+    torch.cuda.synchronize()
+    assert h.data_ptr() == h_io.data_ptr()
+    yr, hr = oracle.scan_prologue(_np(d["x"]), _np(d["B"]), _np(d["C"]), _np(d["dt"]), _np(d["A"]), _np(d["lam"]),
+                                  _np(th), h0=_np(c["h0"]), B_prev=_np(c["B_prev"]), x_prev=_np(c["x_prev"]),
+                                  eps=1e-5, bias_B=_np(bb), bias_C=_np(bc))
+    check_blocks(to64(y), yr, TOL[w.dtype], (1, 3, 4), "y L=1", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL[w.dtype], (2, 3), "h L=1")
+    d0 = dev_inputs(inputs.make_prefill_inputs(w, seed=901, seqlen=0))
+    z0 = torch.empty((w.batch, 0, w.nheads, w.headdim), dtype=w.torch_dtype, device="cuda")
+    out0, h0 = m3.scan_prefill_gated(d0["x"], d0["B"], d0["C"], d0["dt"], d0["A"], d0["lam"], d0["theta"],
+                                     h0=cg["h0"], z=z0, chunk=16)
+    y0, h1 = m3.scan_prefill_prologue(d0["x"], d0["B"], d0["C"], d0["dt"], d0["A"], d0["lam"], d0["theta"],
+                                      h0=cg["h0"], chunk=16)
+    torch.cuda.synchronize()
+    assert out0.numel() == 0 and y0.numel() == 0
+    assert torch.equal(h0, cg["h0"]) and torch.equal(h1, cg["h0"])
