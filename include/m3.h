@@ -230,9 +230,11 @@ typedef struct {
 /* m3_scan_prefill with the fused prologue applied to B, C, B_prev and theta
  * inside the kernel's load stage.  pro must not be NULL (M3_ERR_NULL).  The
  * bias tables take 2 x R x N x 4 bytes of LDS per workgroup beside the chunk's
- * tiles; a shape whose tiles leave too little room gets M3_ERR_SHAPE.  The
- * workspace is the one m3_prefill_workspace_bytes gives for the shape.
- * Everything else as m3_scan_prefill. */
+ * tiles; a shape whose tiles leave too little room gets M3_ERR_SHAPE, and so
+ * does a chunk of more than 128 (token, rank) rows for N <= 64 or 256 for
+ * N = 128 (the default chunks never are).  The workspace is the one
+ * m3_prefill_workspace_bytes gives for the shape.  Everything else as
+ * m3_scan_prefill. */
 m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,
                                    const void* x, const void* B, const void* C,
                                    const float* dt, const float* A, const float* lam,

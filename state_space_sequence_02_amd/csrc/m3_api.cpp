@@ -162,9 +162,15 @@ m3_status prefill_common(const m3_shape* s,
     if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
     if (h_out && in.p != h0 && overlaps(h_out, sbytes, in.p, in.n)) return M3_ERR_ALIAS;
   }
-  // the prologue's bias tables take LDS of their own
+  // the prologue's bias tables take LDS of their own; the prologue runs with
+  // one 16-row output tile per wave only (its variants with two or more
+  // spilled 40-96 bytes per lane to scratch, and one of them made a memory
+  // fault whose cause is not established)
   size_t lds = plan.lds;
   if (pro.on) {
+    const int waves = fused_threads(N) / 64;
+    const int tiles = (plan.Q * R + 31) / 32 * 2;
+    if ((tiles + waves - 1) / waves > 1) return M3_ERR_SHAPE;
     lds = fused_lds_bytes(plan.Q, R, N, P, (int)es, 1);
     if (lds > (size_t)kLdsBudget) return M3_ERR_SHAPE;
   }

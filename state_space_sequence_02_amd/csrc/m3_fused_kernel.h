@@ -1324,10 +1324,8 @@ hipError_t launch_rt(const FusedParams& p, size_t lds, hipStream_t s) {
     if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), true, false>(p, lds, s);
     return hipErrorInvalidValue;
   }
-  if (p.pro) {
+  if (p.pro) {   // (one output tile per wave only: the host rejects larger chunks)
     if (rt <= 1) return launch<T, N, P, R, 1, false, true>(p, lds, s);
-    if (rt <= 2 && kMaxRT >= 2) return launch<T, N, P, R, (kMaxRT >= 2 ? 2 : 1), false, true>(p, lds, s);
-    if (rt <= 4 && kMaxRT >= 4) return launch<T, N, P, R, (kMaxRT >= 4 ? 4 : 1), false, true>(p, lds, s);
     return hipErrorInvalidValue;
   }
   if (rt <= 1) return launch<T, N, P, R, 1, false, false>(p, lds, s);

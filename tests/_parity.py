@@ -36,14 +36,17 @@ def to64(t) -> np.ndarray:
 
 
 def check_blocks(got: np.ndarray, ref: np.ndarray, tol: float, block_axes, what: str,
-                 elem_axes=None):
+                 elem_axes=None, elem_scale=None):
     """Relative Frobenius error over each block (block_axes = axes reduced), then
     an elementwise bound ELEM_FACTOR * tol * (|ref| + scale).  The scale is the larger of the
     block's rms and, when elem_axes is given, the rms over elem_axes (one
     token's rank x column outputs for y): a token whose outputs are far larger
     than the block average (an incoming state that decays away) is judged at
     its own magnitude, and a token whose outputs nearly cancel (C_t . B_t ~ 0
-    after the state has decayed) at the block's."""
+    after the state has decayed) at the block's.  elem_scale, when given, is a
+    further per-element scale (same shape as ref): the gated readout passes the
+    rank sum of |gain| x the token's y rms, so a column the gate amplifies is
+    judged at the size its y error is carried to."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -59,10 +62,32 @@ def check_blocks(got: np.ndarray, ref: np.ndarray, tol: float, block_axes, what:
     scale = np.sqrt((ref ** 2).mean(axis=tuple(block_axes), keepdims=True))
     if elem_axes is not None:
         scale = np.maximum(scale, np.sqrt((ref ** 2).mean(axis=tuple(elem_axes), keepdims=True)))
+    if elem_scale is not None:
+        scale = np.maximum(scale, np.asarray(elem_scale, dtype=np.float64))
     bound = ELEM_FACTOR * tol * (np.abs(ref) + scale) + 1e-30
     ratio = np.abs(err) / bound
     assert ratio.max() <= 1.0, f"{what}: elementwise error {ratio.max():.2f}x the bound"
     return worst
+
+
+def gate_scale(y, z=None, w_y=None, w_z=None, block_axes=None) -> np.ndarray:
+    """Per-element scale of a gated readout out[.., h, p] = sum_r g[r, p] y[.., h, r, p]
+    (g = w_y silu(w_z z)): sum_r |g[r, p]| times the scale y itself is judged
+    at (the larger of the token's rms over its ranks and columns and, with
+    block_axes, the block's rms), so out's bound is y's carried through the
+    gains.  y [.., H, R, P] float64 (the reference outputs)."""
+    import oracle
+    y = np.asarray(y, dtype=np.float64)
+    H, R, P = y.shape[-3:]
+    wy = np.ones((H, R, P)) if w_y is None else np.asarray(w_y, dtype=np.float64)
+    g = np.abs(wy) * np.ones(y.shape)
+    if z is not None:
+        wz = np.ones((H, R, P)) if w_z is None else np.asarray(w_z, dtype=np.float64)
+        g = g * np.abs(oracle.silu(wz * np.asarray(z, dtype=np.float64)[..., None, :]))
+    ys = np.sqrt((y ** 2).mean(axis=(-2, -1), keepdims=True))
+    if block_axes is not None:
+        ys = np.maximum(ys, np.sqrt((y ** 2).mean(axis=tuple(block_axes), keepdims=True)))
+    return g.sum(axis=-2) * ys[..., 0, :]
 
 
 def dev_inputs(d: dict, device="cuda") -> dict:

@@ -178,6 +178,10 @@ def test_prologue_validation_codes(lib):
     assert prefill(ok, y=FAR[11] + 8) == 6       # y overlaps the B bias table
     assert prefill(ok, ws=None) == 4
     assert prefill(m3.make_shape(2, 128, 3, 64, 256, 4, 64, 1)) == 2      # N = 256: decode only
+    # more than one 16-row output tile per wave (chunk above the default): rejected
+    assert prefill(m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1)) == 2
+    assert prefill(m3.make_shape(2, 512, 3, 64, 64, 2, 128, 1)) == 2
+    assert prefill(m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1)) == 2
     dec = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
     assert decode(dec, p=None) == 1
     assert decode(dec, y=FAR[12]) == 6           # y aliases the C bias table

@@ -11,7 +11,7 @@ import oracle
 import state_space_sequence_02_amd as m3
 from state_space_sequence_02_amd import inputs
 
-from _parity import TOL, check_blocks, dev_inputs, note, oracle_inputs, to64
+from _parity import TOL, check_blocks, dev_inputs, gate_scale, note, oracle_inputs, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -68,9 +68,11 @@ def test_prefill_gated(case):
                                    w_z=None if wz is None else wz.cuda(), chunk=chunk)
     torch.cuda.synchronize()
     assert out.shape == (w.batch, w.seqlen, w.nheads, w.headdim)
-    ref, href = oracle.scan_gated(**oracle_inputs({**d, **c}), z=_np(z), w_y=_np(wy), w_z=_np(wz))
+    yref, href = oracle.scan(**oracle_inputs({**d, **c}))
+    ref = oracle.gated_readout(yref, _np(z), _np(wy), _np(wz))
     tol = TOL[w.dtype]
-    check_blocks(to64(out), ref, tol, (1, 3), "gated out")
+    check_blocks(to64(out), ref, tol, (1, 3), "gated out", elem_axes=(3,),
+                 elem_scale=gate_scale(yref, _np(z), _np(wy), _np(wz), block_axes=(1, 3, 4)))
     check_blocks(to64(h), href, tol, (2, 3), "h_out")
     # the state path is the ungated call's (equal up to rounding: with few
     # sequences a chunk may compose its predecessors' maps, an order of the
@@ -106,7 +108,8 @@ def test_decode_gated(shape, gate):
     yr, hr = oracle.decode_steps(h0, d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"])
     ref = oracle.gated_readout(yr, _np(z), _np(wy), _np(wz))
     tol = TOL[w.dtype]
-    check_blocks(to64(torch.stack(outs)), ref, tol, (3,), "decode gated out")
+    check_blocks(to64(torch.stack(outs)), ref, tol, (3,), "decode gated out",
+                 elem_scale=gate_scale(yr, _np(z), _np(wy), _np(wz)))
     check_blocks(to64(h), hr, tol, (2, 3), "decode h")
 
 
@@ -130,6 +133,8 @@ def test_gated_prefill_then_decode_continues():
                                  w_y=wy.cuda(), w_z=wz.cuda())
         outs.append(o[:, None])
     torch.cuda.synchronize()
-    ref, _ = oracle.scan_gated(**oracle_inputs(d), z=_np(z), w_y=_np(wy), w_z=_np(wz))
-    check_blocks(to64(torch.cat(outs, dim=1)), ref, TOL[w.dtype], (1, 3), "gated out")
+    yref, _ = oracle.scan(**oracle_inputs(d))
+    ref = oracle.gated_readout(yref, _np(z), _np(wy), _np(wz))
+    check_blocks(to64(torch.cat(outs, dim=1)), ref, TOL[w.dtype], (1, 3), "gated out", elem_axes=(3,),
+                 elem_scale=gate_scale(yref, _np(z), _np(wy), _np(wz), block_axes=(1, 3, 4)))
     assert np.isfinite(to64(h)).all()

@@ -5,6 +5,8 @@ on a wave) and for the decode step (fp32 state, and bf16 state with bf16
 inputs), against the float64 oracle.  Sizes are small: a prefill spans two
 whole chunks and a ragged third, with an incoming state and previous write.
 """
+import math
+
 import pytest
 import torch
 
@@ -12,7 +14,7 @@ import oracle
 import state_space_sequence_02_amd as m3
 from state_space_sequence_02_amd import inputs
 
-from _parity import TOL, check_blocks, dev_inputs, note, oracle_inputs, to64
+from _parity import TOL, check_blocks, dev_inputs, gate_scale, note, oracle_inputs, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +44,11 @@ NO_PREFILL = {("fp32", 128, 128, 8)}
 # of them (bf16 P=64 R=4) made a GPU memory fault whose cause was not found, so
 # the path was taken out of the library
 N256_SKIP = "N=256 prefill is not built (heavy scratch spills; one unexplained GPU memory fault)"
+# the prologue prefill with two or more output tiles per wave (chunks above the
+# default) spilled to scratch and one of its kernels (bf16 N=64 P=64 R=2) made a
+# GPU memory fault whose cause was not found: the host rejects those chunks
+PRO_RT_SKIP = ("prologue prefill with two or more output tiles per wave is switched off "
+               "(scratch spills; one unexplained GPU memory fault)")
 
 
 @pytest.mark.parametrize("chunk", ["default", "max"])
@@ -102,3 +109,64 @@ def test_decode_grid(dtype, state, N, P, R):
     tol = TOL[dtype]
     check_blocks(to64(torch.stack(ys)), yr, tol, (3, 4), "decode y")
     check_blocks(to64(h), hr, tol, (2, 3), "decode h")
+
+
+def _grid_case(dtype, N, P, R, chunk, seed):
+    """The grid's prefill case: (workload, inputs, carry, chunk) or None when
+    the prefill does not take the shape."""
+    if N == 256:
+        pytest.skip(N256_SKIP)
+    if (dtype, N, P, R) in NO_PREFILL:
+        pytest.skip("the prefill rejects this shape (LDS)")
+    request = 0 if chunk == "default" else 4096
+    q = m3.prefill_chunk_used(m3.make_shape(1, 1, 2, P, N, R, request, _code(dtype)))
+    L = 2 * q + q // 2 + 3
+    w = inputs.workload("mimo", batch=1, seqlen=L, nheads=2, headdim=P, dstate=N, rank=R, chunk=q, dtype=dtype)
+    d = inputs.make_prefill_inputs(w, seed=seed)
+    c = inputs.random_carry(w, seed=seed + 1)
+    return w, q, d, c
+
+
+@pytest.mark.parametrize("chunk", ["default", "max"])
+@pytest.mark.parametrize("dtype,N,P,R", GRID, ids=lambda v: str(v))
+def test_gated_grid(dtype, N, P, R, chunk):
+    w, q, d, c = _grid_case(dtype, N, P, R, chunk, 3000 + N + P + R)
+    g = torch.Generator().manual_seed(3100 + N + P + R)
+    z = torch.randn((w.batch, w.seqlen, w.nheads, P), generator=g).to(w.torch_dtype)
+    wy = torch.randn((w.nheads, R, P), generator=g)
+    wz = torch.rand((w.nheads, R, P), generator=g) + 0.5
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note(f"gated grid {dtype} N={N} P={P} R={R} chunk={q}")
+    out, h = m3.scan_prefill_gated(**{k: dg[k] for k in KEYS}, **cg, z=z.cuda(), w_y=wy.cuda(), w_z=wz.cuda(),
+                                   chunk=q)
+    torch.cuda.synchronize()
+    zn, wyn, wzn = z.double().numpy(), wy.double().numpy(), wz.double().numpy()
+    yref, href = oracle.scan(**oracle_inputs({**d, **c}))
+    ref = oracle.gated_readout(yref, zn, wyn, wzn)
+    check_blocks(to64(out), ref, TOL[dtype], (1, 3), "gated out", elem_axes=(3,),
+                 elem_scale=gate_scale(yref, zn, wyn, wzn, block_axes=(1, 3, 4)))
+    check_blocks(to64(h), href, TOL[dtype], (2, 3), "h_out")
+
+
+@pytest.mark.parametrize("chunk", ["default", "max"])
+@pytest.mark.parametrize("dtype,N,P,R", GRID, ids=lambda v: str(v))
+def test_prologue_grid(dtype, N, P, R, chunk):
+    w, q, d, c = _grid_case(dtype, N, P, R, chunk, 4000 + N + P + R)
+    waves = (1024 if N >= 128 else 512) // 64
+    if -(-((q * R + 31) // 32 * 2) // waves) > 1:
+        pytest.skip(PRO_RT_SKIP)
+    g = torch.Generator().manual_seed(4100 + N + P + R)
+    th = (torch.rand((w.batch, w.seqlen, w.nheads, N // 2), generator=g) * 2 - 1) * math.pi
+    bb = torch.randn((w.nheads, R, N), generator=g) * 0.5
+    bc = torch.randn((w.nheads, R, N), generator=g) * 0.5
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note(f"prologue grid {dtype} N={N} P={P} R={R} chunk={q}")
+    y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
+                                    chunk=q, eps=1e-5, bias_B=bb.cuda(), bias_C=bc.cuda())
+    torch.cuda.synchronize()
+    n = lambda t: t.double().numpy()
+    yr, hr = oracle.scan_prologue(n(d["x"]), n(d["B"]), n(d["C"]), n(d["dt"]), n(d["A"]), n(d["lam"]), n(th),
+                                  h0=n(c["h0"]), B_prev=n(c["B_prev"]), x_prev=n(c["x_prev"]),
+                                  eps=1e-5, bias_B=n(bb), bias_C=n(bc))
+    check_blocks(to64(y), yr, TOL[dtype], (1, 3, 4), "prologue y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL[dtype], (2, 3), "prologue h_out")

@@ -72,7 +72,9 @@ def test_decode_prologue(shape, biases):
 PREFILL = [
     # (workload, overrides, chunk, biases, carry)
     ("siso", dict(batch=2, seqlen=300, nheads=3), 64, True, True),
-    ("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),          # two tiles per wave
+    pytest.param(("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),
+                 marks=pytest.mark.skip(reason="prologue prefill with two or more output tiles per wave is "
+                                               "switched off (scratch spills; one unexplained GPU memory fault)")),
     ("siso", dict(batch=2, seqlen=200, nheads=2), 128, False, False),
     ("mimo", dict(batch=2, seqlen=130, nheads=2), 64, True, True),
     ("mimo", dict(batch=1, seqlen=97, nheads=2), 32, False, True),
