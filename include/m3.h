@@ -232,7 +232,8 @@ typedef struct {
  * bias tables take 2 x R x N x 4 bytes of LDS per workgroup beside the chunk's
  * tiles; a shape whose tiles leave too little room gets M3_ERR_SHAPE, and so
  * does a chunk of more than 128 (token, rank) rows for N <= 64 or 256 for
- * N = 128 (the default chunks never are).  The workspace is the one
+ * N = 128 (the default chunks never are).  fp32 inputs take N <= 64 only
+ * (M3_ERR_SHAPE at N = 128); bf16 inputs every N the prefill takes.  The workspace is the one
  * m3_prefill_workspace_bytes gives for the shape.  Everything else as
  * m3_scan_prefill. */
 m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,

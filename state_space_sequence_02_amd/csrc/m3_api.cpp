@@ -165,9 +165,12 @@ m3_status prefill_common(const m3_shape* s,
   // the prologue's bias tables take LDS of their own; the prologue runs with
   // one 16-row output tile per wave only (its variants with two or more
   // spilled 40-96 bytes per lane to scratch, and one of them made a memory
-  // fault whose cause is not established)
+  // fault whose cause is not established), and not for fp32 inputs at
+  // N = 128 (those kernels spill 60-324 bytes per lane; one of them made a
+  // memory fault whose cause is not established either)
   size_t lds = plan.lds;
   if (pro.on) {
+    if (s->dtype == M3_FP32 && N >= 128) return M3_ERR_SHAPE;
     const int waves = fused_threads(N) / 64;
     const int tiles = (plan.Q * R + 31) / 32 * 2;
     if ((tiles + waves - 1) / waves > 1) return M3_ERR_SHAPE;

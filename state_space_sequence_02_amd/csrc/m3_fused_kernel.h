@@ -90,7 +90,7 @@ __host__ __device__ constexpr int fused_rows_cap(int N) { return N <= 32 ? 512 :
 
 __host__ __device__ constexpr int round_up_i(int a, int b) { return (a + b - 1) / b * b; }
 
-__host__ __device__ inline size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
+__host__ __device__ constexpr size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 
 struct Lds {
   size_t row, rw, W, csH, B, X, misc, pb, total;
@@ -113,11 +113,11 @@ __host__ __device__ constexpr int x_stride(int P, int esize) {
 // B: B~ [QRp][N+8];  X: X [QRp][P+8] (permuted columns)
 // segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
 // pb: the prologue's bias tables [2][R][N] fp32 (B's, then C's), only when pro.
-__host__ __device__ inline Lds lds_layout(int Q, int R, int N, int P, int esize, int pro = 0) {
+__host__ __device__ constexpr Lds lds_layout(int Q, int R, int N, int P, int esize, int pro = 0) {
   const int QRp = round_up_i(Q * R, 32);
   const int kWaves = fused_threads(N) / 64;
   const size_t scan = sizeof(float) * kWaves + sizeof(float4) * (size_t)kWaves * (N / 8);
-  Lds o;
+  Lds o{};
   o.row = 0;
   o.rw = o.row + sizeof(float4) * QRp;
   o.W = o.rw + sizeof(float) * QRp;
@@ -338,16 +338,22 @@ __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
 
 // RT: output row tiles per wave (the chunk has at most RT * 16 * kWaves rows);
 // register arrays are sized by it.
-// Waves per SIMD the register allocation must allow: two 512-thread
-// workgroups per CU (128 VGPRs) for the instantiations that come close to it,
-// and a 1024-thread workgroup needs 4 anyway.
-template <int N, int RT>
-constexpr int prefill_waves_per_simd() { return (fused_threads(N) == 1024 || (N <= 64 && RT <= 2)) ? 4 : 2; }
+// Waves per SIMD the register allocation must allow: a 1024-thread workgroup
+// needs 4 (128 VGPRs); a 512-thread one asks for 4 too, so two workgroups share
+// a CU, unless at the largest chunk it takes two would not fit the CU's LDS
+// anyway -- then 2 (256 VGPRs), which keeps those variants free of spills.
+template <typename T, int N, int P, int R, int RT, bool PRO>
+constexpr int prefill_waves_per_simd() {
+  if (fused_threads(N) == 1024) return 4;
+  if (N > 64 || RT > 2) return 2;
+  constexpr int kQmax = RT * 16 * (fused_threads(N) / 64) / R;
+  return 2 * lds_layout(kQmax, R, N, P, (int)sizeof(T), PRO ? 1 : 0).total > (size_t)kLdsBudget ? 2 : 4;
+}
 
 // G: the gated readout (out [b,L,H,P]) replaces the y store.  PRO: the fused
 // prologue (B, C, B_prev column RMS norm + biases; angle = dt x raw angle).
 template <typename T, int N, int P, int R, int RT, bool G, bool PRO>
-__global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<N, RT>())) void prefill_kernel(FusedParams p) {
+__global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, R, RT, PRO>())) void prefill_kernel(FusedParams p) {
   constexpr int kThreads = fused_threads(N);
   constexpr int kWaves = kThreads / 64;
   constexpr int NH = N / 2;

@@ -182,6 +182,9 @@ def test_prologue_validation_codes(lib):
     assert prefill(m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1)) == 2
     assert prefill(m3.make_shape(2, 512, 3, 64, 64, 2, 128, 1)) == 2
     assert prefill(m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1)) == 2
+    # fp32 inputs at N = 128: rejected
+    assert prefill(m3.make_shape(2, 128, 3, 32, 128, 1, 0, m3.M3_FP32)) == 2
+    assert prefill(m3.make_shape(2, 128, 3, 64, 128, 4, 0, m3.M3_FP32)) == 2
     dec = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
     assert decode(dec, p=None) == 1
     assert decode(dec, y=FAR[12]) == 6           # y aliases the C bias table

@@ -49,6 +49,11 @@ N256_SKIP = "N=256 prefill is not built (heavy scratch spills; one unexplained G
 # GPU memory fault whose cause was not found: the host rejects those chunks
 PRO_RT_SKIP = ("prologue prefill with two or more output tiles per wave is switched off "
                "(scratch spills; one unexplained GPU memory fault)")
+# the fp32 prologue prefill at N = 128 spilled 60-324 bytes per lane and one of
+# its kernels (P=32 R=1) made a GPU memory fault whose cause was not found: the
+# host rejects fp32 inputs at that state size
+PRO_F32_N128_SKIP = ("fp32 prologue prefill at N=128 is switched off "
+                     "(scratch spills; one unexplained GPU memory fault)")
 
 
 @pytest.mark.parametrize("chunk", ["default", "max"])
@@ -152,6 +157,8 @@ def test_gated_grid(dtype, N, P, R, chunk):
 @pytest.mark.parametrize("dtype,N,P,R", GRID, ids=lambda v: str(v))
 def test_prologue_grid(dtype, N, P, R, chunk):
     w, q, d, c = _grid_case(dtype, N, P, R, chunk, 4000 + N + P + R)
+    if dtype == "fp32" and N == 128:
+        pytest.skip(PRO_F32_N128_SKIP)
     waves = (1024 if N >= 128 else 512) // 64
     if -(-((q * R + 31) // 32 * 2) // waves) > 1:
         pytest.skip(PRO_RT_SKIP)
