@@ -332,6 +332,13 @@ __device__ __forceinline__ void store_row(T* d, const float (&v)[TPt]) {
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 __device__ __forceinline__ float4 sub4(float4 a, float4 b) { return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w); }
+// v of the lane kRor places before this one, cyclically, within its row of
+// 16 lanes (DPP row_ror; every lane of the row must be active).
+template <int kRor>
+__device__ __forceinline__ float dpp_row_ror(float v) {
+  static_assert(kRor >= 1 && kRor <= 15, "row_ror takes 1..15");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + kRor, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float4 shfl_up4(float4 v, int off) {
   return make_float4(__shfl_up(v.x, off), __shfl_up(v.y, off), __shfl_up(v.z, off), __shfl_up(v.w, off));
 }
@@ -649,6 +656,15 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
   }
 
   // ---- B: stage B~ = R(-Phi_s) B_s and X (permuted columns) ----
+  // PRO: the B items of one thread (tid + multiples of kThreads) all have the
+  // same rank and 8-column group, so its 8 bias values are read once
+  static_assert(kThreads % (N / 8) == 0 && (kThreads / (N / 8)) % R == 0, "B item -> (rank, columns) per thread");
+  float bbr[8];
+  if constexpr (PRO) {
+    const float* bb = s_pb + ((tid / (N / 8)) & (R - 1)) * N + (tid % (N / 8)) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bbr[e] = bb[e];
+  }
   for (int base = tid; base < ntot; base += kThreads * kBatch) {
     if (base != tid)
       batch_loads(buf_rsrc(Bg, (uint32_t)(nt - 1) * rsB + R * N * esz),
@@ -663,8 +679,15 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        if constexpr (N / 8 == 16) {   // a row is one 16-lane DPP row: rotate-and-add
+          ss += dpp_row_ror<8>(ss);
+          ss += dpp_row_ror<4>(ss);
+          ss += dpp_row_ror<2>(ss);
+          ss += dpp_row_ror<1>(ss);
+        } else {
 #pragma unroll
-        for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off);
+          for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off);
+        }
         pscale = rsqrtf(ss / (float)N + p.eps);
       }
       if (i < nbi) {
@@ -673,9 +696,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
         raw_unpack(raw[u], v);
         if constexpr (PRO) {
           if (row < rows) {
-            const float* bb = s_pb + (row & (R - 1)) * N + ng * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = v[e] * pscale + bb[e];
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * pscale + bbr[e];
           }
         }
         if (row < rows) rotate_neg(v, s_cs + (row >> LOGR) * CSS + ng, NG);
