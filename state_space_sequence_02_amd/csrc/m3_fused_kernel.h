@@ -126,7 +126,7 @@ __host__ __device__ constexpr Lds lds_layout(int Q, int R, int N, int P, int esi
   o.X = o.B + round_up_i((int)max_sz((size_t)esize * QRp * (N + 8), scan), 16);
   o.misc = o.X + (size_t)esize * QRp * x_stride(P, esize);
   o.pb = o.misc + 32;
-  o.total = o.pb + (pro ? sizeof(float) * 2 * (size_t)R * N : 0);
+  o.total = o.pb + (pro ? sizeof(float) * (size_t)R * (2 * N + 4) : 0);   // B's [R][N], C's [R][N + 4]
   o.segl = o.B;
   o.sega = o.B + sizeof(float) * kWaves;
   return o;
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
     constexpr int kPb = R * N / 4;
     if (tid < kPb) {
       *reinterpret_cast<float4*>(s_pb + 4 * tid) = pbv0;
-      *reinterpret_cast<float4*>(s_pb + R * N + 4 * tid) = pbv1;
+      *reinterpret_cast<float4*>(s_pb + R * N + (4 * tid / N) * (N + 4) + 4 * tid % N) = pbv1;
     }
   }
   const float lmnv = (t0 + tid + 1 < p.L && tid < nt) ? lmnv_raw : 1.f;   // (only multiplies dnv = 0 otherwise)
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
       raw_unpack(craw[k][kn], v);
       if constexpr (PRO) {
         if (n0 < N && row_a < rows) {
-          const float* bc = s_pb + R * N + (row_a & (R - 1)) * N + n0;
+          const float* bc = s_pb + R * N + (row_a & (R - 1)) * (N + 4) + n0;   // (rows 4 banks apart)
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = v[e] * cscale + bc[e];
         }
