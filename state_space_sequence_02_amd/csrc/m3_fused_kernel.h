@@ -1270,7 +1270,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
             if (wyh) v *= gate_lds ? swy[r * P + pn] : wyh[r * P + pn];
             if (Zg) {
               const float gz = (wzh ? (gate_lds ? swz[r * P + pn] : wzh[r * P + pn]) : 1.f) * zv[pn];
-              v *= gz / (1.f + __expf(-gz));
+              v *= gz * __builtin_amdgcn_rcpf(1.f + __expf(-gz));   // silu (1-ulp reciprocal)
             }
             o[pn] += v;
           }
