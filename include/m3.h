@@ -229,7 +229,7 @@ typedef struct {
 
 /* m3_scan_prefill with the fused prologue applied to B, C, B_prev and theta
  * inside the kernel's load stage.  pro must not be NULL (M3_ERR_NULL).  The
- * bias tables take 2 x R x N x 4 bytes of LDS per workgroup beside the chunk's
+ * bias tables take R x (2N + 4) x 4 bytes of LDS per workgroup beside the chunk's
  * tiles; a shape whose tiles leave too little room gets M3_ERR_SHAPE, and so
  * does a chunk of more than 128 (token, rank) rows for N <= 64 or 256 for
  * N = 128 (the default chunks never are).  fp32 inputs take N <= 64 only
