@@ -2,15 +2,20 @@
 """Throughput of the MI355X Mamba-3 recurrence: prefill tokens/s/layer and decode
 state-updates/s, with roofline fractions and the CPU oracle timed alongside.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload siso|mimo|long|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|siso|mimo|decode]
 
 One "step" is one call of the hot path over one batch of synthetic input: a
 whole-layer prefill (all heads) for the prefill workloads, or one single-token
 decode step over all (sequence, head) pairs for the decode workload.  Inputs are
 generated on the device from a fixed seed and are resident in HBM before timing.
-Prints ONE JSON line.  The headline `value` is the requested workload (default:
-SISO prefill at the 1.5B-layer shape); the MIMO prefill and the MIMO decode are
-measured in the same run and reported under "secondary".
+Prints ONE JSON line.  The headline `value` is the requested workload, by
+default the largest one-GPU configuration: the long-context MIMO prefill
+(b=1, L=65536, 32 heads, P=64, N=128, R=4).  Its K timed steps are repeated
+three times and `value` / `ms_per_step` are the mean of the three.  The other
+configurations (SISO and MIMO prefill, MIMO decode) and the pages' other decode
+settings are measured in the same run under "secondary", and the float64 CPU
+oracle is timed on a bounded sample of every configuration ("cpu_baseline" for
+the headline, "cpu_baselines" for all).
 """
 from __future__ import annotations
 
@@ -115,11 +120,12 @@ class StepTimer:
 PREWARM_S = 0.3
 
 
-def _timed(step, steps, warmup):
-    """Times `steps` back-to-back steps (the throughput), then the same number
-    again with an event right after each launch (each launch's own duration,
-    which is what the kernel-trace profile reports; the extra events lengthen
-    the steps of that second loop, so it gives no throughput).
+def _timed(step, steps, warmup, reps=1):
+    """Times `steps` back-to-back steps (the throughput) `reps` times, then the
+    same number again with an event right after each launch (each launch's own
+    duration, which is what the kernel-trace profile reports; the extra events
+    lengthen the steps of that loop, so it gives no throughput).  `ms` is the
+    mean step over the repetitions; `ms_reps` lists each repetition's mean.
 
     Before the `warmup` untimed steps the step runs for PREWARM_S seconds of
     wall time: the GPU takes tens of milliseconds of steady work to reach its
@@ -134,24 +140,25 @@ def _timed(step, steps, warmup):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    out = None
-    for bracket in (False, True):
+    runs = []
+    for bracket in [False] * reps + [True]:
         t = StepTimer(steps, bracket)
         for i in range(steps):
             t.mark(i)
             step(i)
             t.mark_after(i)
         t.mark(steps)
-        r = t.result()
+        runs.append(t.result())
         torch.cuda.synchronize()
-        if out is None:
-            out = r
-        else:
-            out.update(ms_launch=r["ms_launch"], ms_launch_median=r["ms_launch_median"])
+    timed, br = runs[:-1], runs[-1]
+    out = dict(ms=sum(r["ms"] for r in timed) / len(timed), ms_reps=[r["ms"] for r in timed],
+               ms_median=sorted(r["ms_median"] for r in timed)[len(timed) // 2],
+               ms_min=min(r["ms_min"] for r in timed),
+               ms_launch=br["ms_launch"], ms_launch_median=br["ms_launch_median"])
     return out
 
 
-def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None):
+def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None, reps=1):
     """One step = one m3_scan_prefill over the whole layer (all heads), with the
     final state exported; `nsets` input sets alternate so a step cannot be served
     from the last-level cache left warm by the previous one.  gate="fused": one
@@ -180,7 +187,9 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None):
     dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
     shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, chunk, dcode)
     ws = torch.zeros(m3.prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-    q_used = m3.prefill_chunk_used(shape)
+    q_used = m3.prefill_chunk_used(shape, "gated" if gate == "fused" else "prologue" if prologue == "fused" else "plain")
+    if q_used == 0:
+        raise m3.M3Error(2, f"the library takes no chunk {chunk} for {w.name}")
     ys = [torch.empty_like(s["x"]) for s in sets]
     hs = [torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
           for _ in sets]
@@ -207,7 +216,9 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None):
         if gate == "torch":
             outs[i % nsets].copy_(gated_readout_torch(ys[i % nsets], d["z"], wy, wz))
 
-    r = _timed(step, steps, warmup)
+    r = _timed(step, steps, warmup, reps)
+    if m3.prefill_status(ws) != 0:
+        raise RuntimeError("a prefill look-back wait gave up during the benchmark")
     ms = r["ms"]
     tok = w.batch * w.seqlen
     bpt = gated_bytes_per_token_head(w) if gate else prefill_bytes_per_token_head(w)
@@ -220,7 +231,7 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None):
                 gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
 
-def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=False, prologue=False):
+def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=False, prologue=False, reps=1):
     """One step = one m3_decode_step over all (sequence, head) pairs; >= 3 state
     buffers (384 MiB at the 128-sequence shape) rotate so a step cannot be served
     from the 256 MB last-level cache left warm by the previous step.  gated:
@@ -260,7 +271,7 @@ def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=Fa
         m3.decode_step(hs[i % nstate], d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"],
                        d["lam"][s], d["theta"][s], y=y, **kw)
 
-    r = _timed(step, steps, warmup)
+    r = _timed(step, steps, warmup, reps)
     ms = r["ms"]
     upd = w.batch * w.nheads
     nbytes = upd * decode_bytes_per_update(w, 2 if state_dtype == torch.bfloat16 else 4)
@@ -298,12 +309,23 @@ def measured_traffic(name):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, target_s=12.0):
-    """The float64 CPU oracle on a bounded sample of the same workload."""
+_ORACLE_THREADS = None
+
+
+def cpu_baseline(w, target_s=10.0):
+    """The float64 CPU oracle, as it stands, on a bounded sample of the same
+    workload (about target_s seconds on all host cores), scaled to the metric's
+    unit.  Prefill: one sequence, min(cores, H) heads, over a prefix of the
+    sequence long enough to take about target_s (the oracle's time is linear in
+    the tokens and the heads), drawn with the workload's distributions; decode:
+    a subset of the sequences, all heads, 16 successive steps."""
     import numpy as np
     import oracle
-    nthreads = oracle.max_threads()
-    if w.steps:   # decode: a subset of (sequence, head) pairs over all steps
+    global _ORACLE_THREADS
+    if _ORACLE_THREADS is None:   # (a run with an explicit count changes the default)
+        _ORACLE_THREADS = oracle.max_threads()
+    nthreads = _ORACLE_THREADS
+    if w.steps:   # decode: a subset of (sequence, head) pairs over 16 steps
         d = inputs.make_decode_inputs(w, seed=0, device="cpu", steps=16)
         def run(npairs):
             seqs = list(range(min(npairs, w.batch)))
@@ -316,28 +338,58 @@ def cpu_baseline(w, target_s=12.0):
         n = max(1, min(w.batch, int(target_s / max(dt1, 1e-3))))
         el, upd = run(n)
         return dict(value=upd / el, unit="state-updates/s", cores=nthreads, kind="oracle",
-                    sample=f"{n} sequences x {w.nheads} heads x 16 steps of the decode workload")
-    d = inputs.make_prefill_inputs(w, seed=0, device="cpu", batch=1)
-    def run(nheads, threads=nthreads):
+                    sample=f"{n} sequences x {w.nheads} heads x 16 steps of the {w.name} workload")
+    nh = min(nthreads, w.nheads)
+
+    def run(nheads, L, threads=nthreads):
+        d = inputs.make_prefill_inputs(w, seed=0, device="cpu", batch=1, seqlen=L)
         heads = list(range(nheads))
-        o = {k: (None if v is None else (v[heads] if k == "A" else v[:, :, heads]))
+        o = {k: (None if v is None else (v[heads] if k == "A" else v[:, :, heads]).double().numpy())
              for k, v in d.items()}
         t0 = time.perf_counter()
         oracle.scan(**o, nthreads=threads)
         return time.perf_counter() - t0
-    nh0 = min(nthreads, w.nheads)
-    t1 = run(nh0)
-    nh = max(nh0, min(w.nheads, int(nh0 * target_s / max(t1, 1e-3))))
-    el = run(nh)
-    tokens_per_s = (w.seqlen * nh / w.nheads) / el
-    el1 = run(1, threads=1)   # one head on one core
+    Lc = min(w.seqlen, 256)
+    tc = run(nh, Lc)
+    Ls = int(min(w.seqlen, max(Lc, Lc * target_s / max(tc, 1e-3))))
+    el = run(nh, Ls)
+    tokens_per_s = (Ls * nh / w.nheads) / el
+    L1 = min(w.seqlen, max(64, Ls // 8))
+    el1 = run(1, L1, threads=1)   # one head on one core
     return dict(value=tokens_per_s, unit="tokens/s/layer", cores=nthreads, kind="oracle",
-                sample=f"1 sequence x {nh} of {w.nheads} heads x L={w.seqlen}, scaled to a full layer",
-                value_1thread=(w.seqlen / w.nheads) / el1)
+                sample=f"1 sequence x {nh} of {w.nheads} heads x the first {Ls} of {w.seqlen} tokens, "
+                       "scaled to a full layer",
+                value_1thread=(L1 / w.nheads) / el1)
 
 
 PREFILL_SOURCES = ["m3_fused_kernel.h", "m3_device.h", "m3_internal.h"]
 DECODE_SOURCES = ["m3_decode.hip", "m3_device.h", "m3_internal.h"]
+
+
+def prefill_chunk_for(w, requested):
+    """The chunk a prefill workload runs at: the requested one when the library
+    takes it, else the largest it takes below it (the long workload's 128-token
+    chunk is 512 (token, rank) rows, which do not fit one compute unit)."""
+    dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, requested, dcode)
+    if requested == 0 or m3.prefill_chunk_used(shape) == requested:
+        return requested
+    return min(requested, m3.prefill_max_chunk(shape))
+
+
+def prefill_line(w, rr):
+    return dict(tokens_per_s_layer=rr["tokens_per_s"], us=round(rr["ms"] * 1e3, 1),
+                us_median=round(rr["ms_median"] * 1e3, 1), chunk=rr["chunk"],
+                us_per_launch=round(rr["ms_launch"] * 1e3, 1),
+                hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
+                mfma_frac=round(rr["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4))
+
+
+def decode_line(wl, rr, state="fp32"):
+    return dict(state_updates_per_s=rr["updates_per_s"], us_per_step=round(rr["ms"] * 1e3, 1),
+                us_median=round(rr["ms_median"] * 1e3, 1), us_per_launch=round(rr["ms_launch"] * 1e3, 1),
+                hbm_gbs=round(rr["gbs_launch"], 1), hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
+                state=state, dstate=wl.dstate, rank=wl.rank)
 
 
 def main():
@@ -345,8 +397,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="siso", choices=["siso", "mimo", "long", "decode", "tiny"])
-    ap.add_argument("--chunk", type=int, default=0, help="prefill tokens per chunk (0: library default)")
+    ap.add_argument("--reps", type=int, default=3, help="repetitions of the timed steps (mean reported)")
+    ap.add_argument("--workload", default="long", choices=["long", "siso", "mimo", "decode", "tiny"])
+    ap.add_argument("--chunk", type=int, default=-1,
+                    help="prefill tokens per chunk (-1: the configuration's; 0: library default)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -363,7 +417,7 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     if w.steps:
-        r = bench_decode(w, args.steps * 10, args.warmup * 10)
+        r = bench_decode(w, args.steps * 10, args.warmup * 10, reps=args.reps)
         value, unit, ms = r["updates_per_s"], "state-updates/s", r["ms"]
         traffic = measured_traffic("decode_kernel_decode")
         roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -375,7 +429,9 @@ def main():
                       state_buffers=3)
         steps_done = args.steps * 10
     else:
-        r = bench_prefill(w, args.steps, args.warmup, chunk=args.chunk)
+        requested = w.chunk if args.chunk < 0 else args.chunk
+        chunk = prefill_chunk_for(w, requested)
+        r = bench_prefill(w, args.steps, args.warmup, chunk=chunk, reps=args.reps)
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
         traffic = measured_traffic(f"prefill_kernel_{w.name}_q{r['chunk']}")
         roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -384,47 +440,43 @@ def main():
                     algorithmic_bytes_per_launch=r["bytes"],
                     us_per_launch=round(r["ms_launch"] * 1e3, 2),
                     mfma_tflops=round(r["tflops_launch"], 2),
-                    mfma_frac=round(r["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4))
+                    mfma_frac=round(r["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4),
+                    algorithmic_flops_per_launch=r["flops"])
         config = dict(workload=f"{w.name} prefill: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
                                f"N={w.dstate}, R={w.rank}, {w.dtype} in, fp32 state",
                       batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, dstate=w.dstate,
-                      headdim=w.headdim, rank=w.rank, chunk=r["chunk"])
+                      headdim=w.headdim, rank=w.rank, chunk=r["chunk"], chunk_requested=requested)
+        if requested and r["chunk"] != requested:
+            config["chunk_note"] = (f"the configuration's {requested}-token chunk is {requested * w.rank} "
+                                    f"(token, rank) rows, which do not fit one compute unit; the largest "
+                                    f"chunk the library takes is used (the result does not depend on it)")
         steps_done = args.steps
     out = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=steps_done, warmup=args.warmup,
-               ms_per_step=ms, ms_median=r["ms_median"], ms_min=r["ms_min"],
+               ms_per_step=ms, ms_reps=r["ms_reps"], reps=args.reps, ms_median=r["ms_median"], ms_min=r["ms_min"],
                higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16" if w.dtype == "bf16" else "f32", data="synthetic (seeded, on device)",
                config=config, roofline=roof)
-    if not args.no_secondary and args.workload == "siso":
+    if not args.no_secondary:
         sec = {}
-        def pre(name, chunk, steps):
+        for name, q in (("siso", 64), ("siso", 0), ("mimo", 64), ("long", 128)):
+            if name == args.workload and (q == 0) == (args.chunk == 0):
+                continue
             wl = inputs.WORKLOADS[name]
-            rr = bench_prefill(wl, steps, args.warmup if name == "siso" else max(2, args.warmup // 5), chunk=chunk)
-            return dict(tokens_per_s_layer=rr["tokens_per_s"], us=round(rr["ms"] * 1e3, 1),
-                        us_median=round(rr["ms_median"] * 1e3, 1), chunk=rr["chunk"],
-                        us_per_launch=round(rr["ms_launch"] * 1e3, 1),
-                        hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
-                        mfma_frac=round(rr["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4))
-        sec["siso_prefill_chunk64"] = pre("siso", 64, args.steps)
-        sec["mimo_prefill"] = pre("mimo", 0, args.steps)
-        sec["long_prefill"] = pre("long", 0, max(3, args.steps // 4))
+            steps = args.steps if name != "long" else max(3, args.steps // 4)
+            key = f"{name}_prefill" + ("_default_chunk" if q == 0 else "")
+            sec[key] = prefill_line(wl, bench_prefill(wl, steps, max(2, args.warmup // 5),
+                                                      chunk=prefill_chunk_for(wl, q)))
         wd = inputs.WORKLOADS["decode"]
-        rd = bench_decode(wd, 200, 30)
-        sec["mimo_decode"] = dict(state_updates_per_s=rd["updates_per_s"], us_per_step=round(rd["ms"] * 1e3, 1),
-                                  us_median=round(rd["ms_median"] * 1e3, 1),
-                                  us_per_launch=round(rd["ms_launch"] * 1e3, 1),
-                                  hbm_gbs=round(rd["gbs_launch"], 1), hbm_frac=round(rd["gbs_launch"] / HBM_PEAK_GBS, 4),
-                                  table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
+        if args.workload != "decode":
+            rd = bench_decode(wd, 200, 30)
+            sec["mimo_decode"] = dict(decode_line(wd, rd),
+                                      table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
         # the paper page's Table 6 decode settings: SISO and MIMO, state size 64
         # or 128, fp32 or bf16 state (128 sequences x 32 heads, P=64)
         def dec(name, state_dtype=torch.float32, **kw):
             wl = inputs.workload("decode", **kw)
             rr = bench_decode(wl, 200, 30, state_dtype=state_dtype)
-            sec[name] = dict(state_updates_per_s=rr["updates_per_s"], us_per_step=round(rr["ms"] * 1e3, 1),
-                             us_per_launch=round(rr["ms_launch"] * 1e3, 1),
-                             hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
-                             state="bf16" if state_dtype == torch.bfloat16 else "fp32",
-                             dstate=wl.dstate, rank=wl.rank)
+            sec[name] = decode_line(wl, rr, "bf16" if state_dtype == torch.bfloat16 else "fp32")
         dec("mimo_decode_bf16_state", torch.bfloat16)
         dec("mimo_decode_n64", dstate=64)
         dec("siso_decode_n128", rank=1)
@@ -432,36 +484,33 @@ def main():
         # the gated readout (rank contraction + rank-expanded SiLU gate) fused
         # into the kernels, and the prefill's unfused alternative
         wm = inputs.WORKLOADS["mimo"]
-        rf = bench_prefill(wm, args.steps, max(2, args.warmup // 5), gate="fused")
-        rt = bench_prefill(wm, args.steps, max(2, args.warmup // 5), gate="torch")
-        sec["mimo_prefill_gated"] = dict(tokens_per_s_layer=rf["tokens_per_s"], us=round(rf["ms"] * 1e3, 1),
-                                         us_per_launch=round(rf["ms_launch"] * 1e3, 1),
-                                         hbm_frac=round(rf["gbs_launch"] / HBM_PEAK_GBS, 4),
-                                         us_unfused_torch_readout=round(rt["ms"] * 1e3, 1))
+        rf = bench_prefill(wm, args.steps, max(2, args.warmup // 5), chunk=64, gate="fused")
+        rt = bench_prefill(wm, args.steps, max(2, args.warmup // 5), chunk=64, gate="torch")
+        sec["mimo_prefill_gated"] = dict(prefill_line(wm, rf), us_unfused_torch_readout=round(rt["ms"] * 1e3, 1))
         rw = bench_decode(wd, 200, 30, nstate=1)
         sec["mimo_decode_warm"] = dict(us_per_launch=round(rw["ms_launch"] * 1e3, 1),
                                        state_updates_per_s=rw["updates_per_s"],
                                        note="one state buffer reused every step, so the 128 MiB state "
                                             "could be served from the 256 MB last-level cache")
         rg = bench_decode(wd, 200, 30, gated=True)
-        sec["mimo_decode_gated"] = dict(state_updates_per_s=rg["updates_per_s"], us_per_step=round(rg["ms"] * 1e3, 1),
-                                        us_per_launch=round(rg["ms_launch"] * 1e3, 1),
-                                        hbm_frac=round(rg["gbs_launch"] / HBM_PEAK_GBS, 4))
+        sec["mimo_decode_gated"] = decode_line(wd, rg)
         # the fused prologue (BCNorm + B/C biases + angle = dt x raw angle), and
-        # the prefill's unfused alternative (the prologue in torch ops first)
-        pf = bench_prefill(wm, args.steps, max(2, args.warmup // 5), prologue="fused")
-        pt = bench_prefill(wm, args.steps, max(2, args.warmup // 5), prologue="torch")
-        sec["mimo_prefill_prologue"] = dict(tokens_per_s_layer=pf["tokens_per_s"], us=round(pf["ms"] * 1e3, 1),
-                                            us_per_launch=round(pf["ms_launch"] * 1e3, 1),
-                                            hbm_frac=round(pf["gbs_launch"] / HBM_PEAK_GBS, 4),
-                                            us_unfused_torch_prologue=round(pt["ms"] * 1e3, 1))
+        # the prefill's unfused alternative (the prologue in torch ops first);
+        # on the SISO workload: the library refuses the N = 128 prologue prefill
+        # (its kernel variants keep a few values in scratch memory)
+        ws_ = inputs.WORKLOADS["siso"]
+        pf = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="fused")
+        pt = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="torch")
+        sec["siso_prefill_prologue"] = dict(prefill_line(ws_, pf), us_unfused_torch_prologue=round(pt["ms"] * 1e3, 1))
         rp = bench_decode(wd, 200, 30, prologue=True)
-        sec["mimo_decode_prologue"] = dict(state_updates_per_s=rp["updates_per_s"], us_per_step=round(rp["ms"] * 1e3, 1),
-                                           us_per_launch=round(rp["ms_launch"] * 1e3, 1),
-                                           hbm_frac=round(rp["gbs_launch"] / HBM_PEAK_GBS, 4))
+        sec["mimo_decode_prologue"] = decode_line(wd, rp)
         out["secondary"] = sec
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        base = {}
+        for name in ("tiny", "siso", "mimo", "decode", "long"):
+            base[name] = cpu_baseline(inputs.WORKLOADS[name], target_s=1.0 if name == "tiny" else 10.0)
+        out["cpu_baseline"] = base[args.workload]
+        out["cpu_baselines"] = base
     print(json.dumps(out), flush=True)
 
 

@@ -49,7 +49,8 @@ typedef enum {
     M3_ERR_DTYPE = 3,       /* unknown dtype code */
     M3_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than m3_prefill_workspace_bytes */
     M3_ERR_DEVICE = 5,      /* a HIP call or kernel launch failed */
-    M3_ERR_ALIAS = 6        /* an output aliases an input it must not alias */
+    M3_ERR_ALIAS = 6,       /* an output aliases an input it must not alias */
+    M3_ERR_TIMEOUT = 7      /* (m3_prefill_status) a prefill's look-back wait gave up */
 } m3_status;
 
 /* Element type of x, B, C, B_prev, x_prev and y.  dt, A, lam, theta and the state
@@ -73,25 +74,65 @@ typedef struct {
     int32_t dtype;
 } m3_shape;
 
-/* Bytes of device workspace m3_scan_prefill needs for this shape (0 on an
- * invalid or unsupported shape, including one of more than 2^26 - 1 chunks).
- * The buffer holds a control word (ticket count and call epoch), per-chunk
+/* Bytes of device workspace m3_scan_prefill, m3_scan_prefill_gated and
+ * m3_scan_prefill_prologue need for this shape (the largest of the three; 0 on an
+ * invalid or unsupported shape, including one of more than 2^26 - 1
+ * chunks).  The buffer holds a control word (ticket count and call epoch) at
+ * offset 0, a sticky error word at offset 8 (see m3_prefill_status), per-chunk
  * flags and per-chunk states.  Zero-fill it once before its first use (e.g.
  * hipMemset); every call leaves it ready for the next one, whatever shape that
  * has, so it may be reused across calls on the same stream with nothing done in
  * between.  Calls that may run at the same time (other streams) need workspaces
- * of their own.  A workspace that was not zero-filled before its first use
- * gives wrong results (never an access outside the buffers) until it is. */
+ * of their own.  A workspace that was not zero-filled before its first use is
+ * detected when its control word is out of range (the call then computes
+ * nothing and m3_prefill_status reports M3_ERR_WORKSPACE); if garbage happens
+ * to look valid, the look-back waits give up and m3_prefill_status reports
+ * M3_ERR_TIMEOUT.  No access ever leaves the buffers. */
 size_t m3_prefill_workspace_bytes(const m3_shape* s);
 
-/* Tokens per chunk m3_scan_prefill will actually use for this shape (the
- * requested value rounded to a supported power of two and capped so that one
- * chunk's tiles fit on a compute unit), or 0 on an invalid shape.  The prefill
- * takes N = 16..128 (N = 256 is decode-only) and every P and R with them
- * except fp32 N=128 P=128 R=8, whose tiles do not fit a compute unit's LDS even
- * at 16 tokens per chunk; those get 0 here and M3_ERR_SHAPE from
- * m3_scan_prefill. */
+/* Tokens per chunk m3_scan_prefill will use for this shape, or 0 when it
+ * takes none (M3_ERR_SHAPE from m3_scan_prefill).  A requested chunk (s->chunk
+ * > 0) is used exactly as given: it must be a power of two in [16, 256] whose
+ * (token, rank) rows, angles and LDS tiles fit one compute unit and whose
+ * kernel variant uses no scratch memory, otherwise the shape is refused
+ * (m3_prefill_max_chunk gives the largest that is taken).  With s->chunk = 0
+ * the library picks 128 (token, rank) rows for N <= 64 and 256 above, halved
+ * until taken.  The prefill takes N = 16..128 (N = 256 is decode-only).  The
+ * library never launches a kernel variant that the build's compiler report
+ * gives any scratch (private memory) per lane: every GPU memory fault and the
+ * one wrong result met in this kernel's development came from such variants,
+ * and their cause was not established.  Those shapes (fp32 at N = 128, bf16 at
+ * N = 128 with P = 128, fp32 N <= 32 P = 128 at chunks of four output tiles
+ * per wave, some prologue variants) get 0 here and M3_ERR_SHAPE from the call. */
 int32_t m3_prefill_chunk_used(const m3_shape* s);
+
+/* The largest chunk (tokens) m3_scan_prefill takes for this shape, ignoring
+ * s->chunk, or 0 when it takes none. */
+int32_t m3_prefill_max_chunk(const m3_shape* s);
+
+/* m3_prefill_chunk_used for m3_scan_prefill_gated and for
+ * m3_scan_prefill_prologue (which have kernel variants, and the prologue
+ * limits, of their own): the chunk each will use, or 0 when it refuses the
+ * shape. */
+int32_t m3_prefill_gated_chunk_used(const m3_shape* s);
+int32_t m3_prefill_prologue_chunk_used(const m3_shape* s);
+
+/* Waits for `stream`, then reads and clears the workspace's error word, which
+ * the prefill kernels set instead of hanging or faulting:
+ *   M3_OK           no error since the last query
+ *   M3_ERR_TIMEOUT  a chunk's look-back wait for its predecessors gave up (a
+ *                   bounded spin); that chunk's outputs and final state are NaN
+ *   M3_ERR_WORKSPACE the control word was out of range (the workspace was not
+ *                   zero-filled before its first use); nothing was computed
+ *   M3_ERR_NULL / M3_ERR_DEVICE on a NULL workspace or a failed HIP call.
+ * The error word accumulates over calls on the workspace until it is queried.
+ * The workspace is as passed to the prefill calls (at least 16 bytes). */
+m3_status m3_prefill_status(void* workspace, size_t workspace_bytes, void* stream);
+
+/* For tests of the error path only: the number of polls a prefill look-back
+ * wait makes before it gives up (0 restores the default, 2^20).  Process-wide;
+ * not for use while prefill calls run on other threads. */
+void m3_debug_set_spin_limit(uint32_t polls);
 
 /* Chunked prefill over a whole sequence (the recurrence above for t = 0..L-1).
  * Defined by: explainer panels 1 (coefficients, Eq. 6), 2 (causal operator as a

@@ -17,8 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libm3.so")
 
 M3_FP32, M3_BF16 = 0, 1
 STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
-          4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS"}
-EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_scan_prefill",
+          4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS", 7: "M3_ERR_TIMEOUT"}
+EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_prefill_max_chunk",
+           "m3_prefill_gated_chunk_used", "m3_prefill_prologue_chunk_used", "m3_prefill_status",
+           "m3_debug_set_spin_limit", "m3_scan_prefill",
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
            "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
            "m3_status_str", "m3_version")
@@ -57,8 +59,14 @@ def load_library(path: str = LIB_PATH):
     sp = ctypes.POINTER(M3Shape)
     lib.m3_prefill_workspace_bytes.restype = sz
     lib.m3_prefill_workspace_bytes.argtypes = [sp]
-    lib.m3_prefill_chunk_used.restype = ctypes.c_int32
-    lib.m3_prefill_chunk_used.argtypes = [sp]
+    for fn in ("m3_prefill_chunk_used", "m3_prefill_max_chunk", "m3_prefill_gated_chunk_used",
+               "m3_prefill_prologue_chunk_used"):
+        getattr(lib, fn).restype = ctypes.c_int32
+        getattr(lib, fn).argtypes = [sp]
+    lib.m3_prefill_status.restype = ctypes.c_int
+    lib.m3_prefill_status.argtypes = [vp, sz, vp]
+    lib.m3_debug_set_spin_limit.restype = None
+    lib.m3_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     lib.m3_scan_prefill.restype = ctypes.c_int
     lib.m3_scan_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.m3_decode_step.restype = ctypes.c_int
@@ -121,8 +129,28 @@ def prefill_workspace_bytes(shape: M3Shape) -> int:
     return int(load_library().m3_prefill_workspace_bytes(ctypes.byref(shape)))
 
 
-def prefill_chunk_used(shape: M3Shape) -> int:
-    return int(load_library().m3_prefill_chunk_used(ctypes.byref(shape)))
+def prefill_chunk_used(shape: M3Shape, variant: str = "plain") -> int:
+    """Chunk (tokens) the prefill entry point `variant` ("plain", "gated" or
+    "prologue") uses for this shape; 0 when it refuses the shape."""
+    fn = {"plain": "m3_prefill_chunk_used", "gated": "m3_prefill_gated_chunk_used",
+          "prologue": "m3_prefill_prologue_chunk_used"}[variant]
+    return int(getattr(load_library(), fn)(ctypes.byref(shape)))
+
+
+def prefill_max_chunk(shape: M3Shape) -> int:
+    return int(load_library().m3_prefill_max_chunk(ctypes.byref(shape)))
+
+
+def prefill_status(workspace: torch.Tensor) -> int:
+    """m3_prefill_status: waits for the workspace's stream, returns (and clears)
+    the status its error word records (0 = M3_OK)."""
+    return int(load_library().m3_prefill_status(
+        _ptr(workspace, None, workspace.device), workspace.numel() * workspace.element_size(),
+        _stream(workspace.device)))
+
+
+def debug_set_spin_limit(polls: int) -> None:
+    load_library().m3_debug_set_spin_limit(int(polls))
 
 
 def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 
 #include "m3_internal.h"
@@ -32,38 +33,76 @@ m3_status check_common(const m3_shape* s, bool need_seq) {
   return M3_OK;
 }
 
-// Tokens per chunk: the requested value (or a default of 128 (token, rank)
-// rows for N <= 64 and 256 rows above),
-// rounded down to a power of two in [16, 256], then halved until the chunk's
-// rows and angles fit the kernel's register budget and its LDS tiles fit on a
-// compute unit.
+// Tokens per chunk.  A chunk of q tokens fits when q is a power of two in
+// [16, 256], its q x R rows and q x N/2 angles fit the kernel's register
+// budget and its LDS tiles fit on a compute unit.  A requested chunk must fit
+// as given (no silent change: anything else is M3_ERR_SHAPE); chunk 0 takes the
+// default, 128 (token, rank) rows for N <= 64 and 256 rows above (the state
+// hand-off per chunk grows with N; so does the work that amortises it),
+// halved until it fits.
 size_t lds_need(int q, const m3_shape& s) {
   return fused_lds_bytes(q, s.rank, s.dstate, s.headdim, (int)esize(s.dtype));
 }
 
-int choose_chunk(const m3_shape& s) {
-  // default: 128 (token, rank) rows per chunk for N <= 64, 256 above (the
-  // state hand-off per chunk grows with N; so does the work that amortises it)
-  const int rows = s.dstate <= 64 ? 128 : 256;
-  int q = s.chunk > 0 ? s.chunk : std::max(16, rows / s.rank);
-  int p2 = 16;
-  while (p2 * 2 <= q && p2 < 256) p2 *= 2;
-  q = std::max(16, std::min(p2, 256));
-  while (q > 16 && (q * s.rank > fused_max_rows(s.dstate) || q * (s.dstate / 2) > kFusedAngleCap))
-    q /= 2;
-  while (q > 16 && lds_need(q, s) > (size_t)kLdsBudget) q /= 2;
-  if (lds_need(q, s) > (size_t)kLdsBudget) return 0;
-  return q;
+// The prologue prefill's own limits on top of the plain one's: bf16 inputs
+// at every N, fp32 at N <= 64, and one 16-row output tile per wave (its
+// variants with more made a GPU memory fault whose cause is not established,
+// as did an fp32 N = 128 one), plus its bias tables' LDS.
+bool prologue_ok(const m3_shape& s, int q) {
+  if (s.dtype == M3_FP32 && s.dstate >= 128) return false;
+  if (fused_row_tiles(q, s.rank, s.dstate) != 1) return false;
+  return fused_lds_bytes(q, s.rank, s.dstate, s.headdim, (int)esize(s.dtype), 1) <= (size_t)kLdsBudget;
 }
+
+bool chunk_fits(int q, const m3_shape& s, int gated, int pro) {
+  if (q < 16 || q > 256 || !is_pow2(q)) return false;
+  if (q * s.rank > fused_max_rows(s.dstate) || q * (s.dstate / 2) > kFusedAngleCap) return false;
+  if (lds_need(q, s) > (size_t)kLdsBudget) return false;
+  if (pro && !prologue_ok(s, q)) return false;
+  const PrefillVariant v{s.dtype, s.dstate, s.headdim, s.rank, fused_row_tiles(q, s.rank, s.dstate), gated, pro};
+  return v.RT != 0 && !prefill_variant_spills(v);
+}
+
+int max_chunk(const m3_shape& s, int gated, int pro) {
+  for (int q = 256; q >= 16; q /= 2)
+    if (chunk_fits(q, s, gated, pro)) return q;
+  return 0;
+}
+
+int choose_chunk(const m3_shape& s, int gated, int pro) {
+  if (s.chunk > 0) return chunk_fits(s.chunk, s, gated, pro) ? s.chunk : 0;
+  const int rows = s.dstate <= 64 ? 128 : 256;
+  for (int q = std::max(16, rows / s.rank); q >= 16; q /= 2)
+    if (chunk_fits(q, s, gated, pro)) return q;
+  return 0;
+}
+
+// The prefill variants that use scratch, from the build's compiler report:
+// {dtype, N, P, R, RT, gated, prologue} per line.
+const PrefillVariant kScratchVariants[] = {
+#include "m3_scratch_table.inc"
+    {-1, 0, 0, 0, 0, 0, 0}};
+
+// Look-back polls before a wait gives up (tests lower it to force the
+// error path; see m3_debug_set_spin_limit).
+std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};
 
 }  // namespace
 
-bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
+bool prefill_variant_spills(const PrefillVariant& v) {
+  for (const PrefillVariant& k : kScratchVariants)
+    if (k.dtype == v.dtype && k.N == v.N && k.P == v.P && k.R == v.R && k.RT == v.RT && k.gated == v.gated &&
+        k.pro == v.pro)
+      return true;
+  return false;
+}
+
+bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro) {
   // N = 256 is decode-only: its prefill kernels spill 76-708 bytes per lane to
   // scratch, and a memory fault was seen in one of them whose cause is not
   // established, so that path is not built.
   if (s.dstate > 128) return false;
-  const int q = choose_chunk(s);
+  const int q = choose_chunk(s, gated, pro);
   if (q == 0) return false;
   plan->Q = q;
   plan->nc = s.seqlen > 0 ? (s.seqlen + q - 1) / q : 0;
@@ -75,7 +114,7 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan) {
   plan->off_maps = align256(plan->off_recs + bhc * (s.dstate + 2) * sizeof(float));
   plan->off_states = align256(plan->off_maps + bhc * map);
   plan->bytes = align256(plan->off_states + bhc * map);
-  plan->lds = lds_need(q, s);
+  plan->lds = pro ? fused_lds_bytes(q, s.rank, s.dstate, s.headdim, (int)esize(s.dtype), 1) : lds_need(q, s);
   return true;
 }
 
@@ -87,17 +126,57 @@ extern "C" {
 
 size_t m3_prefill_workspace_bytes(const m3_shape* s) {
   if (check_common(s, true) != M3_OK) return 0;
-  PrefillPlan plan;
-  if (!plan_prefill(*s, &plan)) return 0;
-  return plan.bytes;
+  // the largest of the three entry points' needs for this shape (they share
+  // the layout; they differ only in which chunks they take)
+  size_t bytes = 0;
+  for (int v = 0; v < 3; ++v) {
+    PrefillPlan plan;
+    if (plan_prefill(*s, &plan, v == 1, v == 2)) bytes = std::max(bytes, plan.bytes);
+  }
+  return bytes;
 }
 
 int32_t m3_prefill_chunk_used(const m3_shape* s) {
   if (check_common(s, true) != M3_OK) return 0;
   PrefillPlan plan;
-  if (!plan_prefill(*s, &plan)) return 0;
+  if (!plan_prefill(*s, &plan, 0, 0)) return 0;
   return plan.Q;
 }
+
+int32_t m3_prefill_gated_chunk_used(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan, 1, 0)) return 0;
+  return plan.Q;
+}
+
+int32_t m3_prefill_prologue_chunk_used(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan, 0, 1)) return 0;
+  return plan.Q;
+}
+
+int32_t m3_prefill_max_chunk(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK || s->dstate > 128) return 0;
+  return max_chunk(*s, 0, 0);
+}
+
+m3_status m3_prefill_status(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return M3_ERR_NULL;
+  if (workspace_bytes < 16) return M3_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  unsigned long long word = 0;
+  unsigned long long* dev = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 8);
+  if (hipMemcpyAsync(&word, dev, sizeof(word), hipMemcpyDeviceToHost, hs) != hipSuccess) return M3_ERR_DEVICE;
+  if (hipStreamSynchronize(hs) != hipSuccess) return M3_ERR_DEVICE;
+  if (word == 0) return M3_OK;
+  if (launch_copy_or_zero(reinterpret_cast<float*>(dev), nullptr, 2, hs) != hipSuccess) return M3_ERR_DEVICE;
+  if (hipStreamSynchronize(hs) != hipSuccess) return M3_ERR_DEVICE;
+  return (word & kErrControl) ? M3_ERR_WORKSPACE : M3_ERR_TIMEOUT;
+}
+
+void m3_debug_set_spin_limit(uint32_t polls) { g_spin_limit.store(polls ? polls : kDefaultSpinLimit); }
 
 }  // extern "C"
 
@@ -142,7 +221,7 @@ m3_status prefill_common(const m3_shape* s,
   if (!x || !B || !C || !dt || !A || !lam || !y) return M3_ERR_NULL;
 
   PrefillPlan plan;
-  if (!plan_prefill(*s, &plan)) return M3_ERR_SHAPE;
+  if (!plan_prefill(*s, &plan, g.gated ? 1 : 0, pro.on ? 1 : 0)) return M3_ERR_SHAPE;
   if (!workspace || workspace_bytes < plan.bytes) return M3_ERR_WORKSPACE;
 
   // y (or out) must not alias any input, the final state or the workspace;
@@ -162,21 +241,7 @@ m3_status prefill_common(const m3_shape* s,
     if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
     if (h_out && in.p != h0 && overlaps(h_out, sbytes, in.p, in.n)) return M3_ERR_ALIAS;
   }
-  // the prologue's bias tables take LDS of their own; the prologue runs with
-  // one 16-row output tile per wave only (its variants with two or more
-  // spilled 40-96 bytes per lane to scratch, and one of them made a memory
-  // fault whose cause is not established), and not for fp32 inputs at
-  // N = 128 (those kernels spill 60-324 bytes per lane; one of them made a
-  // memory fault whose cause is not established either)
-  size_t lds = plan.lds;
-  if (pro.on) {
-    if (s->dtype == M3_FP32 && N >= 128) return M3_ERR_SHAPE;
-    const int waves = fused_threads(N) / 64;
-    const int tiles = (plan.Q * R + 31) / 32 * 2;
-    if ((tiles + waves - 1) / waves > 1) return M3_ERR_SHAPE;
-    lds = fused_lds_bytes(plan.Q, R, N, P, (int)es, 1);
-    if (lds > (size_t)kLdsBudget) return M3_ERR_SHAPE;
-  }
+  const size_t lds = plan.lds;   // (the prologue's plan includes its bias tables)
   if (h_out && overlaps(h_out, sbytes, y, ybytes)) return M3_ERR_ALIAS;
   if (h_out && h0 && h_out != h0 && overlaps(h_out, sbytes, h0, sbytes)) return M3_ERR_ALIAS;
 
@@ -189,6 +254,8 @@ m3_status prefill_common(const m3_shape* s,
   f.z = g.z; f.wy = g.w_y; f.wz = g.z ? g.w_z : nullptr;
   f.pro = pro.on ? 1 : 0; f.eps = pro.eps; f.biasB = pro.bias_B; f.biasC = pro.bias_C;
   f.ctl = reinterpret_cast<unsigned long long*>(ws);
+  f.err = reinterpret_cast<unsigned long long*>(ws + 8);
+  f.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   f.flags = reinterpret_cast<unsigned long long*>(ws + plan.off_flags);
   f.recs = reinterpret_cast<float*>(ws + plan.off_recs);
   f.maps = reinterpret_cast<float*>(ws + plan.off_maps);
@@ -196,7 +263,9 @@ m3_status prefill_common(const m3_shape* s,
   f.batch = b; f.L = L; f.H = H; f.N = N; f.P = P; f.R = R; f.logR = ilog2(R);
   f.Q = plan.Q; f.nc = plan.nc;
   f.use_maps = 1;   // (the launch decides from the device's resident workgroups)
-  if (launch_fused_prefill(f, lds, s->dtype, hs) != hipSuccess) return M3_ERR_DEVICE;
+  const hipError_t e = launch_fused_prefill(f, lds, s->dtype, hs);
+  if (e == hipErrorNotSupported) return M3_ERR_SHAPE;   // the loaded kernel uses scratch
+  if (e != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;
 }
 
@@ -345,6 +414,7 @@ const char* m3_status_str(m3_status st) {
     case M3_ERR_WORKSPACE: return "workspace missing or too small";
     case M3_ERR_DEVICE: return "HIP launch failed";
     case M3_ERR_ALIAS: return "an output aliases an input";
+    case M3_ERR_TIMEOUT: return "a prefill look-back wait gave up (outputs of the affected chunks are NaN)";
   }
   return "unknown status";
 }

@@ -80,13 +80,9 @@ namespace m3 {
 namespace fused {
 
 constexpr int kMaxBatch = 12;         // 16-byte B/X loads per thread per batch, at most
-constexpr unsigned kSpinLimit = 1u << 20;
 constexpr int kMapGroup = 1;        // predecessor maps loaded per round trip
 constexpr int kAngleCap = kFusedAngleCap;   // max Q * N/2 angles per chunk
 
-// Largest number of (token, rank) rows per chunk for state size N (bounds the
-// C~ fragments a wave keeps in registers).
-__host__ __device__ constexpr int fused_rows_cap(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
 
 __host__ __device__ constexpr int round_up_i(int a, int b) { return (a + b - 1) / b * b; }
 
@@ -112,6 +108,7 @@ __host__ __device__ constexpr int x_stride(int P, int esize) {
 //      access that take consecutive groups g of one row read consecutive entries.
 // B: B~ [QRp][N+8];  X: X [QRp][P+8] (permuted columns)
 // segl: kWaves floats, sega: kWaves x N/8 float4 (per-wave scan totals)
+// misc: 8 ints of workgroup scalars, then (prologue) the R column-norm factors of B_prev
 // pb: the prologue's bias tables [2][R][N] fp32 (B's, then C's), only when pro.
 __host__ __device__ constexpr Lds lds_layout(int Q, int R, int N, int P, int esize, int pro = 0) {
   const int QRp = round_up_i(Q * R, 32);
@@ -125,7 +122,7 @@ __host__ __device__ constexpr Lds lds_layout(int Q, int R, int N, int P, int esi
   o.B = o.csH + round_up_i((int)max_sz(sizeof(float2) * (size_t)Q * (N / 2 + 1), (size_t)esize * P * (N + 8)), 16);
   o.X = o.B + round_up_i((int)max_sz((size_t)esize * QRp * (N + 8), scan), 16);
   o.misc = o.X + (size_t)esize * QRp * x_stride(P, esize);
-  o.pb = o.misc + 32;
+  o.pb = o.misc + 64;
   o.total = o.pb + (pro ? sizeof(float) * (size_t)R * (2 * N + 4) : 0);   // B's [R][N], C's [R][N + 4]
   o.segl = o.B;
   o.sega = o.B + sizeof(float) * kWaves;
@@ -403,8 +400,9 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
 
   // ---- ticket: chunk-major order over all sequences ----
   // (the taker of the last ticket readies the control word for the next call:
-  // count 0, next epoch; the modulo only keeps a workspace that was not
-  // zero-filled in bounds)
+  // count 0, next epoch.  A count past the last ticket only arises in a
+  // workspace that was not zero-filled: the workgroup records the error and
+  // computes nothing.)
   const int nbh = p.batch * p.H;
   if (tid == 0) {
     const unsigned total = (unsigned)(nbh * p.nc);
@@ -413,12 +411,17 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
     const unsigned long long epoch = w >> kTicketBits;
     if (cnt == total - 1)
       __hip_atomic_store(p.ctl, (epoch + 1) << kTicketBits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_misc[0] = (int)(cnt % total);
+    if (cnt >= total)
+      __hip_atomic_fetch_or(p.err, (unsigned long long)kErrControl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_misc[0] = cnt < total ? (int)cnt : -1;
     s_misc[6] = (int)(unsigned)(epoch + 1);
     s_misc[7] = (int)(unsigned)((epoch + 1) >> 32);
   }
   __syncthreads();
-  const int ticket = s_misc[0];
+  // (read into a scalar register: the chunk's indices and addresses derived
+  // from it are then scalar too)
+  const int ticket = __builtin_amdgcn_readfirstlane(s_misc[0]);
+  if (ticket < 0) return;   // (uniform: the whole workgroup leaves)
   // this call's flag tag; flag_state() reads a flag of another call as 0
   const unsigned long long tag = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(s_misc[7]) << 32) |
                                  (unsigned)__builtin_amdgcn_readfirstlane(s_misc[6]);
@@ -432,8 +435,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
   const uint32_t esz = sizeof(T);
   const uint32_t rsB = (uint32_t)rowstepB * esz, rsX = (uint32_t)rowstepX * esz;
   float dv, lmv, dnv, lmnv_raw;
-  float4 th4[4];
-  float thdt[4];          // PRO: dt of the angle tokens
+  // tokens per angle thread, at most (NSEG = min(threads / NG, Q) segments of
+  // Q / NSEG tokens; Q * R rows fill at most RT row tiles per wave)
+  constexpr int kQmaxT = RT * 16 * kWaves / R;
+  constexpr int kAL0 = kQmaxT / (kThreads / NG) > 1 ? kQmaxT / (kThreads / NG) : 1;
+  constexpr int kAL = kAL0 < 4 ? kAL0 : 4;
+  float4 th4[kAL];
+  float thdt[kAL];        // PRO: dt of the angle tokens
   float4 pbv0, pbv1;      // PRO: this thread's bias items (B's, C's)
   Raw8<T> raw[kBatch];
   Raw8<T> craw[RTW][NK];
@@ -508,13 +516,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
     lmnv_raw = buf_load_f32(rLn, toff);
     const Rsrc rT = buf_rsrc(p.theta ? p.theta + tok0 * NH : nullptr, p.theta ? (nt - 1) * tsb * NH + NH * 4 : 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kAL; ++j) {
       const bool ok = j < ALEN && sg < NSEG;
       th4[j] = buf_load_f32x4(rT, ok ? (uint32_t)(sg * ALEN + j) * tsb * NH + 16 * cg : kOff);
     }
     if constexpr (PRO) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kAL; ++j) {
         const bool ok = j < ALEN && sg < NSEG;
         thdt[j] = buf_load_f32(rD, ok ? (uint32_t)(sg * ALEN + j) * tsb : kOff);
       }
@@ -556,11 +564,28 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
     s_misc[3] = 0;      // wave counter: map published
     s_misc[4] = 0;      // wave counter: state published
   }
+  float* s_bps = reinterpret_cast<float*>(s_misc + 8);   // PRO: B_prev column norm factors [R]
   if constexpr (PRO) {
     constexpr int kPb = R * N / 4;
     if (tid < kPb) {
       *reinterpret_cast<float4*>(s_pb + 4 * tid) = pbv0;
       *reinterpret_cast<float4*>(s_pb + R * N + (4 * tid / N) * (N + 4) + 4 * tid % N) = pbv1;
+    }
+    // a sequence's first chunk: wave 0 reduces B_prev's column norms now, into
+    // LDS, so the state set-up after the look-back holds no extra registers
+    if (c == 0 && p.Bp && wave == 0) {
+      const T* Bp0 = static_cast<const T*>(p.Bp) + (size_t)bh * R * N;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float ss = 0.f;
+        for (int n = lane; n < N; n += 64) {
+          const float t = to_f(Bp0[r * N + n]);
+          ss += t * t;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+        if (lane == 0) s_bps[r] = rsqrtf(ss / (float)N + p.eps);
+      }
     }
   }
   const float lmnv = (t0 + tid + 1 < p.L && tid < nt) ? lmnv_raw : 1.f;   // (only multiplies dnv = 0 otherwise)
@@ -580,17 +605,17 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
   }
   if constexpr (PRO) {   // raw angles: the step's angle is dt x theta
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kAL; ++j) {
       const float d = thdt[j];
       th4[j] = make_float4(d * th4[j].x, d * th4[j].y, d * th4[j].z, d * th4[j].w);
     }
   }
 #pragma unroll
-  for (int j = 1; j < 4; ++j)
+  for (int j = 1; j < kAL; ++j)
     if (j < ALEN) th4[j] = add4(th4[j], th4[j - 1]);
   float4 atot = th4[0];   // this thread's segment total (constant indices only:
 #pragma unroll               // a run-time index would put th4 in private memory)
-  for (int j = 1; j < 4; ++j)
+  for (int j = 1; j < kAL; ++j)
     if (j < ALEN) atot = th4[j];
   float4 ainc = atot;
 #pragma unroll
@@ -626,7 +651,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
   }
   if (sg < NSEG) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kAL; ++j) {
       if (j < ALEN) {
         const float4 ph = add4(abase, th4[j]);
         float s0, c0, s1, c1, s2, c2, s3, c3;
@@ -909,22 +934,13 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
     if (p.Bp) kappa0 = (1.f - p.lam[tok0]) * p.dt[tok0];
     const T* Bp = p.Bp ? static_cast<const T*>(p.Bp) + (size_t)bh * R * N : nullptr;
     const T* xp = p.xp ? static_cast<const T*>(p.xp) + (size_t)bh * R * P : nullptr;
-    float bps[R];   // PRO: B_prev column norm factors (every wave reduces over its lanes)
+    float bps[R];   // PRO: B_prev column norm factors (reduced in phase A, in LDS)
 #pragma unroll
     for (int r = 0; r < R; ++r) bps[r] = 1.f;
     if constexpr (PRO) {
       if (Bp) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float ss = 0.f;
-          for (int n = lane; n < N; n += 64) {
-            const float t = to_f(Bp[r * N + n]);
-            ss += t * t;
-          }
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
-          bps[r] = rsqrtf(ss / (float)N + p.eps);
-        }
+        for (int r = 0; r < R; ++r) bps[r] = s_bps[r];
       }
     }
 #pragma unroll
@@ -978,7 +994,7 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
           if (k0 > k2 || (k2 == W && k0 >= W)) { nmap = k2; state = k2 < W; break; }
           if (k0 > 0) { nmap = k0; state = 0; break; }   // compose what is there, then wait
           __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) { nmap = -1; break; }
+          if (++spins > p.spin_limit) { nmap = -1; break; }
         }
         if (lane == 0) { s_misc[1] = nmap; s_misc[5] = state; }
       }
@@ -1059,6 +1075,8 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
     }
   }
   const float nanv = __builtin_nanf("");
+  if (!chain_ok && tid == 0)   // the wait gave up: recorded for m3_prefill_status
+    __hip_atomic_fetch_or(p.err, (unsigned long long)kErrLookback, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool publish = c + 1 < p.nc;
   const Rsrc rSo = buf_rsrc(p.states + chunk_id * SLOT, publish ? SLOT * 4 : 0);
   // S_in^T goes into the (now free) cos/sin region for the readout
@@ -1291,14 +1309,28 @@ __global__ __launch_bounds__(fused_threads(N), (prefill_waves_per_simd<T, N, P, 
 
 template <typename T, int N, int P, int R, int RT, bool G, bool PRO>
 hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
-  // LDS limit raised once per instantiation
-  static bool lds_set = false;
-  hipError_t e;
-  if (!lds_set && lds > 64 * 1024) {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G, PRO>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)) != hipSuccess)
-      return e;
-    lds_set = true;
+  // A variant that uses scratch is never launched (the host plan already
+  // refuses the ones the build report lists; this checks the loaded code).
+  static std::atomic<int> scratch_state{0};   // 0 unknown, 1 none, 2 uses scratch
+  int st = scratch_state.load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G, PRO>)) != hipSuccess)
+      return hipErrorInvalidDeviceFunction;
+    st = fa.localSizeBytes > 0 ? 2 : 1;
+    scratch_state.store(st, std::memory_order_relaxed);
+  }
+  if (st == 2) return hipErrorNotSupported;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  // The LDS limit is raised once per instantiation and device (one bit per
+  // device; callers racing on the first launch just set it twice).
+  static std::atomic<unsigned long long> lds_set{0};
+  if (lds > 64 * 1024 && (dev < 0 || !(lds_set.load(std::memory_order_acquire) >> dev & 1ull))) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<T, N, P, R, RT, G, PRO>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+    if (e != hipSuccess) return e;
+    if (dev >= 0) lds_set.fetch_or(1ull << dev, std::memory_order_acq_rel);
   }
   const size_t grid = (size_t)p.batch * p.H * p.nc;
   // Maps let a chunk finish before its predecessor's state exists; they pay off
@@ -1311,8 +1343,7 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   // computed for: one 64-bit word per device, so concurrent callers never see
   // half an update)
   static std::atomic<unsigned long long> cache[64];
-  int dev = 0, resident = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  int resident = 0;
   const unsigned long long hit = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0ull;
   if (hit != 0 && (hit >> 32) == (unsigned long long)lds) {
     resident = (int)(hit & 0xffffffffull);
@@ -1332,16 +1363,10 @@ hipError_t launch(const FusedParams& p, size_t lds, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Row tiles per wave for a chunk of Q tokens x R ranks (rows rounded up to 32)
-// shared out over the waves of an N-state workgroup.
-inline int row_tiles_per_wave(int Q, int R, int N) {
-  const int rows = round_up_i(Q * R, 32), waves = fused_threads(N) / 64;
-  return (rows / 16 + waves - 1) / waves;
-}
 
 template <typename T, int N, int P, int R>
 hipError_t launch_rt(const FusedParams& p, size_t lds, hipStream_t s) {
-  const int rt = row_tiles_per_wave(p.Q, R, N);
+  const int rt = fused_row_tiles(p.Q, R, N);
   constexpr int kWaves = fused_threads(N) / 64;
   constexpr int kMaxRT = (fused_rows_cap(N) / 16 + kWaves - 1) / kWaves;
   // variants: plain, gated readout, prologue (not both)

@@ -41,6 +41,11 @@ inline bool supported_rank(int R) { return R == 1 || R == 2 || R == 4 || R == 8;
 constexpr int kTicketBits = 26;
 constexpr unsigned long long kTicketMask = (1ull << kTicketBits) - 1;
 constexpr size_t kMaxChunks = (size_t)kTicketMask;   // chunks per call, at most
+// Bits of the workspace's error word (offset 8), set by the prefill kernel and
+// read back (and cleared) by m3_prefill_status.
+constexpr unsigned kErrLookback = 1u;   // a look-back wait gave up (outputs of that chunk are NaN)
+constexpr unsigned kErrControl = 2u;    // the control word was out of range (workspace not zero-filled)
+constexpr unsigned kDefaultSpinLimit = 1u << 20;
 struct PrefillPlan {
   int Q;              // tokens per chunk
   int nc;             // chunks per sequence
@@ -48,8 +53,9 @@ struct PrefillPlan {
   size_t lds;         // dynamic LDS per workgroup
 };
 
-// Fills `plan` for a validated shape; returns false if no chunk size fits.
-bool plan_prefill(const m3_shape& s, PrefillPlan* plan);
+// Fills `plan` for a validated shape and entry point (gated readout,
+// prologue); returns false if no chunk size fits.
+bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro);
 
 struct FusedParams {
   const void* x; const void* B; const void* C;
@@ -59,6 +65,8 @@ struct FusedParams {
   void* out;               // gated readout out [b,L,H,P], or NULL
   const void* z; const float* wy; const float* wz;   // gate input and weights (each may be NULL)
   unsigned long long* ctl; unsigned long long* flags; float* recs; float* maps; float* states;
+  unsigned long long* err;   // sticky error word (kErr* bits), read back by m3_prefill_status
+  unsigned spin_limit;       // polls a look-back wait makes before it gives up
   int batch, L, H, N, P, R, logR, Q, nc;
   int use_maps;          // publish chunk maps when the predecessor's state is late
   int pro; float eps;    // prologue: B/C/B_prev column RMS norm (+ eps), angle = dt x theta
@@ -78,7 +86,23 @@ __host__ __device__ constexpr int fused_slot_floats(int N, int P) {
 }
 // Chunk limits of the single-pass prefill: (token, rank) rows per chunk and
 // angles (tokens x N/2) per chunk; they bound the per-thread prefetch registers.
-inline int fused_max_rows(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
+__host__ __device__ constexpr int fused_rows_cap(int N) { return N <= 32 ? 512 : N <= 128 ? 256 : 128; }
+inline int fused_max_rows(int N) { return fused_rows_cap(N); }
+// Output row tiles per wave -- the kernel variant's RT -- for a chunk of Q
+// tokens x R ranks at state size N: the rows rounded up to 32, in 16-row tiles
+// shared out over the waves, rounded up to 1, 2 or 4.
+inline int fused_row_tiles(int Q, int R, int N) {
+  const int rows = (Q * R + 31) / 32 * 32, waves = fused_threads(N) / 64;
+  const int rt = (rows / 16 + waves - 1) / waves;
+  return rt <= 1 ? 1 : rt <= 2 ? 2 : rt <= 4 ? 4 : 0;
+}
+// A prefill kernel variant: the template arguments the launch picks.
+struct PrefillVariant { int dtype, N, P, R, RT, gated, pro; };
+// Whether the build's compiler report gave this variant any scratch (private
+// memory) per lane.  The library launches no such kernel: every GPU memory
+// fault and the one wrong result met in this kernel's development came from
+// variants that spilled to scratch, and their cause was not established.
+bool prefill_variant_spills(const PrefillVariant& v);
 constexpr int kFusedAngleCap = 8192;
 size_t fused_lds_bytes(int Q, int R, int N, int P, int esize, int pro = 0);
 hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hipStream_t stream);

@@ -155,7 +155,7 @@ def test_gated_validation_codes(lib):
 
 
 def test_prologue_validation_codes(lib):
-    ok = m3.make_shape(2, 128, 3, 64, 64, 4, 64, m3.M3_BF16)
+    ok = m3.make_shape(2, 128, 3, 64, 64, 4, 32, m3.M3_BF16)   # 128 rows: one output tile per wave
     pro = m3.M3Prologue(1e-6, FAR[11], FAR[12])
 
     def prefill(shape, p=pro, **over):
@@ -182,6 +182,10 @@ def test_prologue_validation_codes(lib):
     assert prefill(m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1)) == 2
     assert prefill(m3.make_shape(2, 512, 3, 64, 64, 2, 128, 1)) == 2
     assert prefill(m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1)) == 2
+    assert prefill(m3.make_shape(2, 128, 3, 64, 64, 4, 64, 1)) == 2   # 256 rows: two tiles per wave
+    for R, q in ((1, 256), (2, 128), (4, 64)):   # the chunk query agrees with the call
+        assert m3.prefill_chunk_used(m3.make_shape(2, 512, 3, 64, 64, R, q, 1), "prologue") == 0
+        assert m3.prefill_chunk_used(m3.make_shape(2, 512, 3, 64, 64, R, q, 1)) == q
     # fp32 inputs at N = 128: rejected
     assert prefill(m3.make_shape(2, 128, 3, 32, 128, 1, 0, m3.M3_FP32)) == 2
     assert prefill(m3.make_shape(2, 128, 3, 64, 128, 4, 0, m3.M3_FP32)) == 2
@@ -198,6 +202,8 @@ def test_workspace_size_matches_layout(lib, name):
     w = inputs.WORKLOADS[name]
     dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
     shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, dcode)
+    if m3.prefill_chunk_used(shape) == 0:   # the long workload's 128-token chunk: 512 rows do not fit
+        shape.chunk = min(w.chunk, m3.prefill_max_chunk(shape))
     q = m3.prefill_chunk_used(shape)
     assert q >= 16 and (q & (q - 1)) == 0
     nc = -(-w.seqlen // q)
@@ -227,28 +233,85 @@ def test_chunk_count_cap(lib):
     assert m3.prefill_chunk_used(s(256)) == 0 and m3.prefill_workspace_bytes(s(256)) == 0
 
 
+def _scratch_variants():
+    """Prefill variants (dtype code, N, P, R, RT, gated, prologue) the build's
+    compiler report gives scratch memory, read from the report itself."""
+    import json
+    import re
+    path = os.path.join(os.path.dirname(m3.LIB_PATH), "..", "_build", "kernel_usage.json")
+    if not os.path.exists(path):
+        pytest.skip("no kernel usage report (build the library first)")
+    usage = json.load(open(path))
+    pat = re.compile(r"prefill_kernelI(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E")
+    out = set()
+    for name, u in usage.items():
+        m = pat.search(name)
+        if m and u.get("scratch", 0) > 0:
+            t, *rest = m.groups()
+            out.add((1 if t == "DF16b" else 0, *map(int, rest)))
+    return out
+
+
+def _row_tiles(q, R, N):
+    rows = -(-q * R // 32) * 32
+    waves = (1024 if N >= 128 else 512) // 64
+    rt = -(-(rows // 16) // waves)
+    return 1 if rt <= 1 else 2 if rt <= 2 else 4
+
+
+def test_prefill_refuses_scratch_variants(lib):
+    """No shape the host plan takes runs a kernel variant that uses scratch
+    (from the compiler report of this build), for each entry point; and the
+    configurations' kernels use none."""
+    spills = _scratch_variants()
+    for variant, (g, pro) in {"plain": (0, 0), "gated": (1, 0), "prologue": (0, 1)}.items():
+        for code in (m3.M3_BF16, m3.M3_FP32):
+            for N in (16, 32, 64, 128):
+                for P in (16, 32, 64, 128):
+                    for R in (1, 2, 4, 8):
+                        for chunk in (0, 16, 32, 64, 128, 256):
+                            s = m3.make_shape(1, 300, 2, P, N, R, chunk, code)
+                            q = m3.prefill_chunk_used(s, variant)
+                            if q:
+                                assert (code, N, P, R, _row_tiles(q, R, N), g, pro) not in spills
+    from state_space_sequence_02_amd import inputs
+    for name in ("tiny", "siso", "mimo", "long"):
+        w = inputs.WORKLOADS[name]
+        code = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+        s = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0, code)
+        assert m3.prefill_chunk_used(s) > 0 and m3.prefill_chunk_used(s, "gated") > 0, name
+
+
 def test_prefill_unsupported_shapes(lib):
     # the prefill takes N <= 128 (N = 256 is decode-only); fp32 N=128 P=128 R=8
-    # does not fit one compute unit's 160 KB of LDS even at 16 tokens per chunk
-    too_big = {("fp32", 128, 128, 8)} | {(dt, 256, P, R) for dt in ("bf16", "fp32")
-                                          for P in (16, 32, 64, 128) for R in (1, 2, 4, 8)}
+    # does not fit one compute unit's 160 KB of LDS even at 16 tokens per chunk;
+    # every variant that uses scratch is refused as well
+    spills = _scratch_variants()
     for dt, code in (("bf16", m3.M3_BF16), ("fp32", m3.M3_FP32)):
         for N in (16, 32, 64, 128, 256):
             for P in (16, 32, 64, 128):
                 for R in (1, 2, 4, 8):
                     s = m3.make_shape(1, 100, 2, P, N, R, 0, code)
                     q, ws = m3.prefill_chunk_used(s), m3.prefill_workspace_bytes(s)
-                    if (dt, N, P, R) in too_big:
-                        assert q == 0 and ws == 0, (dt, N, P, R)
+                    if N == 256 or (dt, N, P, R) == ("fp32", 128, 128, 8):
+                        assert q == 0 and m3.prefill_max_chunk(s) == 0, (dt, N, P, R)
+                        continue
+                    # the default: 128 rows (N <= 64) or 256 rows, halved until taken
+                    cands = [c for c in (256, 128, 64, 32, 16) if c <= max(16, (128 if N <= 64 else 256) // R)]
+                    ok = [c for c in cands if (code, N, P, R, _row_tiles(c, R, N), 0, 0) not in spills]
+                    if q:
+                        assert q in ok and ws > 0, (dt, N, P, R, q)
                     else:
-                        assert q >= 16 and ws > 0, (dt, N, P, R)
+                        assert all((code, N, P, R, _row_tiles(c, R, N), 0, 0) in spills for c in cands) or ws == 0
 
 
-def test_chunk_request_rounding(lib):
+def test_chunk_request_is_exact(lib):
     s = lambda c, R=1, N=64: m3.make_shape(1, 1000, 1, 64, N, R, c, m3.M3_BF16)
     assert m3.prefill_chunk_used(s(64)) == 64
-    assert m3.prefill_chunk_used(s(100)) == 64          # rounded down to a power of two
-    assert m3.prefill_chunk_used(s(5)) == 16            # at least 16
-    assert m3.prefill_chunk_used(s(4096)) <= 256
+    assert m3.prefill_chunk_used(s(100)) == 0           # not a power of two: refused, not rounded
+    assert m3.prefill_chunk_used(s(5)) == 0              # below 16
+    assert m3.prefill_chunk_used(s(512)) == 0            # above 256
+    assert m3.prefill_chunk_used(s(128, R=4, N=128)) == 0         # 512 rows do not fit one CU
+    assert m3.prefill_max_chunk(s(128, R=4, N=128)) == 64
     assert m3.prefill_chunk_used(s(0, R=4, N=128)) == 64          # 256 rows by default
     assert m3.prefill_chunk_used(s(0)) == 128                     # N <= 64: 128 rows by default

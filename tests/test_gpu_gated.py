@@ -11,7 +11,7 @@ import oracle
 import state_space_sequence_02_amd as m3
 from state_space_sequence_02_amd import inputs
 
-from _parity import TOL, check_blocks, dev_inputs, gate_scale, note, oracle_inputs, to64
+from _parity import TOL, check_blocks, dev_inputs, gate_scale, note, oracle_inputs, taken_chunk, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ CASES = [
     ("mimo", dict(batch=1, seqlen=97, nheads=2), 64, True, False),           # gate, unit weights
     ("mimo", dict(batch=1, seqlen=70, nheads=2, rank=2, dstate=64), 64, True, True),
     ("mimo", dict(batch=1, seqlen=90, nheads=2, rank=8, dstate=64), 16, True, True),
-    ("mimo", dict(batch=1, seqlen=90, nheads=1, rank=8, headdim=128, dstate=128), 16, True, True),
+    ("mimo", dict(batch=1, seqlen=90, nheads=1, rank=8, headdim=128, dstate=64), 16, True, True),
     ("tiny", dict(batch=1, seqlen=100, nheads=2, rank=4, headdim=32, dstate=32), 32, True, True),   # fp32
     ("tiny", dict(batch=2, seqlen=77, nheads=1), 16, True, True),                                    # fp32 R=1
 ]
@@ -62,6 +62,7 @@ def test_prefill_gated(case):
     c = inputs.random_carry(w, seed=seed + 1)
     z, wy, wz = _gate_inputs(w, seed + 2, (w.batch, w.seqlen), gate, weights)
     dg, cg = dev_inputs(d), dev_inputs(c)
+    assert taken_chunk(w, chunk, "gated") == chunk
     note(f"prefill gated {name} {kw} {w.dtype} chunk={chunk} gate={gate} weights={weights}")
     out, h = m3.scan_prefill_gated(**{k: dg[k] for k in KEYS}, **cg,
                                    z=None if z is None else z.cuda(), w_y=None if wy is None else wy.cuda(),

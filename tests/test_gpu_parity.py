@@ -12,7 +12,7 @@ import oracle
 import state_space_sequence_02_amd as m3
 from state_space_sequence_02_amd import inputs
 
-from _parity import TOL, check_blocks, dev_inputs, note, oracle_inputs, to64
+from _parity import TOL, check_blocks, dev_inputs, note, oracle_inputs, taken_chunk, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -63,11 +63,11 @@ SMALL = [
     dict(name="mimo", kw=dict(batch=1, seqlen=130, nheads=2), chunk=32),
     dict(name="mimo", kw=dict(batch=2, seqlen=97, nheads=2), chunk=64),
     dict(name="mimo", kw=dict(batch=1, seqlen=70, nheads=2, headdim=16, dstate=16, rank=8), chunk=16),
-    dict(name="mimo", kw=dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=128, rank=2), chunk=32),
+    dict(name="mimo", kw=dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=64, rank=2), chunk=32),
     pytest.param(dict(name="mimo", kw=dict(batch=1, seqlen=64, nheads=1, headdim=64, dstate=256, rank=1), chunk=32),
                  marks=pytest.mark.skip(reason="N=256 prefill is not built (heavy scratch spills; one unexplained "
                                                 "GPU memory fault)")),
-    dict(name="long", kw=dict(seqlen=515, nheads=2), chunk=128),
+    dict(name="long", kw=dict(seqlen=515, nheads=2), chunk=64),
     # 256 and 512 (token, rank) rows per chunk: two and four 16-row output tiles per wave
     dict(name="siso", kw=dict(batch=1, seqlen=600, nheads=2), chunk=256),
     dict(name="mimo", kw=dict(batch=1, seqlen=300, nheads=2, headdim=64, dstate=32, rank=4), chunk=128),
@@ -113,7 +113,11 @@ def test_chunk_size_invariance(dtype):
     dg, cg = dev_inputs(d), dev_inputs(c)
     yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
     outs = []
-    for q in (16, 32, 64, 128):
+    # (fp32 at 128 tokens x R = 2: the tiles do not fit one compute unit's LDS,
+    # so the library refuses that chunk)
+    chunks = [q for q in (16, 32, 64, 128) if taken_chunk(w, q) == q]
+    assert chunks[:3] == [16, 32, 64]
+    for q in chunks:
         note(f"chunk invariance {dtype} q={q}")
         y, h = _run_prefill(dg, cg, chunk=q)
         check_blocks(to64(y), yr, TOL[dtype], (1, 3, 4), f"y q={q}", elem_axes=(3, 4))
@@ -394,16 +398,41 @@ def test_workload_siso_full_size():
 
 def test_workload_mimo_full_size():
     w = inputs.WORKLOADS["mimo"]
-    _prefill_case(w, seed=0, carry=False, chunk=w.chunk, heads=[0, 22])
+    _prefill_case(w, seed=0, carry=False, chunk=w.chunk, heads=[0, 7, 22, 31])
+
+
+def test_refused_shapes_raise_before_launch():
+    """Shapes the host plan refuses (512-row chunks, kernel variants that would
+    use scratch memory) raise M3_ERR_SHAPE and launch nothing."""
+    for name, kw, chunk in (("long", dict(seqlen=300, nheads=2), 128),
+                            ("mimo", dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=128, rank=2), 32)):
+        w = inputs.workload(name, **kw)
+        assert taken_chunk(w, chunk) == 0
+        dg = dev_inputs(inputs.make_prefill_inputs(w, seed=2))
+        note(f"refused prefill {name} {kw} chunk={chunk}")
+        with pytest.raises(m3.M3Error, match="M3_ERR_SHAPE"):
+            _run_prefill(dg, chunk=chunk)
+
+
+def test_workload_siso_default_chunk_all_heads():
+    """The SISO workload exactly as the benchmark launches it (the library's
+    default chunk, 128 tokens), every head of every sequence."""
+    w = inputs.WORKLOADS["siso"]
+    assert taken_chunk(w, 0) == 128
+    _prefill_case(w, seed=0, carry=False, chunk=0)
 
 
 def test_workload_long_full_size():
     w = inputs.WORKLOADS["long"]
     note("long: generating inputs on the device")
     d = inputs.make_prefill_inputs(w, seed=0, device="cuda")
-    note(f"prefill long chunk={w.chunk}")
-    y, h = _run_prefill(d, chunk=w.chunk)
-    heads = [5, 30]
+    # the configuration's 128-token chunk is 512 (token, rank) rows, which do not
+    # fit one compute unit; the largest chunk the library takes for it is used
+    q = taken_chunk(w, 0)
+    assert taken_chunk(w, w.chunk) == 0 and q == 64
+    note(f"prefill long chunk={q}")
+    y, h = _run_prefill(d, chunk=q)
+    heads = [0, 5, 17, 30]
     yr, hr = oracle.scan(**oracle_inputs(d, heads))
     check_blocks(to64(y[:, :, heads]), yr, TOL["bf16"], (1, 3, 4), "long y", elem_axes=(3, 4))
     check_blocks(to64(h[:, heads]), hr, TOL["bf16"], (2, 3), "long h")
@@ -421,11 +450,74 @@ def test_workload_decode_full_size():
         ys.append(m3.decode_step(h, d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["A"], d["lam"][s],
                                  d["theta"][s], **kw))
     torch.cuda.synchronize()
-    seqs, heads = [0, 77, 127], [0, 19, 31]
+    seqs, heads = [0, 1, 41, 77, 100, 127], [0, 7, 19, 31]
     ysel = torch.stack([ys[s][seqs][:, heads] for s in range(w.steps)])
     sub = {k: (v[:, seqs][:, :, heads] if (v is not None and k != "A") else v) for k, v in d.items()}
     sub["A"] = d["A"][heads]
-    yr, hr = oracle.decode_steps(np.zeros((3, 3, w.dstate, w.headdim)), sub["x"], sub["B"], sub["C"],
+    yr, hr = oracle.decode_steps(np.zeros((len(seqs), len(heads), w.dstate, w.headdim)), sub["x"], sub["B"], sub["C"],
                                  sub["dt"], sub["A"], sub["lam"], sub["theta"])
     check_blocks(to64(ysel), yr, TOL["bf16"], (3, 4), "decode workload y")
     check_blocks(to64(h[seqs][:, heads]), hr, TOL["bf16"], (2, 3), "decode workload h")
+
+
+# ---------------------------------------------------------------------------
+# error reporting (forced from the host: every kernel still exits normally)
+
+def _ws_for(w, chunk):
+    return torch.zeros(m3.prefill_workspace_bytes(_shape_of(w, chunk)), dtype=torch.uint8, device="cuda")
+
+
+def test_lookback_timeout_is_reported():
+    """A look-back wait that gives up (the spin limit lowered to one poll, so
+    chunks whose predecessors are still running give up) writes NaN for that
+    chunk and sets the workspace's error word: m3_prefill_status reports
+    M3_ERR_TIMEOUT once and clears it; the same workspace then serves a normal
+    call whose outputs match the oracle."""
+    w = inputs.workload("mimo", batch=1, seqlen=2048, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=91)
+    dg = dev_inputs(d)
+    ws = _ws_for(w, 64)
+    note("prefill with a one-poll look-back limit")
+    try:
+        m3.debug_set_spin_limit(1)
+        y, h = m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS}, chunk=64, workspace=ws)
+        st = m3.prefill_status(ws)
+    finally:
+        m3.debug_set_spin_limit(0)
+    assert st in (0, 7)
+    if st == 7:
+        assert torch.isnan(y.float()).any()
+    assert m3.prefill_status(ws) == 0          # cleared by the query
+    note("prefill on the same workspace, default limit")
+    y, h = m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS}, chunk=64, workspace=ws)
+    assert m3.prefill_status(ws) == 0
+    yr, hr = oracle.scan(**oracle_inputs(d))
+    check_blocks(to64(y), yr, TOL["bf16"], (1, 3, 4), "y after timeout", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL["bf16"], (2, 3), "h after timeout")
+
+
+def test_unzeroed_workspace_is_reported():
+    """A workspace that was never zero-filled (all ones here) is reported by
+    m3_prefill_status (M3_ERR_WORKSPACE for the out-of-range control word, or
+    M3_ERR_TIMEOUT from waits on garbage flags, with the spin limit low so
+    they give up at once) instead of silently wrong results; zero-filled, it
+    then works."""
+    w = inputs.workload("mimo", batch=1, seqlen=300, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=92)
+    dg = dev_inputs(d)
+    ws = _ws_for(w, 32)
+    ws.fill_(255)
+    note("prefill on a workspace of all ones")
+    try:
+        m3.debug_set_spin_limit(4)
+        m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS}, chunk=32, workspace=ws)
+        st = m3.prefill_status(ws)
+    finally:
+        m3.debug_set_spin_limit(0)
+    assert st in (4, 7), st
+    ws.zero_()
+    note("prefill on the same workspace, zero-filled")
+    y, h = m3.scan_prefill(**{k: dg[k] for k in PREFILL_KEYS}, chunk=32, workspace=ws)
+    assert m3.prefill_status(ws) == 0
+    yr, hr = oracle.scan(**oracle_inputs(d))
+    check_blocks(to64(y), yr, TOL["bf16"], (1, 3, 4), "y", elem_axes=(3, 4))

@@ -12,7 +12,7 @@ import oracle
 import state_space_sequence_02_amd as m3
 from state_space_sequence_02_amd import inputs
 
-from _parity import TOL, check_blocks, dev_inputs, note, to64
+from _parity import TOL, check_blocks, dev_inputs, note, taken_chunk, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -72,15 +72,18 @@ def test_decode_prologue(shape, biases):
 PREFILL = [
     # (workload, overrides, chunk, biases, carry)
     ("siso", dict(batch=2, seqlen=300, nheads=3), 64, True, True),
-    pytest.param(("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),
-                 marks=pytest.mark.skip(reason="prologue prefill with two or more output tiles per wave is "
-                                               "switched off (scratch spills; one unexplained GPU memory fault)")),
+    # two output tiles per wave: refused on the host (the prologue's variants
+    # with more than one tile per wave spilled to scratch and one of them made
+    # a GPU memory fault whose cause was not established)
+    ("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),
     ("siso", dict(batch=2, seqlen=200, nheads=2), 128, False, False),
     ("mimo", dict(batch=2, seqlen=130, nheads=2), 64, True, True),
     ("mimo", dict(batch=1, seqlen=97, nheads=2), 32, False, True),
     ("mimo", dict(batch=1, seqlen=70, nheads=2, rank=2, dstate=64), 64, True, True),
     ("mimo", dict(batch=1, seqlen=90, nheads=2, rank=8, dstate=32), 16, True, True),
     ("mimo", dict(batch=1, seqlen=90, nheads=1, rank=8, headdim=128, dstate=128), 16, True, True),
+    ("mimo", dict(batch=2, seqlen=130, nheads=2, dstate=64), 32, True, True),
+    ("mimo", dict(batch=1, seqlen=150, nheads=2, dstate=64, rank=2), 64, False, True),
     ("tiny", dict(batch=1, seqlen=100, nheads=2, rank=4, headdim=32, dstate=32), 32, True, True),   # fp32
     ("tiny", dict(batch=2, seqlen=77, nheads=1), 16, True, True),                                    # fp32 R=1
 ]
@@ -95,6 +98,15 @@ def test_prefill_prologue(case):
     c = inputs.random_carry(w, seed=seed + 1) if carry else {}
     th, bb, bc = _pro_inputs(w, seed + 2, (w.batch, w.seqlen), biases)
     dg, cg = dev_inputs(d), (dev_inputs(c) if c else {})
+    if taken_chunk(w, chunk, "prologue") == 0:
+        # refused on the host: two or more output tiles per wave, or a kernel
+        # variant the build report gives scratch memory (at N = 128 the prologue
+        # variants keep a few values in scratch)
+        note(f"prefill prologue {name} {kw} chunk={chunk}: refused on the host")
+        with pytest.raises(m3.M3Error, match="M3_ERR_SHAPE"):
+            m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
+                                     chunk=chunk, eps=eps)
+        return
     note(f"prefill prologue {name} {kw} {w.dtype} chunk={chunk} biases={biases} carry={carry}")
     y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
                                     chunk=chunk, eps=eps, bias_B=None if bb is None else bb.cuda(),
@@ -111,7 +123,7 @@ def test_prefill_prologue(case):
 def test_prologue_prefill_then_decode():
     """prefill with the prologue over L - 2 tokens, then two decode steps with
     it, equals the prologue's recurrence over the whole sequence."""
-    w = inputs.workload("mimo", batch=2, seqlen=70, nheads=2)
+    w = inputs.workload("mimo", batch=2, seqlen=70, nheads=2, dstate=64)
     d = inputs.make_prefill_inputs(w, seed=801)
     th, bb, bc = _pro_inputs(w, 802, (w.batch, w.seqlen), True)
     dg = dev_inputs(d)
@@ -138,7 +150,7 @@ def test_prologue_prefill_then_decode():
 def test_fused_entry_points_edges():
     """L = 0 (h_out receives h0), L = 1 with h_out aliasing h0, for the gated
     and prologue prefill entry points."""
-    w = inputs.workload("mimo", batch=2, seqlen=1, nheads=2)
+    w = inputs.workload("mimo", batch=2, seqlen=1, nheads=2, dstate=64)
     d = inputs.make_prefill_inputs(w, seed=901)
     c = inputs.random_carry(w, seed=902)
     dg, cg = dev_inputs(d), dev_inputs(c)
