@@ -195,6 +195,29 @@ m3_status m3_decode_step(const m3_shape* s,
                          const float* theta,
                          void* y, void* stream);
 
+/* Size of the scratch buffer m3_scan_prefill_noalloc uses on each device. */
+#define M3_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* m3_scan_prefill for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same computation and arguments without the workspace.  The chunk hand-off
+ * lives in a buffer of M3_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds
+ * on each device it runs on until the process ends; the call allocates nothing
+ * and calls no allocating routine.  Shapes whose workspace
+ * (m3_prefill_workspace_bytes) is larger get M3_ERR_WORKSPACE (e.g. a few
+ * thousand chunks of a 128 x 64 state); nothing is launched then.  Every call
+ * on a device shares that device's buffer and clears its control words first
+ * (with a kernel on `stream`): calls that overlap on one device race, so a
+ * caller serialises them (one stream, or events).  Errors of the look-back
+ * show as NaN outputs (there is no status query for this buffer).  Everything
+ * else as m3_scan_prefill. */
+m3_status m3_scan_prefill_noalloc(const m3_shape* s,
+                                  const void* x, const void* B, const void* C,
+                                  const float* dt, const float* A, const float* lam,
+                                  const float* theta,
+                                  const float* h0, const void* B_prev, const void* x_prev,
+                                  void* y, float* h_out, void* stream);
+
 /* m3_decode_step with the state held in bf16 between steps: the pages' decode
  * kernels are benchmarked with an FP32 or a BF16 state (paper page, Table 6).
  * Each step reads the bf16 state, does the update in fp32, reads y from the

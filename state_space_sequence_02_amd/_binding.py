@@ -20,7 +20,7 @@ STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
           4: "M3_ERR_WORKSPACE", 5: "M3_ERR_DEVICE", 6: "M3_ERR_ALIAS", 7: "M3_ERR_TIMEOUT"}
 EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_prefill_max_chunk",
            "m3_prefill_gated_chunk_used", "m3_prefill_prologue_chunk_used", "m3_prefill_status",
-           "m3_debug_set_spin_limit", "m3_scan_prefill",
+           "m3_debug_set_spin_limit", "m3_scan_prefill", "m3_scan_prefill_noalloc",
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
            "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
            "m3_status_str", "m3_version")
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH):
     lib.m3_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     lib.m3_scan_prefill.restype = ctypes.c_int
     lib.m3_scan_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.m3_scan_prefill_noalloc.restype = ctypes.c_int
+    lib.m3_scan_prefill_noalloc.argtypes = [sp] + [vp] * 13
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.m3_decode_step_bf16_state.restype = ctypes.c_int

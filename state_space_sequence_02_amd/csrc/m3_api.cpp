@@ -379,6 +379,32 @@ m3_status m3_scan_prefill(const m3_shape* s,
                         kNoPro, y, h_out, workspace, workspace_bytes, stream);
 }
 
+m3_status m3_scan_prefill_noalloc(const m3_shape* s,
+                                  const void* x, const void* B, const void* C,
+                                  const float* dt, const float* A, const float* lam,
+                                  const float* theta,
+                                  const float* h0, const void* B_prev, const void* x_prev,
+                                  void* y, float* h_out, void* stream) {
+  static_assert(kNoAllocScratchBytes == (size_t)M3_NOALLOC_SCRATCH_BYTES, "scratch size");
+  m3_status st = check_common(s, true);
+  if (st != M3_OK) return st;
+  if ((size_t)s->batch * s->nheads == 0 || s->seqlen == 0)   // nothing to hand off between chunks
+    return m3_scan_prefill(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, y, h_out, nullptr, 0, stream);
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan, 0, 0)) return M3_ERR_SHAPE;
+  if (plan.bytes > kNoAllocScratchBytes) return M3_ERR_WORKSPACE;   // larger than the built-in scratch
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return M3_ERR_DEVICE;
+  // The buffer keeps the last call's contents: its control word, error word
+  // and flags must start at zero, so this call clears them (with a kernel, so
+  // that a captured call records no memset node).
+  if (launch_copy_or_zero(static_cast<float*>(ws), nullptr, plan.off_recs / sizeof(float),
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return M3_ERR_DEVICE;
+  return m3_scan_prefill(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, y, h_out, ws, kNoAllocScratchBytes,
+                         stream);
+}
+
 m3_status m3_scan_prefill_gated(const m3_shape* s,
                                 const void* x, const void* B, const void* C,
                                 const float* dt, const float* A, const float* lam,

@@ -125,6 +125,12 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
 
+// The device-resident prefill scratch of m3_scan_prefill_noalloc: its size
+// (M3_NOALLOC_SCRATCH_BYTES in m3.h) and its device address on the current
+// device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Copies (or zero-fills when src is NULL) `n` floats on the stream with a kernel
 // (no memset/memcpy nodes, so the call stays safe under graph capture).
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t stream);

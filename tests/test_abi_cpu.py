@@ -315,3 +315,18 @@ def test_chunk_request_is_exact(lib):
     assert m3.prefill_max_chunk(s(128, R=4, N=128)) == 64
     assert m3.prefill_chunk_used(s(0, R=4, N=128)) == 64          # 256 rows by default
     assert m3.prefill_chunk_used(s(0)) == 128                     # N <= 64: 128 rows by default
+
+
+def test_noalloc_rejects_oversize_shapes(lib):
+    """m3_scan_prefill_noalloc takes shapes whose workspace fits its 64 MiB
+    scratch and refuses larger ones with M3_ERR_WORKSPACE before touching the
+    device; invalid shapes get M3_ERR_SHAPE / M3_ERR_NULL as in m3_scan_prefill."""
+    big = m3.make_shape(4, 4096, 32, 64, 128, 4, 64, m3.M3_BF16)    # the MIMO workload: 8192 chunks
+    assert m3.prefill_workspace_bytes(big) > 64 << 20
+    args = [FAR[i] for i in range(10)] + [None, FAR[11], FAR[12], None]
+    a = lambda shape, **kw: lib.m3_scan_prefill_noalloc(ctypes.byref(shape), *args)
+    assert a(big) == 4
+    assert a(m3.make_shape(4, 4096, 32, 64, 128, 3, 64, m3.M3_BF16)) == 2      # R = 3
+    assert a(m3.make_shape(4, 4096, 32, 64, 128, 4, 128, m3.M3_BF16)) == 2     # 512-row chunk
+    small = m3.make_shape(1, 150, 2, 64, 128, 4, 32, m3.M3_BF16)
+    assert 0 < m3.prefill_workspace_bytes(small) <= 64 << 20
