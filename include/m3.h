@@ -321,6 +321,51 @@ m3_status m3_decode_step_prologue(const m3_shape* s, const m3_prologue* pro,
                                   const float* theta,
                                   void* y, void* stream);
 
+/* Bytes of device workspace m3_scan_backward needs for this shape (0 when it
+ * takes none): every state H_t of the forward pass, b x H x L x N x P fp32.
+ * The backward takes N = 16..128, P = 16..64, every R, fp32 or bf16 inputs,
+ * except the variants whose compiled kernels use scratch memory (R = 8 at the
+ * larger N x P); the call refuses those with M3_ERR_SHAPE. */
+size_t m3_scan_backward_workspace_bytes(const m3_shape* s);
+
+/* Gradients of the prefill (the recurrence of m3_scan_prefill): given the
+ * forward call's inputs and the cotangents dy of y and dh_out of h_out, the
+ * gradients of <dy, y> + <dh_out, h_out> with respect to every input.
+ * Defined by the recurrence itself (explainer panels 1, 3, 4; paper page,
+ * Table 1 caption), differentiated backwards through time as the explainer's
+ * training remark describes (a recurrence of the same form):
+ *   G_t = C_t dY_t^T + alpha_{t+1} R(phi_{t+1})^T G_{t+1},  Q_t = R(phi_t)^T G_t,
+ *   dV_t = gamma_t G_t + beta_{t+1} Q_{t+1},  dC_t = H_t dY_t,  dB_t = dV_t X_t,
+ *   dX_t = dV_t^T B_t,  dalpha_t = <Q_t, H_{t-1}>,  dbeta_t = <Q_t, V_{t-1}>,
+ *   dgamma_t = <G_t, V_t>, dphi_t[k] = sum_p (G_t[2k+1] K_t[2k] - G_t[2k] K_t[2k+1])
+ *   with K_t = H_t - gamma_t V_t, and the chain rule of alpha, beta, gamma into
+ * dt, lam and A.
+ *
+ *   inputs       as m3_scan_prefill (theta, h0, B_prev/x_prev may be NULL)
+ *   dy           [b, L, H, R, P]  dtype   cotangent of y
+ *   dh_out       [b, H, N, P]     fp32    cotangent of h_out, or NULL (zeros)
+ *   outputs, all fp32, written whole (not accumulated):
+ *   dx [b,L,H,R,P], dB, dC [b,L,H,R,N], ddt, dlam [b,L,H], dA [H],
+ *   dtheta [b,L,H,N/2]   (NULL exactly when theta is NULL)
+ *   dh0 [b,H,N,P]        or NULL (not computed; given h0 NULL it is the
+ *                        gradient with respect to a zero initial state)
+ *   dB_prev [b,H,R,N], dx_prev [b,H,R,P]  or NULL; must be NULL when B_prev is
+ *   workspace            at least m3_scan_backward_workspace_bytes(s); no
+ *                        contents required
+ * Errors: M3_ERR_NULL (a required pointer, or dtheta not matching theta),
+ * M3_ERR_SHAPE, M3_ERR_WORKSPACE, M3_ERR_ALIAS (an output overlapping an input,
+ * the workspace or another output).  Work runs on `stream`: one workgroup per
+ * (sequence, head) runs the recurrence forward storing every state, then
+ * backwards through time. */
+m3_status m3_scan_backward(const m3_shape* s,
+                           const void* x, const void* B, const void* C,
+                           const float* dt, const float* A, const float* lam, const float* theta,
+                           const float* h0, const void* B_prev, const void* x_prev,
+                           const void* dy, const float* dh_out,
+                           float* dx, float* dB, float* dC, float* ddt, float* dA, float* dlam,
+                           float* dtheta, float* dh0, float* dB_prev, float* dx_prev,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_str(m3_status st);
 

@@ -21,6 +21,7 @@ STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
 EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_prefill_max_chunk",
            "m3_prefill_gated_chunk_used", "m3_prefill_prologue_chunk_used", "m3_prefill_status",
            "m3_debug_set_spin_limit", "m3_scan_prefill", "m3_scan_prefill_noalloc",
+           "m3_scan_backward", "m3_scan_backward_workspace_bytes",
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
            "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
            "m3_status_str", "m3_version")
@@ -69,6 +70,10 @@ def load_library(path: str = LIB_PATH):
     lib.m3_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     lib.m3_scan_prefill.restype = ctypes.c_int
     lib.m3_scan_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.m3_scan_backward_workspace_bytes.restype = sz
+    lib.m3_scan_backward_workspace_bytes.argtypes = [sp]
+    lib.m3_scan_backward.restype = ctypes.c_int
+    lib.m3_scan_backward.argtypes = [sp] + [vp] * 23 + [sz, vp]
     lib.m3_scan_prefill_noalloc.restype = ctypes.c_int
     lib.m3_scan_prefill_noalloc.argtypes = [sp] + [vp] * 13
     lib.m3_decode_step.restype = ctypes.c_int
@@ -328,3 +333,48 @@ def decode_step(h, x, B, C, dt, A, lam, theta=None, B_prev=None, x_prev=None, y=
         _ptr(y, x.dtype, dev), _stream(dev))
     _check(code)
     return y
+
+
+def backward_workspace_bytes(shape: M3Shape) -> int:
+    return int(load_library().m3_scan_backward_workspace_bytes(ctypes.byref(shape)))
+
+
+def scan_backward(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
+                  dy=None, dh_out=None, workspace=None, want=("h0", "B_prev", "x_prev")) -> dict:
+    """Gradients of <dy, y> + <dh_out, h_out> for the prefill (m3_scan_backward).
+
+    Inputs as scan_prefill; dy [b,L,H,R,P] in x's dtype; dh_out [b,H,N,P] fp32
+    or None.  Returns a dict of fp32 gradients: x, B, C, dt, A, lam, theta (None
+    without theta), h0, B_prev, x_prev (computed when named in `want` and, for
+    the previous write, given).  The workspace (every forward state) is
+    allocated with torch when not given."""
+    lib = load_library()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    shape = make_shape(b, L, H, P, N, R, 0, _dtype_code(x))
+    need = int(lib.m3_scan_backward_workspace_bytes(ctypes.byref(shape)))
+    if need == 0:
+        raise M3Error(2, "the backward does not take this shape")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(x=torch.empty((b, L, H, R, P), **f32), B=torch.empty((b, L, H, R, N), **f32),
+             C=torch.empty((b, L, H, R, N), **f32), dt=torch.empty((b, L, H), **f32),
+             A=torch.empty((H,), **f32), lam=torch.empty((b, L, H), **f32),
+             theta=None if theta is None else torch.empty((b, L, H, N // 2), **f32),
+             h0=torch.empty((b, H, N, P), **f32) if "h0" in want else None,
+             B_prev=torch.empty((b, H, R, N), **f32) if ("B_prev" in want and B_prev is not None) else None,
+             x_prev=torch.empty((b, H, R, P), **f32) if ("x_prev" in want and B_prev is not None) else None)
+    f = torch.float32
+    code = lib.m3_scan_backward(
+        ctypes.byref(shape), _ptr(x, x.dtype, dev), _ptr(B, x.dtype, dev), _ptr(C, x.dtype, dev),
+        _ptr(dt, f, dev), _ptr(A, f, dev), _ptr(lam, f, dev), _ptr(theta, f, dev),
+        _ptr(h0, f, dev), _ptr(B_prev, x.dtype, dev), _ptr(x_prev, x.dtype, dev),
+        _ptr(dy, x.dtype, dev), _ptr(dh_out, f, dev),
+        _ptr(g["x"], f, dev), _ptr(g["B"], f, dev), _ptr(g["C"], f, dev), _ptr(g["dt"], f, dev),
+        _ptr(g["A"], f, dev), _ptr(g["lam"], f, dev), _ptr(g["theta"], f, dev), _ptr(g["h0"], f, dev),
+        _ptr(g["B_prev"], f, dev), _ptr(g["x_prev"], f, dev),
+        _ptr(workspace, None, dev), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code)
+    return g

@@ -77,6 +77,11 @@ int choose_chunk(const m3_shape& s, int gated, int pro) {
   return 0;
 }
 
+// The backward variants {dtype, N, P, R} that use scratch (build report).
+const int kBackwardScratch[][4] = {
+#include "m3_scratch_table_bwd.inc"
+    {-1, 0, 0, 0}};
+
 // The prefill variants that use scratch, from the build's compiler report:
 // {dtype, N, P, R, RT, gated, prologue} per line.
 const PrefillVariant kScratchVariants[] = {
@@ -377,6 +382,75 @@ m3_status m3_scan_prefill(const m3_shape* s,
                           void* stream) {
   return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{false, nullptr, nullptr, nullptr},
                         kNoPro, y, h_out, workspace, workspace_bytes, stream);
+}
+
+size_t m3_scan_backward_workspace_bytes(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  if (s->dstate > 128 || s->headdim > 64) return 0;
+  for (const auto& k : kBackwardScratch)
+    if (k[0] == s->dtype && k[1] == s->dstate && k[2] == s->headdim && k[3] == s->rank) return 0;
+  const size_t n = (size_t)s->batch * s->nheads * s->seqlen * s->dstate * s->headdim;
+  return std::max<size_t>(256, align256(n * sizeof(float)));
+}
+
+m3_status m3_scan_backward(const m3_shape* s,
+                           const void* x, const void* B, const void* C,
+                           const float* dt, const float* A, const float* lam, const float* theta,
+                           const float* h0, const void* B_prev, const void* x_prev,
+                           const void* dy, const float* dh_out,
+                           float* dx, float* dB, float* dC, float* ddt, float* dA, float* dlam,
+                           float* dtheta, float* dh0, float* dB_prev, float* dx_prev,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  m3_status st = check_common(s, true);
+  if (st != M3_OK) return st;
+  const int b = s->batch, L = s->seqlen, H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
+  if ((B_prev == nullptr) != (x_prev == nullptr)) return M3_ERR_NULL;
+  if (!B_prev && (dB_prev || dx_prev)) return M3_ERR_NULL;     // no previous write, no gradient of it
+  if ((theta == nullptr) != (dtheta == nullptr)) return M3_ERR_NULL;
+  const size_t need = m3_scan_backward_workspace_bytes(s);
+  if (need == 0) return M3_ERR_SHAPE;
+  const size_t bh = (size_t)b * H, tok = bh * L;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (bh == 0) return M3_OK;
+  if (!A || !dA) return M3_ERR_NULL;
+  if (L > 0 && (!x || !B || !C || !dt || !lam || !dy || !dx || !dB || !dC || !ddt || !dlam))
+    return M3_ERR_NULL;
+  if (L > 0 && (!workspace || workspace_bytes < need)) return M3_ERR_WORKSPACE;
+  const size_t es = esize(s->dtype);
+  const size_t sbytes = bh * N * P * sizeof(float);
+  struct Buf { const void* p; size_t n; };
+  const Buf ins[] = {{x, tok * R * P * es}, {B, tok * R * N * es}, {C, tok * R * N * es},
+                     {dt, tok * 4}, {A, (size_t)H * 4}, {lam, tok * 4}, {theta, theta ? tok * (N / 2) * 4 : 0},
+                     {h0, h0 ? sbytes : 0}, {B_prev, B_prev ? bh * R * N * es : 0},
+                     {x_prev, x_prev ? bh * R * P * es : 0}, {dy, tok * R * P * es}, {dh_out, dh_out ? sbytes : 0},
+                     {workspace, L > 0 ? need : 0}};
+  const Buf outs[] = {{dx, tok * R * P * 4}, {dB, tok * R * N * 4}, {dC, tok * R * N * 4}, {ddt, tok * 4},
+                      {dA, (size_t)H * 4}, {dlam, tok * 4}, {dtheta, dtheta ? tok * (N / 2) * 4 : 0},
+                      {dh0, dh0 ? sbytes : 0}, {dB_prev, dB_prev ? bh * R * N * 4 : 0},
+                      {dx_prev, dx_prev ? bh * R * P * 4 : 0}};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Buf& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return M3_ERR_ALIAS;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return M3_ERR_ALIAS;
+  }
+  // dA is a sum over the batch and the tokens: start it at zero (a kernel)
+  if (launch_copy_or_zero(dA, nullptr, (size_t)H, hs) != hipSuccess) return M3_ERR_DEVICE;
+  if (L == 0) {   // nothing between the incoming state and h_out: dh0 = dh_out
+    if (dh0 && launch_copy_or_zero(dh0, dh_out, bh * N * P, hs) != hipSuccess) return M3_ERR_DEVICE;
+    if (dB_prev && launch_copy_or_zero(dB_prev, nullptr, bh * R * N, hs) != hipSuccess) return M3_ERR_DEVICE;
+    if (dx_prev && launch_copy_or_zero(dx_prev, nullptr, bh * R * P, hs) != hipSuccess) return M3_ERR_DEVICE;
+    return M3_OK;
+  }
+  BackwardParams p;
+  p.x = x; p.B = B; p.C = C; p.dt = dt; p.A = A; p.lam = lam; p.theta = theta;
+  p.h0 = h0; p.Bp = B_prev; p.xp = x_prev; p.dy = dy; p.dh = dh_out;
+  p.dx = dx; p.dB = dB; p.dC = dC; p.ddt = ddt; p.dA = dA; p.dlam = dlam; p.dtheta = dtheta;
+  p.dh0 = dh0; p.dBp = dB_prev; p.dxp = dx_prev;
+  p.hs = static_cast<float*>(workspace);
+  p.batch = b; p.L = L; p.H = H;
+  if (launch_backward(p, s->dtype, N, P, R, hs) != hipSuccess) return M3_ERR_DEVICE;
+  return M3_OK;
 }
 
 m3_status m3_scan_prefill_noalloc(const m3_shape* s,

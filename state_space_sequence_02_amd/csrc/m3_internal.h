@@ -125,6 +125,22 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
 
+// Backward (m3_backward.hip): inputs of the forward call, the cotangents dy
+// [b,L,H,R,P] (input dtype) and dh [b,H,N,P] (fp32 or NULL), the fp32
+// gradients (dtheta / dh0 / dBp / dxp may be NULL: not computed; dA must be
+// zero on entry: workgroups add into it), and the workspace of every state.
+struct BackwardParams {
+  const void* x; const void* B; const void* C;
+  const float* dt; const float* A; const float* lam; const float* theta;
+  const float* h0; const void* Bp; const void* xp;
+  const void* dy; const float* dh;
+  float* dx; float* dB; float* dC; float* ddt; float* dA; float* dlam; float* dtheta;
+  float* dh0; float* dBp; float* dxp;
+  float* hs;                    // H_t for every t, [b, H, L, N, P] fp32
+  int batch, L, H;
+};
+hipError_t launch_backward(const BackwardParams& p, int dtype, int N, int P, int R, hipStream_t stream);
+
 // The device-resident prefill scratch of m3_scan_prefill_noalloc: its size
 // (M3_NOALLOC_SCRATCH_BYTES in m3.h) and its device address on the current
 // device (looked up once per device).

@@ -330,3 +330,27 @@ def test_noalloc_rejects_oversize_shapes(lib):
     assert a(m3.make_shape(4, 4096, 32, 64, 128, 4, 128, m3.M3_BF16)) == 2     # 512-row chunk
     small = m3.make_shape(1, 150, 2, 64, 128, 4, 32, m3.M3_BF16)
     assert 0 < m3.prefill_workspace_bytes(small) <= 64 << 20
+
+
+def test_backward_validation_codes(lib):
+    """m3_scan_backward checks its arguments on the host before any launch."""
+    ok = m3.make_shape(2, 64, 3, 64, 128, 4, 0, m3.M3_BF16)
+    assert lib.m3_scan_backward_workspace_bytes(ctypes.byref(ok)) == 2 * 3 * 64 * 128 * 64 * 4
+    assert lib.m3_scan_backward_workspace_bytes(ctypes.byref(m3.make_shape(2, 64, 3, 128, 128, 4, 0, 1))) == 0
+    assert lib.m3_scan_backward_workspace_bytes(ctypes.byref(m3.make_shape(2, 64, 3, 64, 256, 4, 0, 1))) == 0
+
+    def call(shape, **over):
+        a = dict(x=FAR[0], B=FAR[1], C=FAR[2], dt=FAR[3], A=FAR[4], lam=FAR[5], theta=FAR[6], h0=None,
+                 Bp=None, xp=None, dy=FAR[7], dh=None, dx=FAR[8], dB=FAR[9], dC=FAR[10], ddt=FAR[11],
+                 dA=FAR[12], dlam=FAR[13], dth=FAR[14], dh0=None, dBp=None, dxp=None, ws=FAR[15], wsb=1 << 40)
+        a.update(over)
+        return lib.m3_scan_backward(ctypes.byref(shape), *a.values(), None)
+
+    assert call(ok, theta=None) == 1                       # dtheta given without theta
+    assert call(ok, dBp=FAR[16]) == 1                      # dB_prev without B_prev
+    assert call(ok, dx=None) == 1
+    assert call(ok, ws=None) == 4
+    assert call(ok, wsb=1000) == 4
+    assert call(ok, dx=FAR[0]) == 6                        # dx aliases x
+    assert call(ok, dC=FAR[9] + 64) == 6                   # two outputs overlap
+    assert call(m3.make_shape(2, 64, 3, 64, 128, 3, 0, 1)) == 2   # R = 3

@@ -1,0 +1,110 @@
+"""GPU parity of the backward (m3_scan_backward) against the float64 backward
+oracle (oracle/backward.py, pinned on the CPU by finite differences of the
+forward oracle and exact adjoint identities): every gradient, both input
+dtypes, with and without rotation and incoming state, ranks 1-8, L = 1 and an
+empty sequence."""
+import numpy as np
+import pytest
+import torch
+
+import state_space_sequence_02_amd as m3
+from oracle.backward import scan_vjp
+from state_space_sequence_02_amd import inputs
+
+from _parity import TOL, check_blocks, dev_inputs, note, to64
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("x", "B", "C", "dt", "A", "lam", "theta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m3.load_library()
+
+
+def _case(w, seed, carry=True, rotation=True, dh=True):
+    d = inputs.make_prefill_inputs(w, seed=seed)
+    if not rotation:
+        d["theta"] = None
+    c = inputs.random_carry(w, seed=seed + 1) if carry else {}
+    g = torch.Generator().manual_seed(seed + 2)
+    dy = torch.randn(d["x"].shape, generator=g).to(d["x"].dtype)
+    dho = torch.randn((w.batch, w.nheads, w.dstate, w.headdim), generator=g) if dh else None
+    return d, c, dy, dho
+
+
+def _check(w, d, c, dy, dho, got):
+    n = lambda t: None if t is None else t.double().numpy()
+    ref = scan_vjp(**{k: n(v) for k, v in d.items()}, h0=n(c.get("h0")), B_prev=n(c.get("B_prev")),
+                   x_prev=n(c.get("x_prev")), dy=n(dy), dh_out=n(dho))
+    tol = TOL[w.dtype]
+    check_blocks(to64(got["x"]), ref["x"], tol, (1, 3, 4), "dx")
+    check_blocks(to64(got["B"]), ref["B"], tol, (1, 3, 4), "dB")
+    check_blocks(to64(got["C"]), ref["C"], tol, (1, 3, 4), "dC")
+    check_blocks(to64(got["dt"]), ref["dt"], tol, (1,), "ddt")
+    check_blocks(to64(got["lam"]), ref["lam"], tol, (1,), "dlam")
+    np.testing.assert_allclose(to64(got["A"]), ref["A"], rtol=tol, atol=tol * np.abs(ref["A"]).max())
+    if d["theta"] is not None:
+        check_blocks(to64(got["theta"]), ref["theta"], tol, (1, 3), "dtheta")
+    else:
+        assert got["theta"] is None
+    check_blocks(to64(got["h0"]), ref["h0"] if ref["h0"] is not None else _dh0_zero_state(d, c, dy, dho),
+                 tol, (2, 3), "dh0")
+    if c:
+        check_blocks(to64(got["B_prev"]), ref["B_prev"], tol, (2, 3), "dB_prev")
+        check_blocks(to64(got["x_prev"]), ref["x_prev"], tol, (2, 3), "dx_prev")
+
+
+def _dh0_zero_state(d, c, dy, dho):
+    """The oracle's gradient with respect to a zero incoming state."""
+    n = lambda t: None if t is None else t.double().numpy()
+    b, L, H, R, P = d["x"].shape
+    N = d["B"].shape[-1]
+    return scan_vjp(**{k: n(v) for k, v in d.items()}, h0=np.zeros((b, H, N, P)), dy=n(dy),
+                    dh_out=n(dho))["h0"]
+
+
+CASES = [
+    ("tiny", dict(), True, True),
+    ("tiny", dict(seqlen=37, batch=2, nheads=3, headdim=32, dstate=32, rank=2), True, True),
+    ("siso", dict(batch=2, seqlen=90, nheads=2), True, True),
+    ("siso", dict(batch=1, seqlen=70, nheads=2), False, True),
+    ("mimo", dict(batch=1, seqlen=60, nheads=2), True, True),
+    ("mimo", dict(batch=2, seqlen=33, nheads=1), True, False),
+    ("mimo", dict(batch=1, seqlen=40, nheads=2, headdim=16, dstate=32, rank=8), True, True),
+    ("tiny", dict(batch=1, seqlen=50, nheads=2, headdim=64, dstate=128, rank=4), True, True),   # fp32
+    ("mimo", dict(batch=1, seqlen=1, nheads=3), True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}-carry{int(c[2])}-rot{int(c[3])}")
+def test_backward_matches_oracle(case):
+    name, kw, carry, rotation = case
+    w = inputs.workload(name, **kw)
+    d, c, dy, dho = _case(w, seed=5000 + w.seqlen + w.rank, carry=carry, rotation=rotation)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note(f"backward {name} {kw} {w.dtype} carry={carry} rotation={rotation}")
+    got = m3.scan_backward(**{k: dg[k] for k in KEYS}, **cg, dy=dy.cuda(),
+                           dh_out=None if dho is None else dho.cuda())
+    torch.cuda.synchronize()
+    _check(w, d, c, dy, dho, got)
+
+
+def test_backward_without_dh_and_empty_sequence():
+    w = inputs.workload("mimo", batch=2, seqlen=45, nheads=2)
+    d, c, dy, _ = _case(w, seed=5101, dh=False)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note("backward without dh_out")
+    got = m3.scan_backward(**{k: dg[k] for k in KEYS}, **cg, dy=dy.cuda())
+    torch.cuda.synchronize()
+    _check(w, d, c, dy, None, got)
+    note("backward of an empty sequence")
+    w0 = inputs.workload("mimo", batch=2, seqlen=0, nheads=2)
+    d0 = dev_inputs(inputs.make_prefill_inputs(w0, seed=5102))
+    dho = torch.randn((2, 2, w0.dstate, w0.headdim), device="cuda")
+    g0 = m3.scan_backward(**{k: d0[k] for k in KEYS}, **cg, dy=torch.empty_like(d0["x"]), dh_out=dho)
+    torch.cuda.synchronize()
+    assert torch.equal(g0["h0"], dho) and not g0["A"].any() and not g0["B_prev"].any()
