@@ -77,6 +77,43 @@ def prefill_flops_per_token_head(w, q) -> float:
     return (q + 1) * R * R * (N + P) + 4 * N * P * R
 
 
+def backward_bytes_per_token_head(w) -> int:
+    """Algorithmic bytes of the backward: the forward inputs and dy read once,
+    every gradient (fp32) written once.  The stored forward states (the
+    workspace) are the implementation's, not counted."""
+    es, R, N, P = esize(w), w.rank, w.dstate, w.headdim
+    rot = (N // 2) * 4 if w.rotation else 0
+    reads = R * P * es + 2 * R * N * es + 8 + rot + R * P * es
+    writes = R * P * 4 + 2 * R * N * 4 + 8 + rot
+    return reads + writes
+
+
+def bench_backward(w, steps, warmup, reps=1):
+    """One step = one m3_scan_backward over the whole layer (all heads), from
+    seeded inputs and cotangents resident on the device."""
+    dev = torch.device("cuda")
+    d = inputs.make_prefill_inputs(w, seed=0, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(91)
+    dy = torch.randn(d["x"].shape, generator=g, device=dev).to(d["x"].dtype)
+    dh = torch.randn((w.batch, w.nheads, w.dstate, w.headdim), generator=g, device=dev)
+    dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0, dcode)
+    ws = torch.empty(m3.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        m3.scan_backward(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dy=dy, dh_out=dh,
+                         workspace=ws)
+
+    r = _timed(step, steps, warmup, reps)
+    tok = w.batch * w.seqlen
+    nbytes = tok * w.nheads * backward_bytes_per_token_head(w) + w.batch * w.nheads * w.dstate * w.headdim * 8
+    del d, ws
+    return dict(r, tokens_per_s=tok / (r["ms"] * 1e-3), bytes=nbytes,
+                gbs_launch=nbytes / (r["ms_launch"] * 1e-3) / 1e9,
+                workspace_bytes=m3.backward_workspace_bytes(shape))
+
+
 def decode_bytes_per_update(w, state_bytes=4) -> int:
     es, R, N, P = esize(w), w.rank, w.dstate, w.headdim
     return (2 * N * P * state_bytes + R * P * es + 2 * R * N * es + R * N * es + R * P * es + 8 + (N // 2) * 4
@@ -504,6 +541,16 @@ def main():
         sec["siso_prefill_prologue"] = dict(prefill_line(ws_, pf), us_unfused_torch_prologue=round(pt["ms"] * 1e3, 1))
         rp = bench_decode(wd, 200, 30, prologue=True)
         sec["mimo_decode_prologue"] = decode_line(wd, rp)
+        # the backward of the recurrence (every gradient), at the SISO and MIMO
+        # prefill shapes
+        for name in ("siso", "mimo"):
+            wl = inputs.WORKLOADS[name]
+            rb = bench_backward(wl, 3, 1)
+            sec[f"{name}_backward"] = dict(tokens_per_s_layer=rb["tokens_per_s"], us=round(rb["ms"] * 1e3, 1),
+                                           us_per_launch=round(rb["ms_launch"] * 1e3, 1),
+                                           hbm_frac=round(rb["gbs_launch"] / HBM_PEAK_GBS, 4),
+                                           algorithmic_bytes_per_launch=rb["bytes"],
+                                           workspace_bytes=rb["workspace_bytes"])
         out["secondary"] = sec
     if not args.no_cpu_baseline:
         base = {}
