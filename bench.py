@@ -114,6 +114,24 @@ def bench_backward(w, steps, warmup, reps=1):
                 workspace_bytes=m3.backward_workspace_bytes(shape))
 
 
+def bench_copy(nbytes, steps=200, warmup=30):
+    """A plain device-to-device copy of `nbytes` (read once, written once) by
+    torch, three buffer pairs in rotation: what streaming the decode's state
+    costs with no arithmetic, as a practical ceiling beside the 8 TB/s peak."""
+    n = nbytes // 4
+    bufs = [(torch.randn(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(3)]
+
+    def step(i):
+        dst, src = bufs[i % 3][1], bufs[i % 3][0]
+        dst.copy_(src)
+
+    r = _timed(step, steps, warmup)
+    del bufs
+    return dict(us_per_launch=round(r["ms_launch"] * 1e3, 2), bytes_moved=2 * nbytes,
+                gbs=round(2 * nbytes / (r["ms_launch"] * 1e-3) / 1e9, 1),
+                hbm_frac=round(2 * nbytes / (r["ms_launch"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def decode_bytes_per_update(w, state_bytes=4) -> int:
     es, R, N, P = esize(w), w.rank, w.dstate, w.headdim
     return (2 * N * P * state_bytes + R * P * es + 2 * R * N * es + R * N * es + R * P * es + 8 + (N // 2) * 4
@@ -518,6 +536,10 @@ def main():
         dec("mimo_decode_n64", dstate=64)
         dec("siso_decode_n128", rank=1)
         dec("siso_decode_n64", rank=1, dstate=64)
+        # torch's device copy of the decode states' bytes (N=64 fp32 or N=128
+        # bf16: 64 MiB; N=128 fp32: 128 MiB), read once and written once
+        sec["device_copy_64MiB"] = bench_copy(64 << 20)
+        sec["device_copy_128MiB"] = bench_copy(128 << 20)
         # the gated readout (rank contraction + rank-expanded SiLU gate) fused
         # into the kernels, and the prefill's unfused alternative
         wm = inputs.WORKLOADS["mimo"]
