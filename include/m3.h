@@ -322,7 +322,9 @@ m3_status m3_decode_step_prologue(const m3_shape* s, const m3_prologue* pro,
                                   void* y, void* stream);
 
 /* Bytes of device workspace m3_scan_backward needs for this shape (0 when it
- * takes none): every state H_t of the forward pass, b x H x L x N x P fp32.
+ * takes none): every state H_t of the forward pass (b x H x L x N x P fp32),
+ * then, per segment of the sequence (16..256 tokens, chosen from L and b x H),
+ * two N x P fp32 hand-off arrays and two N/2 complex propagators.
  * The backward takes N = 16..128, P = 16..64, every R, fp32 or bf16 inputs,
  * except the variants whose compiled kernels use scratch memory (R = 8 at the
  * larger N x P); the call refuses those with M3_ERR_SHAPE. */
@@ -354,9 +356,11 @@ size_t m3_scan_backward_workspace_bytes(const m3_shape* s);
  *                        contents required
  * Errors: M3_ERR_NULL (a required pointer, or dtheta not matching theta),
  * M3_ERR_SHAPE, M3_ERR_WORKSPACE, M3_ERR_ALIAS (an output overlapping an input,
- * the workspace or another output).  Work runs on `stream`: one workgroup per
- * (sequence, head) runs the recurrence forward storing every state, then
- * backwards through time. */
+ * the workspace or another output).  Work runs on `stream` in six launches:
+ * each segment of each (sequence, head) runs forward from a zero state, a
+ * short pass per (sequence, head) composes the segments' states, the segments
+ * run again from their true entering states storing every state, and the same
+ * three steps run backwards through time for the gradient of the state. */
 m3_status m3_scan_backward(const m3_shape* s,
                            const void* x, const void* B, const void* C,
                            const float* dt, const float* A, const float* lam, const float* theta,

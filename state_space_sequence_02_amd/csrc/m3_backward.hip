@@ -13,17 +13,26 @@
 //   d h0 = alpha_0 Q_0,  dV_{-1} = beta_0 Q_0 (-> d B_prev, d x_prev)
 // and the coefficients' chain rule into dt, lam and A.
 //
-// Two launches, one workgroup per (sequence, head), time sequential:
-//  1. states_kernel runs the recurrence forward and stores every H_t (fp32) in
-//     the workspace [b, H, L, N, P];
-//  2. grads_kernel runs t = L-1..0 with G carried in registers, reading H_t
-//     and H_{t-1} back from the workspace.
-// A unit is (row pair k, quad q: columns 4q..4q+3), as in the decode step, so a
-// state row moves as whole 16-byte runs and the pair's rotation is
-// lane-local.  The pair's QP = P/4 quads sit in consecutive lanes: sums over
-// the head columns (dC, dB, d phi) are xor shuffles within those lanes, sums
-// over the state rows (dX) and over everything (d alpha, d beta, d gamma) add
-// the lanes of one quad, then the waves through LDS (one barrier per step).
+// Segment-parallel.  The transition alpha_t R(phi_t) is one complex scalar per
+// row pair, so over a segment of S tokens each direction is a local result
+// plus a per-pair propagator times what enters from outside:
+//   forward:  H_{s1} = U_j + [prod_{t=s0..s1} alpha_t R(phi_t)] H_{s0-1}
+//   backward: G_{s0} = G~_j + [prod_{t=s0+1..s1+1} alpha_t R(phi_t)^T] G_{s1+1}
+// (U_j, G~_j: the segment's own result with zero entering).  Six launches:
+//  1. fwd_maps_kernel   per (segment, sequence, head): U_j and its propagator;
+//  2. fwd_combine_kernel per (sequence, head), over the segments in order: the
+//     state entering each segment;
+//  3. states_kernel     per segment: the recurrence from its entering state,
+//     storing every H_t (fp32) in the workspace [b, H, L, N, P];
+//  4. bwd_maps_kernel   per segment: G~_j and its propagator;
+//  5. bwd_combine_kernel per (sequence, head), over the segments in reverse: the
+//     G entering each segment from the right;
+//  6. grads_kernel      per segment: t = s1..s0 with G carried in registers from
+//     the entering G, reading H_t back from the workspace, writing every
+//     gradient of the segment's tokens (the first segment also d h0, d B_prev,
+//     d x_prev; every segment adds its part of dA with one atomic).
+// The propagators are accumulated step by step as complex products (unit
+// rotations times decays), not from summed angles.
 #include "m3_device.h"
 
 namespace m3 {
@@ -77,38 +86,80 @@ __device__ __forceinline__ void vwrite(const float2 (&b)[R], const float4 (&xq)[
   }
 }
 
+// Segment j of work item blockIdx.x = j * (b*H) + (sequence, head).
+struct Seg {
+  int j, bh, b, h, s0, s1;
+};
+__device__ __forceinline__ Seg segment_of(const BackwardParams& p) {
+  Seg g;
+  const int nbh = p.batch * p.H;
+  g.j = blockIdx.x / nbh;
+  g.bh = blockIdx.x - g.j * nbh;
+  g.b = g.bh / p.H;
+  g.h = g.bh - g.b * p.H;
+  g.s0 = g.j * p.S;
+  g.s1 = min(p.L, g.s0 + p.S) - 1;
+  return g;
+}
+
+// The write of the token before s0 (B_prev / x_prev, or zeros, before token 0)
+// for the unit's pair k and quad q.
 template <typename T, int N, int P, int R>
-__global__ __launch_bounds__(bwd_threads(N, P)) void states_kernel(BackwardParams p) {
+__device__ __forceinline__ void prev_write(const BackwardParams& p, const Seg& g, size_t tok0, int k, int q,
+                                           float4& v0, float4& v1) {
+  const T* Bm = g.s0 > 0 ? static_cast<const T*>(p.B) + (tok0 + (size_t)(g.s0 - 1) * p.H) * R * N
+                         : (p.Bp ? static_cast<const T*>(p.Bp) + (size_t)g.bh * R * N : nullptr);
+  const T* Xm = g.s0 > 0 ? static_cast<const T*>(p.x) + (tok0 + (size_t)(g.s0 - 1) * p.H) * R * P
+                         : (p.xp ? static_cast<const T*>(p.xp) + (size_t)g.bh * R * P : nullptr);
+  float4 xq[R];
+  float2 bq[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    xq[r] = Xm ? ld4(Xm + r * P + 4 * q) : f4(0.f);
+    bq[r] = Bm ? ld2(Bm + r * N + 2 * k) : make_float2(0.f, 0.f);
+  }
+  vwrite<R>(bq, xq, v0, v1);
+}
+
+// One forward step of a unit: H <- R(phi)[alpha H + beta V_prev] + gamma V_t.
+template <typename T, int N, int P, int R>
+__device__ __forceinline__ void fwd_step(const T* Bt, const float4 (&xq)[R], int k, float al, float be, float ga,
+                                         float c, float s, float4& H0, float4& H1, float4& V0, float4& V1) {
+  float2 bq[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) bq[r] = ld2(Bt + r * N + 2 * k);
+  float4 w0, w1;
+  vwrite<R>(bq, xq, w0, w1);
+  float4 m0 = fma4(be, V0, mul4(al, H0)), m1 = fma4(be, V1, mul4(al, H1));
+  rot(c, s, m0, m1);
+  H0 = fma4(ga, w0, m0);
+  H1 = fma4(ga, w1, m1);
+  V0 = w0;
+  V1 = w1;
+}
+
+// 1. The segment's end state from a zero entering state (its previous write
+// included) and the product of its alpha_t R(phi_t) per pair.
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(bwd_threads(N, P)) void fwd_maps_kernel(BackwardParams p) {
   constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
   constexpr int UPT = (UNITS + NT - 1) / NT;
-  const int bh = blockIdx.x, b = bh / p.H, h = bh - b * p.H;
+  const Seg g = segment_of(p);
   const int tid = threadIdx.x, q = tid % QP;
-  const int L = p.L;
-  const size_t tstep = (size_t)p.H;                    // token step of [b, L, H] arrays
-  const size_t tok0 = (size_t)b * L * p.H + h;         // token 0 of this sequence and head
-  const float Ah = p.A[h];
+  const size_t tok0 = (size_t)g.b * p.L * p.H + g.h;
+  const float Ah = p.A[g.h];
   float4 H0[UPT], H1[UPT], V0[UPT], V1[UPT];
-  // incoming state and previous write
-  {
-    const T* Bp = p.Bp ? static_cast<const T*>(p.Bp) + (size_t)bh * R * N : nullptr;
-    const T* Xp = p.xp ? static_cast<const T*>(p.xp) + (size_t)bh * R * P : nullptr;
-    float4 xq[R];
+  float zr[UPT], zi[UPT];
 #pragma unroll
-    for (int r = 0; r < R; ++r) xq[r] = Xp ? ld4(Xp + r * P + 4 * q) : f4(0.f);
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * NT, k = (u < UNITS ? u : 0) / QP;
-      H0[i] = p.h0 ? ld4(p.h0 + ((size_t)bh * N + 2 * k) * P + 4 * q) : f4(0.f);
-      H1[i] = p.h0 ? ld4(p.h0 + ((size_t)bh * N + 2 * k + 1) * P + 4 * q) : f4(0.f);
-      float2 bq[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) bq[r] = Bp ? ld2(Bp + r * N + 2 * k) : make_float2(0.f, 0.f);
-      vwrite<R>(bq, xq, V0[i], V1[i]);
-    }
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT, k = (u < UNITS ? u : 0) / QP;
+    H0[i] = H1[i] = f4(0.f);
+    prev_write<T, N, P, R>(p, g, tok0, k, q, V0[i], V1[i]);
+    zr[i] = 1.f;
+    zi[i] = 0.f;
   }
-  float* hs = p.hs + (size_t)bh * L * N * P;
-  for (int t = 0; t < L; ++t) {
-    const size_t tok = tok0 + (size_t)t * tstep;
+  for (int t = g.s0; t <= g.s1; ++t) {
+    const size_t tok = tok0 + (size_t)t * p.H;
     const float d = p.dt[tok], lm = p.lam[tok];
     const float al = __expf(d * Ah), be = (1.f - lm) * d * al, ga = lm * d;
     const T* Bt = static_cast<const T*>(p.B) + tok * R * N;
@@ -121,24 +172,208 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void states_kernel(BackwardParam
       const int u = tid + i * NT;
       if (u >= UNITS) continue;
       const int k = u / QP;
-      float2 bq[R];
+      float c = 1.f, sn = 0.f;
+      if (p.theta) __sincosf(p.theta[tok * (N / 2) + k], &sn, &c);
+      fwd_step<T, N, P, R>(Bt, xq, k, al, be, ga, c, sn, H0[i], H1[i], V0[i], V1[i]);
+      const float r0 = zr[i];
+      zr[i] = al * (r0 * c - zi[i] * sn);
+      zi[i] = al * (r0 * sn + zi[i] * c);
+    }
+  }
+  const size_t slot = (size_t)g.bh * p.nseg + g.j;
 #pragma unroll
-      for (int r = 0; r < R; ++r) bq[r] = ld2(Bt + r * N + 2 * k);
-      float4 w0, w1;
-      vwrite<R>(bq, xq, w0, w1);
-      float4 m0 = fma4(be, V0[i], mul4(al, H0[i])), m1 = fma4(be, V1[i], mul4(al, H1[i]));
-      if (p.theta) {
-        float s, c;
-        __sincosf(p.theta[tok * (N / 2) + k], &s, &c);
-        rot(c, s, m0, m1);
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    if (u >= UNITS) continue;
+    const int k = u / QP;
+    float* row = p.sega + (slot * N + 2 * k) * P + 4 * q;
+    *reinterpret_cast<float4*>(row) = H0[i];
+    *reinterpret_cast<float4*>(row + P) = H1[i];
+    if (q == 0) *reinterpret_cast<float2*>(p.zf + (slot * (N / 2) + k) * 2) = make_float2(zr[i], zi[i]);
+  }
+}
+
+// 2. The state entering each segment, segment by segment:
+//   S_{-1} = h0 (or 0),  entering_j = S_{j-1},  S_j = z_j S_{j-1} + U_j.
+template <int N, int P>
+__global__ __launch_bounds__(bwd_threads(N, P)) void fwd_combine_kernel(BackwardParams p) {
+  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
+  constexpr int UPT = (UNITS + NT - 1) / NT;
+  const int bh = blockIdx.x, tid = threadIdx.x, q = tid % QP;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    if (u >= UNITS) continue;
+    const int k = u / QP;
+    const size_t r0 = (size_t)(2 * k) * P + 4 * q;
+    float4 S0 = p.h0 ? ld4(p.h0 + (size_t)bh * N * P + r0) : f4(0.f);
+    float4 S1 = p.h0 ? ld4(p.h0 + (size_t)bh * N * P + r0 + P) : f4(0.f);
+    for (int j = 0; j < p.nseg; ++j) {
+      const size_t slot = (size_t)bh * p.nseg + j;
+      float* e = p.segb + slot * N * P + r0;
+      *reinterpret_cast<float4*>(e) = S0;
+      *reinterpret_cast<float4*>(e + P) = S1;
+      if (j + 1 < p.nseg) {
+        const float2 z = *reinterpret_cast<const float2*>(p.zf + (slot * (N / 2) + k) * 2);
+        const float* U = p.sega + slot * N * P + r0;
+        rot(z.x, z.y, S0, S1);
+        S0 = addv(S0, ld4(U));
+        S1 = addv(S1, ld4(U + P));
       }
-      H0[i] = fma4(ga, w0, m0);
-      H1[i] = fma4(ga, w1, m1);
-      V0[i] = w0;
-      V1[i] = w1;
+    }
+  }
+}
+
+// 3. The recurrence over the segment from its entering state, every H_t stored.
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(bwd_threads(N, P)) void states_kernel(BackwardParams p) {
+  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
+  constexpr int UPT = (UNITS + NT - 1) / NT;
+  const Seg g = segment_of(p);
+  const int tid = threadIdx.x, q = tid % QP;
+  const size_t tok0 = (size_t)g.b * p.L * p.H + g.h;
+  const float Ah = p.A[g.h];
+  const size_t slot = (size_t)g.bh * p.nseg + g.j;
+  float4 H0[UPT], H1[UPT], V0[UPT], V1[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT, k = (u < UNITS ? u : 0) / QP;
+    const float* e = p.segb + (slot * N + 2 * k) * P + 4 * q;
+    H0[i] = ld4(e);
+    H1[i] = ld4(e + P);
+    prev_write<T, N, P, R>(p, g, tok0, k, q, V0[i], V1[i]);
+  }
+  float* hs = p.hs + (size_t)g.bh * p.L * N * P;
+  for (int t = g.s0; t <= g.s1; ++t) {
+    const size_t tok = tok0 + (size_t)t * p.H;
+    const float d = p.dt[tok], lm = p.lam[tok];
+    const float al = __expf(d * Ah), be = (1.f - lm) * d * al, ga = lm * d;
+    const T* Bt = static_cast<const T*>(p.B) + tok * R * N;
+    const T* Xt = static_cast<const T*>(p.x) + tok * R * P;
+    float4 xq[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xq[r] = ld4(Xt + r * P + 4 * q);
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      if (u >= UNITS) continue;
+      const int k = u / QP;
+      float c = 1.f, sn = 0.f;
+      if (p.theta) __sincosf(p.theta[tok * (N / 2) + k], &sn, &c);
+      fwd_step<T, N, P, R>(Bt, xq, k, al, be, ga, c, sn, H0[i], H1[i], V0[i], V1[i]);
       float* row = hs + ((size_t)t * N + 2 * k) * P + 4 * q;
       *reinterpret_cast<float4*>(row) = H0[i];
       *reinterpret_cast<float4*>(row + P) = H1[i];
+    }
+  }
+}
+
+// 4. The segment's G at its first token from a zero G entering at its end (the
+// last segment starts from dh_out), and the product of alpha_u R(phi_u)^T,
+// u = s0+1 .. s1+1, per pair.
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(bwd_threads(N, P)) void bwd_maps_kernel(BackwardParams p) {
+  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
+  constexpr int UPT = (UNITS + NT - 1) / NT;
+  const Seg g = segment_of(p);
+  const int tid = threadIdx.x, q = tid % QP;
+  const size_t tok0 = (size_t)g.b * p.L * p.H + g.h;
+  const float Ah = p.A[g.h];
+  const bool last = g.j == p.nseg - 1;
+  float4 G0[UPT], G1[UPT];
+  float wr[UPT], wi[UPT];
+  // coefficients of the token after the segment (none after the last token)
+  float a_n = 1.f;
+  const bool next = g.s1 + 1 < p.L;
+  const size_t tokn = tok0 + (size_t)(next ? g.s1 + 1 : g.s1) * p.H;
+  if (next) a_n = __expf(p.dt[tokn] * Ah);
+  float cn[UPT], sn[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT, k = (u < UNITS ? u : 0) / QP;
+    G0[i] = G1[i] = f4(0.f);
+    if (last && p.dh) {
+      G0[i] = ld4(p.dh + ((size_t)g.bh * N + 2 * k) * P + 4 * q);
+      G1[i] = ld4(p.dh + ((size_t)g.bh * N + 2 * k + 1) * P + 4 * q);
+    }
+    cn[i] = 1.f;
+    sn[i] = 0.f;
+    if (next && p.theta) __sincosf(p.theta[tokn * (N / 2) + k], &sn[i], &cn[i]);
+    wr[i] = 1.f;
+    wi[i] = 0.f;
+  }
+  for (int t = g.s1; t >= g.s0; --t) {
+    const size_t tok = tok0 + (size_t)t * p.H;
+    const T* Ct = static_cast<const T*>(p.C) + tok * R * N;
+    const T* dYt = static_cast<const T*>(p.dy) + tok * R * P;
+    float4 dyq[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) dyq[r] = ld4(dYt + r * P + 4 * q);
+    const float al = __expf(p.dt[tok] * Ah);
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      if (u >= UNITS) continue;
+      const int k = u / QP;
+      // G_t = C_t dY_t^T + alpha_{t+1} R(phi_{t+1})^T G_{t+1}
+      rot(cn[i], -sn[i], G0[i], G1[i]);
+      G0[i] = mul4(a_n, G0[i]);
+      G1[i] = mul4(a_n, G1[i]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float2 cq = ld2(Ct + r * N + 2 * k);
+        G0[i] = fma4(cq.x, dyq[r], G0[i]);
+        G1[i] = fma4(cq.y, dyq[r], G1[i]);
+      }
+      const float r0 = wr[i];
+      wr[i] = a_n * (r0 * cn[i] + wi[i] * sn[i]);
+      wi[i] = a_n * (wi[i] * cn[i] - r0 * sn[i]);
+      float c = 1.f, s = 0.f;
+      if (p.theta) __sincosf(p.theta[tok * (N / 2) + k], &s, &c);
+      cn[i] = c;
+      sn[i] = s;
+    }
+    a_n = al;
+  }
+  const size_t slot = (size_t)g.bh * p.nseg + g.j;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    if (u >= UNITS) continue;
+    const int k = u / QP;
+    float* row = p.sega + (slot * N + 2 * k) * P + 4 * q;
+    *reinterpret_cast<float4*>(row) = G0[i];
+    *reinterpret_cast<float4*>(row + P) = G1[i];
+    if (q == 0) *reinterpret_cast<float2*>(p.zb + (slot * (N / 2) + k) * 2) = make_float2(wr[i], wi[i]);
+  }
+}
+
+// 5. The G entering each segment from the right, last segment first:
+//   E_last = 0,  E_{j-1} = G~_j + w_j E_j.
+template <int N, int P>
+__global__ __launch_bounds__(bwd_threads(N, P)) void bwd_combine_kernel(BackwardParams p) {
+  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
+  constexpr int UPT = (UNITS + NT - 1) / NT;
+  const int bh = blockIdx.x, tid = threadIdx.x, q = tid % QP;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    if (u >= UNITS) continue;
+    const int k = u / QP;
+    const size_t r0 = (size_t)(2 * k) * P + 4 * q;
+    float4 E0 = f4(0.f), E1 = f4(0.f);
+    for (int j = p.nseg - 1; j >= 0; --j) {
+      const size_t slot = (size_t)bh * p.nseg + j;
+      float* e = p.segb + slot * N * P + r0;
+      *reinterpret_cast<float4*>(e) = E0;
+      *reinterpret_cast<float4*>(e + P) = E1;
+      if (j > 0) {
+        const float2 w = *reinterpret_cast<const float2*>(p.zb + (slot * (N / 2) + k) * 2);
+        const float* Gl = p.sega + slot * N * P + r0;
+        rot(w.x, w.y, E0, E1);
+        E0 = addv(E0, ld4(Gl));
+        E1 = addv(E1, ld4(Gl + P));
+      }
     }
   }
 }
@@ -147,12 +382,14 @@ template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(bwd_threads(N, P)) void grads_kernel(BackwardParams p) {
   constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
   constexpr int UPT = (UNITS + NT - 1) / NT, NW = NT / 64;
-  const int bh = blockIdx.x, b = bh / p.H, h = bh - b * p.H;
+  const Seg g = segment_of(p);
+  const int bh = g.bh, h = g.h;
   const int tid = threadIdx.x, q = tid % QP, lane = tid & 63, wave = tid >> 6;
   const int L = p.L;
   const size_t tstep = (size_t)p.H;
-  const size_t tok0 = (size_t)b * L * p.H + h;
+  const size_t tok0 = (size_t)g.b * L * p.H + h;
   const float Ah = p.A[h];
+  const bool last = g.j == p.nseg - 1;
   __shared__ float s_dx[2][NW][R * P];   // dX partial sums per wave (by step parity)
   __shared__ float s_sc[2][NW][4];       // d alpha, d beta, d gamma partials per wave
   const float* hs = p.hs + (size_t)bh * L * N * P;
@@ -164,12 +401,21 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void grads_kernel(BackwardParams
   float2 Bc[UPT][R];
   float4 Xc[R];
   float cn[UPT], sn[UPT];   // cos / sin of phi_{t+1} of each unit's pair
-  // (before the last token: G_L = dH enters with a unit coefficient, no turn)
+  // Entering the segment's last token s1: for the sequence's last token, G_L =
+  // dH with a unit coefficient and no turn; otherwise G_{s1+1} (from the
+  // combine) with token s1+1's alpha, beta and phi, and Q_{s1+1} = R(phi)^T G.
   float a_n = 1.f, b_n = 0.f, dA_acc = 0.f;
+  if (!last) {
+    const size_t tokn = tok0 + (size_t)(g.s1 + 1) * tstep;
+    const float dn = p.dt[tokn], ln = p.lam[tokn];
+    a_n = __expf(dn * Ah);
+    b_n = (1.f - ln) * dn * a_n;
+  }
   {
-    const size_t tok = tok0 + (size_t)(L - 1) * tstep;
+    const size_t tok = tok0 + (size_t)g.s1 * tstep;
     const T* Bt = static_cast<const T*>(p.B) + tok * R * N;
     const T* Xt = static_cast<const T*>(p.x) + tok * R * P;
+    const size_t slot = (size_t)bh * p.nseg + g.j;
 #pragma unroll
     for (int r = 0; r < R; ++r) Xc[r] = ld4(Xt + r * P + 4 * q);
 #pragma unroll
@@ -178,19 +424,29 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void grads_kernel(BackwardParams
 #pragma unroll
       for (int r = 0; r < R; ++r) Bc[i][r] = ld2(Bt + r * N + 2 * k);
       vwrite<R>(Bc[i], Xc, V0[i], V1[i]);
-      const float* row = hs + ((size_t)(L - 1) * N + 2 * k) * P + 4 * q;
+      const float* row = hs + ((size_t)g.s1 * N + 2 * k) * P + 4 * q;
       H0[i] = ld4(row);
       H1[i] = ld4(row + P);
       G0[i] = G1[i] = Q0[i] = Q1[i] = f4(0.f);
       cn[i] = 1.f;
       sn[i] = 0.f;
-      if (p.dh) {   // dH enters G_{L-1}
-        G0[i] = ld4(p.dh + ((size_t)bh * N + 2 * k) * P + 4 * q);
-        G1[i] = ld4(p.dh + ((size_t)bh * N + 2 * k + 1) * P + 4 * q);
+      if (last) {
+        if (p.dh) {   // dH enters G_{L-1}
+          G0[i] = ld4(p.dh + ((size_t)bh * N + 2 * k) * P + 4 * q);
+          G1[i] = ld4(p.dh + ((size_t)bh * N + 2 * k + 1) * P + 4 * q);
+        }
+      } else {
+        const float* e = p.segb + (slot * N + 2 * k) * P + 4 * q;
+        G0[i] = ld4(e);
+        G1[i] = ld4(e + P);
+        if (p.theta) __sincosf(p.theta[(tok + tstep) * (N / 2) + k], &sn[i], &cn[i]);
+        Q0[i] = G0[i];
+        Q1[i] = G1[i];
+        rot(cn[i], -sn[i], Q0[i], Q1[i]);
       }
     }
   }
-  for (int t = L - 1; t >= 0; --t) {
+  for (int t = g.s1; t >= g.s0; --t) {
     const size_t tok = tok0 + (size_t)t * tstep;
     const float d = p.dt[tok], lm = p.lam[tok];
     const float al = __expf(d * Ah), be = (1.f - lm) * d * al, ga = lm * d;
@@ -360,6 +616,10 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void grads_kernel(BackwardParams
 #pragma unroll
     for (int r = 0; r < R; ++r) Xc[r] = xm[r];
   }
+  if (g.j != 0) {   // the token before s0 belongs to the previous segment
+    if (tid == 0) atomicAdd(p.dA + h, dA_acc);
+    return;
+  }
   // d h0 = alpha_0 Q_0;  dV_{-1} = beta_0 Q_0 -> d B_prev, d x_prev
   float4 dxq[R];
 #pragma unroll
@@ -429,11 +689,14 @@ namespace {
 
 template <typename T, int N, int P, int R>
 hipError_t run_backward(const BackwardParams& p, hipStream_t s) {
-  const unsigned grid = (unsigned)(p.batch * p.H);
-  hipLaunchKernelGGL((states_kernel<T, N, P, R>), dim3(grid), dim3(bwd_threads(N, P)), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grads_kernel<T, N, P, R>), dim3(grid), dim3(bwd_threads(N, P)), 0, s, p);
+  const unsigned nbh = (unsigned)(p.batch * p.H), nsg = nbh * (unsigned)p.nseg;
+  const dim3 blk(bwd_threads(N, P));
+  hipLaunchKernelGGL((fwd_maps_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
+  hipLaunchKernelGGL((fwd_combine_kernel<N, P>), dim3(nbh), blk, 0, s, p);
+  hipLaunchKernelGGL((states_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
+  hipLaunchKernelGGL((bwd_maps_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
+  hipLaunchKernelGGL((bwd_combine_kernel<N, P>), dim3(nbh), blk, 0, s, p);
+  hipLaunchKernelGGL((grads_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
   return hipGetLastError();
 }
 

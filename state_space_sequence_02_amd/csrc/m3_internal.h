@@ -128,7 +128,8 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
 // Backward (m3_backward.hip): inputs of the forward call, the cotangents dy
 // [b,L,H,R,P] (input dtype) and dh [b,H,N,P] (fp32 or NULL), the fp32
 // gradients (dtheta / dh0 / dBp / dxp may be NULL: not computed; dA must be
-// zero on entry: workgroups add into it), and the workspace of every state.
+// zero on entry: workgroups add into it), and the workspace: every state and
+// the per-segment hand-off of the segment-parallel passes.
 struct BackwardParams {
   const void* x; const void* B; const void* C;
   const float* dt; const float* A; const float* lam; const float* theta;
@@ -137,8 +138,19 @@ struct BackwardParams {
   float* dx; float* dB; float* dC; float* ddt; float* dA; float* dlam; float* dtheta;
   float* dh0; float* dBp; float* dxp;
   float* hs;                    // H_t for every t, [b, H, L, N, P] fp32
+  float* sega;                  // [b*H][nseg][N][P]: forward local end states, then backward local G
+  float* segb;                  // [b*H][nseg][N][P]: states entering each segment, then G entering it
+  float* zf;                    // [b*H][nseg][N/2] (re, im): forward propagator of each segment
+  float* zb;                    // [b*H][nseg][N/2] (re, im): backward propagator of each segment
   int batch, L, H;
+  int S, nseg;                  // tokens per segment, segments per sequence
 };
+// Tokens per backward segment: about 8192 segment workgroups in all, 16..256.
+inline int backward_segment(long long L, long long nbh) {
+  long long want = L * nbh / 8192, S = 16;
+  while (S * 2 <= want && S < 256) S *= 2;
+  return (int)S;
+}
 hipError_t launch_backward(const BackwardParams& p, int dtype, int N, int P, int R, hipStream_t stream);
 
 // The device-resident prefill scratch of m3_scan_prefill_noalloc: its size

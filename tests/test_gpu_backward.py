@@ -2,7 +2,10 @@
 oracle (oracle/backward.py, pinned on the CPU by finite differences of the
 forward oracle and exact adjoint identities): every gradient, both input
 dtypes, with and without rotation and incoming state, ranks 1-8, L = 1 and an
-empty sequence."""
+empty sequence.  The backward runs segment-parallel (16..256 tokens per
+segment, chosen from the sequence length and the number of (sequence, head)
+pairs), so these cases span one to over a hundred segments, with ragged last
+segments."""
 import numpy as np
 import pytest
 import torch
@@ -77,6 +80,8 @@ CASES = [
     ("mimo", dict(batch=1, seqlen=40, nheads=2, headdim=16, dstate=32, rank=8), True, True),
     ("tiny", dict(batch=1, seqlen=50, nheads=2, headdim=64, dstate=128, rank=4), True, True),   # fp32
     ("mimo", dict(batch=1, seqlen=1, nheads=3), True, True),
+    # 32-token segments (2100 tokens x 8 heads), a ragged last segment of 20
+    ("siso", dict(batch=1, seqlen=2100, nheads=8), True, True),
 ]
 
 
