@@ -97,6 +97,24 @@ def test_prefill_without_rotation():
     _prefill_case(w, seed=4, carry=True, chunk=32)
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_large_phases_fp32(chunk):
+    """fp32 inputs with angles near 3 rad per step, so the chunk-local phases the
+    prefill turns into cos/sin reach hundreds of radians (about 190 at chunk 64,
+    380 at 128), held to the fp32 tolerance; the decode step takes the same
+    angles one at a time."""
+    w = inputs.workload("tiny", batch=1, seqlen=300, nheads=2, headdim=16, dstate=32, rank=2)
+    d = inputs.make_prefill_inputs(w, seed=21)
+    g = torch.Generator().manual_seed(22)
+    d["theta"] = (2.9 + 0.2 * torch.rand(d["theta"].shape, generator=g)).to(torch.float32)
+    assert taken_chunk(w, chunk) == chunk
+    note(f"prefill fp32 large phases chunk={chunk}")
+    y, h = _run_prefill(dev_inputs(d), chunk=chunk)
+    yr, hr = oracle.scan(**oracle_inputs(d))
+    check_blocks(to64(y), yr, TOL["fp32"], (1, 3, 4), "y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL["fp32"], (2, 3), "h_out")
+
+
 def test_zero_angles_match_no_rotation_bitwise():
     w = inputs.workload("mimo", batch=1, seqlen=100, nheads=2)
     d = dev_inputs(inputs.make_prefill_inputs(w, seed=5))
