@@ -480,6 +480,58 @@ def test_workload_decode_full_size():
     check_blocks(to64(h), hr, TOL["bf16"], (2, 3), "decode workload h")
 
 
+def _rotate_pairs(S, ang, scale):
+    """scale x R(ang) on row pairs (2k, 2k+1) of S [b, H, N, P]; ang [b, H, N/2], scale [b, H]."""
+    c, s = torch.cos(ang)[..., None], torch.sin(ang)[..., None]
+    e, o = S[:, :, 0::2], S[:, :, 1::2]
+    out = torch.empty_like(S)
+    out[:, :, 0::2] = c * e - s * o
+    out[:, :, 1::2] = s * e + c * o
+    return out * scale[:, :, None, None]
+
+
+def test_sequence_shards_compose():
+    """The sequence-sharding plan for the long prefill, run through the ABI on
+    one GPU: the sequence is cut into 4 shards; pass 1 runs every shard from a
+    zero state (its first token's delayed write taken from the previous
+    shard's last B, x), giving its end state S_g; the shard's map is its total
+    decay exp(A sum dt) and total angle sum(phi) per pair; the prefix
+    T_g = a_g R(Psi_g) T_{g-1} + S_g gives every shard's entering state; pass 2
+    reruns shards 1..3 from T_{g-1}.  The stitched y and the final state match
+    the oracle over the whole sequence (with a non-zero incoming carry)."""
+    w = inputs.workload("long", seqlen=4096, nheads=4)
+    d = inputs.make_prefill_inputs(w, seed=31)
+    c = inputs.random_carry(w, seed=32)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    G, L = 4, w.seqlen
+    Ls = L // G
+    sl = [slice(g * Ls, (g + 1) * Ls) for g in range(G)]
+    part = lambda g, k: dg[k][:, sl[g]].contiguous()
+    halo = lambda g: ((cg["B_prev"], cg["x_prev"]) if g == 0 else
+                      (dg["B"][:, g * Ls - 1].contiguous(), dg["x"][:, g * Ls - 1].contiguous()))
+
+    def run(g, h0):
+        Bp, xp = halo(g)
+        return m3.scan_prefill(part(g, "x"), part(g, "B"), part(g, "C"), part(g, "dt"), dg["A"], part(g, "lam"),
+                               part(g, "theta"), h0=h0, B_prev=Bp, x_prev=xp, chunk=64)
+
+    note("sharded prefill: pass 1 (zero entering state)")
+    first = [run(g, cg["h0"] if g == 0 else None) for g in range(G)]
+    T = first[0][1]
+    ys = [first[0][0]]
+    for g in range(1, G):
+        a = torch.exp(dg["A"][None, :] * dg["dt"][:, sl[g]].double().sum(1).float())   # [b, H]
+        psi = dg["theta"][:, sl[g]].double().sum(1).float()                              # [b, H, N/2]
+        note(f"sharded prefill: pass 2, shard {g}")
+        y, _ = run(g, T)
+        ys.append(y)
+        T = _rotate_pairs(T, psi, a) + first[g][1]
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
+    check_blocks(to64(torch.cat(ys, dim=1)), yr, TOL["bf16"], (1, 3, 4), "sharded y", elem_axes=(3, 4))
+    check_blocks(to64(T), hr, TOL["bf16"], (2, 3), "sharded h_out")
+
+
 # ---------------------------------------------------------------------------
 # error reporting (forced from the host: every kernel still exits normally)
 
