@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <cstring>
 
 #include "m3_internal.h"
 
@@ -536,7 +537,12 @@ m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,
 }
 
 const char* m3_status_str(m3_status st) {
-  switch (st) {
+  // read as an integer: a C caller may pass any int, which would not be a
+  // valid value of the enum type in this C++ translation unit
+  static_assert(sizeof(m3_status) == sizeof(int32_t), "status width");
+  int32_t v;
+  std::memcpy(&v, &st, sizeof v);
+  switch (v) {
     case M3_OK: return "ok";
     case M3_ERR_NULL: return "a required pointer is NULL";
     case M3_ERR_SHAPE: return "invalid or unsupported shape";

@@ -1,0 +1,61 @@
+"""Host sanitizer builds (CPU only): the C oracle and the host side of the C
+ABI compiled with AddressSanitizer and UndefinedBehaviorSanitizer, each run
+by a driver under tests/sanitize/ that exercises it (oracle: scans of several
+shapes, split-and-resume, every validation error; ABI: every query over a grid
+of valid and invalid shapes, status strings, and each entry point's host-side
+argument errors, with no GPU).  A sanitizer report makes the driver exit
+non-zero.  The device code is linked unchanged (no GPU sanitizer exists for
+it here)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SAN = os.path.join(ROOT, "tests", "sanitize")
+BUILD = os.path.join(ROOT, "_build")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+CLANG = os.path.join(ROCM, "llvm", "bin", "clang++")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def _run(cmd, **kw):
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, **kw)
+    assert r.returncode == 0, f"{' '.join(cmd[:3])} ... failed ({r.returncode}):\n{r.stdout[-2000:]}\n{r.stderr[-4000:]}"
+    return r
+
+
+def test_oracle_under_asan_ubsan(tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    exe = str(tmp_path / "oracle_asan")
+    _run(["gcc", "-std=c11", "-O1", "-g", *SAN_FLAGS, os.path.join(ROOT, "oracle", "m3ref.c"),
+          os.path.join(SAN, "oracle_driver.c"), "-o", exe, "-lm"])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = _run([exe], env=env)
+    assert "oracle ok" in r.stdout
+
+
+def test_abi_host_code_under_asan_ubsan(tmp_path):
+    objs = [os.path.join(BUILD, f) for f in sorted(os.listdir(BUILD))
+            if f.endswith(".o") and f != "m3_api.cpp.o"] if os.path.isdir(BUILD) else []
+    if not objs or not os.path.exists(CLANG) or not os.path.exists(HIPCC):
+        pytest.skip("library objects or ROCm compilers not found (run the build first)")
+    api = str(tmp_path / "api.o")
+    drv = str(tmp_path / "drv.o")
+    exe = str(tmp_path / "abi_asan")
+    host_san = []
+    for f in SAN_FLAGS:   # host pass only: the device code is built as usual
+        host_san += ["-Xarch_host", f]
+    _run([HIPCC, "-x", "hip", "-O1", "-g", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+          "-Xclang", "-packed-fp32-ops", *host_san, "-I", os.path.join(ROOT, "include"), "-I", BUILD, "-c",
+          os.path.join(ROOT, "state_space_sequence_02_amd", "csrc", "m3_api.cpp"), "-o", api])
+    _run([CLANG, "-O1", "-g", "-std=c++17", *SAN_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+          os.path.join(SAN, "abi_driver.cpp"), "-o", drv])
+    _run([CLANG, *SAN_FLAGS, drv, api, *objs, f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib", "-o", exe])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1",
+               HIP_VISIBLE_DEVICES="")
+    r = _run([exe], env=env)
+    assert "abi ok" in r.stdout
