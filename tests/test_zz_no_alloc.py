@@ -65,3 +65,40 @@ def test_noalloc_matches_workspace_entry_point():
         yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
         check_blocks(to64(y0), yr, TOL["bf16"], (1, 3, 4), "no-alloc y", elem_axes=(3, 4))
         check_blocks(to64(h0), hr, TOL["bf16"], (2, 3), "no-alloc h")
+
+
+def test_noalloc_graph_replay():
+    """The entry point is meant for code under graph capture: a captured call
+    is right on every replay, with eager no-alloc calls (sharing the same
+    device array) between the replays."""
+    w = inputs.workload("mimo", batch=1, seqlen=300, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=203)
+    c = inputs.random_carry(w, seed=204)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    yr, hr = oracle.scan(**oracle_inputs({**d, **c}))
+    note("no-alloc prefill before capture")
+    _noalloc(dg, cg, 32)                       # eager: the device array's address is looked up here
+    torch.cuda.synchronize()
+    out = {}
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    note("no-alloc prefill graph capture")
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            out["y"], out["h"] = _noalloc(dg, cg, 32)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out["y"].zero_()
+        out["h"].zero_()
+        torch.cuda.synchronize()
+        note(f"no-alloc graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        check_blocks(to64(out["y"]), yr, TOL["bf16"], (1, 3, 4), f"y replay {rep}", elem_axes=(3, 4))
+        check_blocks(to64(out["h"]), hr, TOL["bf16"], (2, 3), f"h replay {rep}")
+        ye, he = _noalloc(dg, cg, 32)          # eager, the same device array
+        torch.cuda.synchronize()
+        check_blocks(to64(ye), yr, TOL["bf16"], (1, 3, 4), f"y eager after replay {rep}", elem_axes=(3, 4))
+        check_blocks(to64(he), hr, TOL["bf16"], (2, 3), f"h eager after replay {rep}")
