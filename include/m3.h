@@ -322,12 +322,14 @@ m3_status m3_decode_step_prologue(const m3_shape* s, const m3_prologue* pro,
                                   void* y, void* stream);
 
 /* Bytes of device workspace m3_scan_backward needs for this shape (0 when it
- * takes none): every state H_t of the forward pass (b x H x L x N x P fp32),
- * then, per segment of the sequence (16..256 tokens, chosen from L and b x H),
- * two N x P fp32 hand-off arrays and two N/2 complex propagators.
+ * takes none): per segment of the sequence (1..32 tokens, the most whose rows
+ * fit one compute unit's 160 KB LDS for this N, P, R; 32 at R = 1, 8 at R = 4)
+ * three N x P fp32 hand-off arrays (the segment's state from a zero start,
+ * its true entering state, the state gradient entering from its right) and
+ * two N/2 complex propagators.  No per-token state is stored.
  * The backward takes N = 16..128, P = 16..64, every R, fp32 or bf16 inputs,
- * except the variants whose compiled kernels use scratch memory (R = 8 at the
- * larger N x P); the call refuses those with M3_ERR_SHAPE. */
+ * except variants whose compiled kernels use scratch memory (none in the
+ * current build); the call refuses those with M3_ERR_SHAPE. */
 size_t m3_scan_backward_workspace_bytes(const m3_shape* s);
 
 /* Gradients of the prefill (the recurrence of m3_scan_prefill): given the
@@ -356,11 +358,14 @@ size_t m3_scan_backward_workspace_bytes(const m3_shape* s);
  *                        contents required
  * Errors: M3_ERR_NULL (a required pointer, or dtheta not matching theta),
  * M3_ERR_SHAPE, M3_ERR_WORKSPACE, M3_ERR_ALIAS (an output overlapping an input,
- * the workspace or another output).  Work runs on `stream` in six launches:
- * each segment of each (sequence, head) runs forward from a zero state, a
- * short pass per (sequence, head) composes the segments' states, the segments
- * run again from their true entering states storing every state, and the same
- * three steps run backwards through time for the gradient of the state. */
+ * the workspace or another output).  Work runs on `stream` in five launches:
+ * each segment of each (sequence, head) runs forward from a zero state and
+ * forms its propagator, a short pass per (sequence, head) composes them into
+ * every segment's entering state, the same two steps run backwards through
+ * time for the state gradient entering each segment from its right, and a
+ * last launch forms every gradient of a segment from those two in closed
+ * matrix form (pairwise products of the segment's rows), without a stored
+ * per-token state. */
 m3_status m3_scan_backward(const m3_shape* s,
                            const void* x, const void* B, const void* C,
                            const float* dt, const float* A, const float* lam, const float* theta,

@@ -386,25 +386,27 @@ m3_status m3_scan_prefill(const m3_shape* s,
 }
 
 namespace {
-// Backward workspace: every state [b*H][L][N][P] | two segment hand-off arrays
-// [b*H][nseg][N][P] | the forward and backward propagators [b*H][nseg][N/2]
-// (re, im), each region 256-byte aligned.
+// Backward workspace: three segment hand-off arrays [b*H][nseg][N][P] (local
+// states then local G; the state entering each segment; the G entering each
+// segment) | the forward and backward propagators [b*H][nseg][N/2] (re, im),
+// each region 256-byte aligned.
 struct BackwardLayout {
   int S, nseg;
-  size_t off_sega, off_segb, off_zf, off_zb, bytes;
+  size_t off_sega, off_segb, off_segc, off_zf, off_zb, bytes;
 };
 BackwardLayout backward_layout(const m3_shape& s) {
   BackwardLayout o;
   const size_t nbh = (size_t)s.batch * s.nheads, NP = (size_t)s.dstate * s.headdim;
-  o.S = backward_segment(s.seqlen, (long long)nbh);
-  o.nseg = s.seqlen > 0 ? (s.seqlen + o.S - 1) / o.S : 0;
+  o.S = backward_segment(s.rank, s.dstate, s.headdim);
+  o.nseg = s.seqlen > 0 && o.S > 0 ? (s.seqlen + o.S - 1) / o.S : 0;
   const size_t seg = align256(nbh * o.nseg * NP * sizeof(float));
   const size_t z = align256(nbh * o.nseg * (s.dstate / 2) * 2 * sizeof(float));
-  o.off_sega = align256(nbh * s.seqlen * NP * sizeof(float));
-  o.off_segb = o.off_sega + seg;
-  o.off_zf = o.off_segb + seg;
-  o.off_zb = o.off_zf + z;
-  o.bytes = o.off_zb + z;
+  o.off_sega = 0;
+  o.off_segb = seg;
+  o.off_segc = 2 * seg;
+  o.off_zf = 3 * seg;
+  o.off_zb = 3 * seg + z;
+  o.bytes = 3 * seg + 2 * z;
   return o;
 }
 }  // namespace
@@ -414,6 +416,7 @@ size_t m3_scan_backward_workspace_bytes(const m3_shape* s) {
   if (s->dstate > 128 || s->headdim > 64) return 0;
   for (const auto& k : kBackwardScratch)
     if (k[0] == s->dtype && k[1] == s->dstate && k[2] == s->headdim && k[3] == s->rank) return 0;
+  if (backward_segment(s->rank, s->dstate, s->headdim) == 0) return 0;
   return std::max<size_t>(256, backward_layout(*s).bytes);
 }
 
@@ -473,9 +476,9 @@ m3_status m3_scan_backward(const m3_shape* s,
   p.dh0 = dh0; p.dBp = dB_prev; p.dxp = dx_prev;
   const BackwardLayout lay = backward_layout(*s);
   char* ws = static_cast<char*>(workspace);
-  p.hs = reinterpret_cast<float*>(ws);
   p.sega = reinterpret_cast<float*>(ws + lay.off_sega);
   p.segb = reinterpret_cast<float*>(ws + lay.off_segb);
+  p.segc = reinterpret_cast<float*>(ws + lay.off_segc);
   p.zf = reinterpret_cast<float*>(ws + lay.off_zf);
   p.zb = reinterpret_cast<float*>(ws + lay.off_zb);
   p.batch = b; p.L = L; p.H = H;

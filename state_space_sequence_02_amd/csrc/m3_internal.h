@@ -128,8 +128,8 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
 // Backward (m3_backward.hip): inputs of the forward call, the cotangents dy
 // [b,L,H,R,P] (input dtype) and dh [b,H,N,P] (fp32 or NULL), the fp32
 // gradients (dtheta / dh0 / dBp / dxp may be NULL: not computed; dA must be
-// zero on entry: workgroups add into it), and the workspace: every state and
-// the per-segment hand-off of the segment-parallel passes.
+// zero on entry: workgroups add into it), and the workspace: the per-segment
+// hand-off of the segment-parallel passes.
 struct BackwardParams {
   const void* x; const void* B; const void* C;
   const float* dt; const float* A; const float* lam; const float* theta;
@@ -137,19 +137,62 @@ struct BackwardParams {
   const void* dy; const float* dh;
   float* dx; float* dB; float* dC; float* ddt; float* dA; float* dlam; float* dtheta;
   float* dh0; float* dBp; float* dxp;
-  float* hs;                    // H_t for every t, [b, H, L, N, P] fp32
   float* sega;                  // [b*H][nseg][N][P]: forward local end states, then backward local G
-  float* segb;                  // [b*H][nseg][N][P]: states entering each segment, then G entering it
+  float* segb;                  // [b*H][nseg][N][P]: the state entering each segment
+  float* segc;                  // [b*H][nseg][N][P]: the G entering each segment from the right
   float* zf;                    // [b*H][nseg][N/2] (re, im): forward propagator of each segment
   float* zb;                    // [b*H][nseg][N/2] (re, im): backward propagator of each segment
   int batch, L, H;
   int S, nseg;                  // tokens per segment, segments per sequence
 };
-// Tokens per backward segment: about 8192 segment workgroups in all, 16..256.
-inline int backward_segment(long long L, long long nbh) {
-  long long want = L * nbh / 8192, S = 16;
-  while (S * 2 <= want && S < 256) S *= 2;
-  return (int)S;
+// LDS of the backward's segment kernel (floats, each array 16-byte aligned;
+// N and P strides padded to 32, the rows to MK = a multiple of 32 >= S*R):
+// B~, C~ [MK][N]; X, dY [MK][P]; S0', D' [N][P]; four [MK]^2 pairwise arrays;
+// [S]^2; cos/sin [S][N/2] and [N/2]; per-token fields [S][16]; five [S][N/2]
+// partial sums; per-row e^{l}; the previous write [R][N], [R][P]; reduction
+// scratch.
+struct BwdLds {
+  size_t MK, B, C, X, Y, S, D, G1, G1T, G2T, PR, OM, CS, CN, TK, PA, PC, PB, PK, PI, EL, BM, XM, RD, total;
+};
+__host__ __device__ constexpr size_t bwd_r4(size_t n) { return (n + 3) & ~(size_t)3; }
+__host__ __device__ constexpr BwdLds bwd_lds(int Q, int R, int N, int P) {
+  const size_t NS = N < 32 ? 32 : N, PS = P < 32 ? 32 : P, NH = (size_t)N / 2;
+  const size_t MK = ((size_t)Q * R + 31) / 32 * 32;
+  BwdLds o{};
+  size_t at = 0;
+  o.MK = MK;
+  o.B = at; at += bwd_r4(MK * NS);
+  o.C = at; at += bwd_r4(MK * NS);
+  o.X = at; at += bwd_r4(MK * PS);
+  o.Y = at; at += bwd_r4(MK * PS);
+  o.S = at; at += bwd_r4(NS * PS);
+  o.D = at; at += bwd_r4(NS * PS);
+  o.G1 = at; at += bwd_r4(MK * MK);
+  o.G1T = at; at += bwd_r4(MK * MK);
+  o.G2T = at; at += bwd_r4(MK * MK);
+  o.PR = at; at += bwd_r4(MK * MK);
+  o.OM = at; at += bwd_r4((size_t)Q * Q);
+  o.CS = at; at += bwd_r4((size_t)Q * NH * 2);
+  o.CN = at; at += bwd_r4(NH * 2);
+  o.TK = at; at += bwd_r4((size_t)Q * 16);
+  o.PA = at; at += bwd_r4((size_t)Q * NH);
+  o.PC = at; at += bwd_r4((size_t)Q * NH);
+  o.PB = at; at += bwd_r4((size_t)Q * NH);
+  o.PK = at; at += bwd_r4((size_t)Q * NH);
+  o.PI = at; at += bwd_r4((size_t)Q * NH);
+  o.EL = at; at += bwd_r4(MK);
+  o.BM = at; at += bwd_r4((size_t)R * N);
+  o.XM = at; at += bwd_r4((size_t)R * P);
+  o.RD = at; at += bwd_r4(336);
+  o.total = at;
+  return o;
+}
+// Tokens per backward segment: the largest of 32, 16, ..., 1 whose segment
+// kernel fits a compute unit's LDS.
+__host__ __device__ constexpr int backward_segment(int R, int N, int P) {
+  for (int S = 32; S >= 1; S /= 2)
+    if (bwd_lds(S, R, N, P).total * sizeof(float) <= (size_t)kLdsBudget) return S;
+  return 0;
 }
 hipError_t launch_backward(const BackwardParams& p, int dtype, int N, int P, int R, hipStream_t stream);
 

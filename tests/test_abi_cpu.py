@@ -335,12 +335,12 @@ def test_noalloc_rejects_oversize_shapes(lib):
 def test_backward_validation_codes(lib):
     """m3_scan_backward checks its arguments on the host before any launch."""
     ok = m3.make_shape(2, 64, 3, 64, 128, 4, 0, m3.M3_BF16)
-    # every state (b*H*L*N*P fp32), two segment hand-off arrays and two
-    # propagator arrays: 64 tokens over 6 (sequence, head) pairs make 4
-    # segments of 16 tokens
-    nbh, nseg = 2 * 3, 4
+    # three segment hand-off arrays [b*H][nseg][N][P] and two propagator arrays
+    # [b*H][nseg][N/2] complex: at R=4, N=128, P=64 a segment is 8 tokens, so
+    # 64 tokens make 8 segments over 6 (sequence, head) pairs
+    nbh, nseg = 2 * 3, 8
     assert lib.m3_scan_backward_workspace_bytes(ctypes.byref(ok)) == (
-        nbh * 64 * 128 * 64 * 4 + 2 * nbh * nseg * 128 * 64 * 4 + 2 * nbh * nseg * 64 * 2 * 4)
+        3 * nbh * nseg * 128 * 64 * 4 + 2 * nbh * nseg * 64 * 2 * 4)
     assert lib.m3_scan_backward_workspace_bytes(ctypes.byref(m3.make_shape(2, 64, 3, 128, 128, 4, 0, 1))) == 0
     assert lib.m3_scan_backward_workspace_bytes(ctypes.byref(m3.make_shape(2, 64, 3, 64, 256, 4, 0, 1))) == 0
 

@@ -2,10 +2,10 @@
 oracle (oracle/backward.py, pinned on the CPU by finite differences of the
 forward oracle and exact adjoint identities): every gradient, both input
 dtypes, with and without rotation and incoming state, ranks 1-8, L = 1 and an
-empty sequence.  The backward runs segment-parallel (16..256 tokens per
-segment, chosen from the sequence length and the number of (sequence, head)
-pairs), so these cases span one to over a hundred segments, with ragged last
-segments."""
+empty sequence.  The backward runs segment-parallel (1..32 tokens per
+segment, the most whose rows fit one compute unit's LDS: 32 at rank 1, 8 at
+rank 4, 4 at rank 8 for N = 128, P = 64), so these cases span one to over
+five hundred segments, with ragged last segments."""
 import numpy as np
 import pytest
 import torch
@@ -82,6 +82,8 @@ CASES = [
     ("mimo", dict(batch=1, seqlen=1, nheads=3), True, True),
     # 32-token segments (2100 tokens x 8 heads), a ragged last segment of 20
     ("siso", dict(batch=1, seqlen=2100, nheads=8), True, True),
+    # rank 8 at N = 128, P = 64: 4-token segments, a ragged last one of 3
+    ("mimo", dict(batch=1, seqlen=47, nheads=2, rank=8), True, True),
 ]
 
 
