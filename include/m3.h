@@ -134,6 +134,32 @@ m3_status m3_prefill_status(void* workspace, size_t workspace_bytes, void* strea
  * not for use while prefill calls run on other threads. */
 void m3_debug_set_spin_limit(uint32_t polls);
 
+/* The two implementations of m3_scan_prefill.  Both compute the same chunked
+ * rearrangement of the recurrence (explainer sec. 3.3) with the same
+ * workspace:
+ *   M3_KERNEL_PER_CHUNK  one workgroup per (sequence, chunk), every variant
+ *                        (dtype, N = 16..128, P, R, gate, prologue);
+ *   M3_KERNEL_STREAM     one persistent workgroup per compute unit streaming
+ *                        its chunks' B and X through LDS in 32-row blocks while
+ *                        the next blocks' loads are in flight; bf16 inputs,
+ *                        P = 64, no gate or prologue, N = 64 at R = 1, 2 or 4
+ *                        with chunks of 128 or 256 (token, rank) rows, N = 128
+ *                        with 128 rows (R = 1, 2, 4) or 256 rows (R = 4). */
+enum { M3_KERNEL_PER_CHUNK = 1, M3_KERNEL_STREAM = 2 };
+
+/* The kernel m3_scan_prefill runs for this shape (s->chunk as in
+ * m3_prefill_chunk_used): M3_KERNEL_STREAM where that kernel takes the shape
+ * at N = 128 (at N = 64 the per-chunk kernel is the faster one), else
+ * M3_KERNEL_PER_CHUNK; 0 when the call refuses the shape. */
+int32_t m3_prefill_kernel_used(const m3_shape* s);
+
+/* For tests and measurement: restricts m3_scan_prefill (and the queries) to one
+ * kernel.  0 restores the library's choice, M3_KERNEL_PER_CHUNK uses only the
+ * per-chunk kernel, M3_KERNEL_STREAM the streaming kernel wherever it takes
+ * the shape.  Any other value: M3_ERR_SHAPE, nothing changed.  Process-wide;
+ * not for use while prefill calls run on other threads. */
+m3_status m3_debug_set_prefill_kernel(int32_t which);
+
 /* Chunked prefill over a whole sequence (the recurrence above for t = 0..L-1).
  * Defined by: explainer panels 1 (coefficients, Eq. 6), 2 (causal operator as a
  * decay x two-band product, Eq. 7), 3 (rotations as data-dependent RoPE,

@@ -7,4 +7,5 @@ from ._binding import (  # noqa: F401
     M3Error, M3Prologue, M3Shape, M3_BF16, M3_FP32, EXPORTS, LIB_PATH, decode_step, decode_step_gated, decode_step_prologue, load_library,
     make_shape, prefill_chunk_used, prefill_workspace_bytes, scan_prefill, scan_prefill_gated, scan_prefill_prologue,
     prefill_max_chunk, prefill_status, debug_set_spin_limit, STATUS, scan_backward, backward_workspace_bytes,
+    prefill_kernel_used, debug_set_prefill_kernel, M3_KERNEL_PER_CHUNK, M3_KERNEL_STREAM,
 )

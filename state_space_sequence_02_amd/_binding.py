@@ -24,7 +24,9 @@ EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_prefill_ma
            "m3_scan_backward", "m3_scan_backward_workspace_bytes",
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
            "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
+           "m3_prefill_kernel_used", "m3_debug_set_prefill_kernel",
            "m3_status_str", "m3_version")
+M3_KERNEL_PER_CHUNK, M3_KERNEL_STREAM = 1, 2
 
 
 class M3Shape(ctypes.Structure):
@@ -68,6 +70,10 @@ def load_library(path: str = LIB_PATH):
     lib.m3_prefill_status.argtypes = [vp, sz, vp]
     lib.m3_debug_set_spin_limit.restype = None
     lib.m3_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
+    lib.m3_prefill_kernel_used.restype = ctypes.c_int32
+    lib.m3_prefill_kernel_used.argtypes = [sp]
+    lib.m3_debug_set_prefill_kernel.restype = ctypes.c_int
+    lib.m3_debug_set_prefill_kernel.argtypes = [ctypes.c_int32]
     lib.m3_scan_prefill.restype = ctypes.c_int
     lib.m3_scan_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.m3_scan_backward_workspace_bytes.restype = sz
@@ -158,6 +164,18 @@ def prefill_status(workspace: torch.Tensor) -> int:
 
 def debug_set_spin_limit(polls: int) -> None:
     load_library().m3_debug_set_spin_limit(int(polls))
+
+
+def prefill_kernel_used(shape: M3Shape) -> int:
+    """m3_prefill_kernel_used: M3_KERNEL_STREAM (2), M3_KERNEL_PER_CHUNK (1) or
+    0 when m3_scan_prefill refuses the shape."""
+    return int(load_library().m3_prefill_kernel_used(ctypes.byref(shape)))
+
+
+def debug_set_prefill_kernel(which: int) -> None:
+    """m3_debug_set_prefill_kernel: 0 the library's choice, 1 the per-chunk
+    kernel only, 2 the streaming kernel wherever it takes the shape."""
+    _check(load_library().m3_debug_set_prefill_kernel(int(which)))
 
 
 def scan_prefill(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,

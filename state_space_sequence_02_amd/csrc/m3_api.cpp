@@ -78,6 +78,18 @@ int choose_chunk(const m3_shape& s, int gated, int pro) {
   return 0;
 }
 
+// The streaming prefill variants {N, P, R, 32-row blocks} that use scratch
+// (build report): those shapes take the per-chunk kernel.
+const int kStreamScratch[][4] = {
+#include "m3_scratch_table_stream.inc"
+    {-1, 0, 0, 0}};
+
+bool stream_spills(int N, int P, int R, int Q) {
+  for (const auto& k : kStreamScratch)
+    if (k[0] == N && k[1] == P && k[2] == R && k[3] * 32 == Q * R) return true;
+  return false;
+}
+
 // The backward variants {dtype, N, P, R} that use scratch (build report).
 const int kBackwardScratch[][4] = {
 #include "m3_scratch_table_bwd.inc"
@@ -92,6 +104,11 @@ const PrefillVariant kScratchVariants[] = {
 // Look-back polls before a wait gives up (tests lower it to force the
 // error path; see m3_debug_set_spin_limit).
 std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};
+
+// Which prefill kernel plain calls may use (m3_debug_set_prefill_kernel):
+// 0 the library's choice, M3_KERNEL_PER_CHUNK only that one, M3_KERNEL_STREAM
+// the streaming kernel wherever it takes the shape.
+std::atomic<int> g_prefill_kernel{0};
 
 }  // namespace
 
@@ -121,6 +138,20 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro) {
   plan->off_states = align256(plan->off_maps + bhc * map);
   plan->bytes = align256(plan->off_states + bhc * map);
   plan->lds = pro ? fused_lds_bytes(q, s.rank, s.dstate, s.headdim, (int)esize(s.dtype), 1) : lds_need(q, s);
+  plan->kernel = M3_KERNEL_PER_CHUNK;
+  // The streaming kernel takes the shapes it supports at N = 128, where a
+  // chunk of the per-chunk kernel fills a compute unit's LDS on its own, so
+  // nothing overlaps its loads with its arithmetic.  At N = 64 the per-chunk
+  // kernel runs two workgroups per compute unit and measured faster (SISO,
+  // 4 x 4096 tokens x 32 heads, chunk 128: 134 us against 196 us); the
+  // streaming kernel runs there only when asked for (m3_debug_set_prefill_kernel).
+  const int mode = g_prefill_kernel.load(std::memory_order_relaxed);
+  if (mode != M3_KERNEL_PER_CHUNK && (mode == M3_KERNEL_STREAM || s.dstate == 128) &&
+      stream_supported(s.dtype, s.dstate, s.headdim, s.rank, q, gated, pro) &&
+      !stream_spills(s.dstate, s.headdim, s.rank, q)) {
+    plan->kernel = M3_KERNEL_STREAM;
+    plan->lds = stream_lds_bytes(q, s.rank, s.dstate, s.headdim);
+  }
   return true;
 }
 
@@ -183,6 +214,19 @@ m3_status m3_prefill_status(void* workspace, size_t workspace_bytes, void* strea
 }
 
 void m3_debug_set_spin_limit(uint32_t polls) { g_spin_limit.store(polls ? polls : kDefaultSpinLimit); }
+
+int32_t m3_prefill_kernel_used(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan, 0, 0)) return 0;
+  return plan.kernel;
+}
+
+m3_status m3_debug_set_prefill_kernel(int32_t which) {
+  if (which != 0 && which != M3_KERNEL_PER_CHUNK && which != M3_KERNEL_STREAM) return M3_ERR_SHAPE;
+  g_prefill_kernel.store(which, std::memory_order_relaxed);
+  return M3_OK;
+}
 
 }  // extern "C"
 
@@ -269,7 +313,8 @@ m3_status prefill_common(const m3_shape* s,
   f.batch = b; f.L = L; f.H = H; f.N = N; f.P = P; f.R = R; f.logR = ilog2(R);
   f.Q = plan.Q; f.nc = plan.nc;
   f.use_maps = 1;   // (the launch decides from the device's resident workgroups)
-  const hipError_t e = launch_fused_prefill(f, lds, s->dtype, hs);
+  const hipError_t e = plan.kernel == M3_KERNEL_STREAM ? launch_stream_prefill(f, hs)
+                                                       : launch_fused_prefill(f, lds, s->dtype, hs);
   if (e == hipErrorNotSupported) return M3_ERR_SHAPE;   // the loaded kernel uses scratch
   if (e != hipSuccess) return M3_ERR_DEVICE;
   return M3_OK;

@@ -152,8 +152,9 @@ __device__ __forceinline__ void mem_done() {
 // Every one of the workgroup's `nwaves` waves calls this once after
 // mem_done(); the last one to arrive raises flag `f` to `val`.  `ctr` is an
 // LDS counter starting at 0.
-__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned long long* f, unsigned long long val, int nwaves) {
-  if ((threadIdx.x & 63) == 0) {
+__device__ __forceinline__ void arrive_and_flag(int* ctr, unsigned long long* f, unsigned long long val, int nwaves,
+                                                bool lane0 = (threadIdx.x & 63) == 0) {
+  if (lane0) {
     const int n = atomicAdd(ctr, 1);
     if (n == nwaves - 1) __hip_atomic_store(f, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -218,10 +219,11 @@ __device__ __forceinline__ void rotate_neg(float (&v)[8], const float2* cs, int 
 // may depend on the lane's group lane/16).  bf16: two ds_read_b64_tr_b16 (within
 // each 16-lane group, lane i supplies row r + i/4, columns c0 + 4*(i%4)..+3, and
 // lane l receives rows r..r+3 of column c0 + l).  fp32: eight scalar reads.
-__device__ __forceinline__ void frag_tr(Frag<bf16>& f, const bf16* base, int stride, int r0, int r1, int c0) {
+// (i: the lane's index within its 16-lane group, lane % 16)
+__device__ __forceinline__ void frag_tr(Frag<bf16>& f, const bf16* base, int stride, int r0, int r1, int c0,
+                                        int i = threadIdx.x & 15) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const int i = threadIdx.x & 15;
   const bf16* p0 = base + (r0 + (i >> 2)) * stride + c0 + 4 * (i & 3);
   const bf16* p1 = base + (r1 + (i >> 2)) * stride + c0 + 4 * (i & 3);
   const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);

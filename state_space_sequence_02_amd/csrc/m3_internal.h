@@ -51,6 +51,7 @@ struct PrefillPlan {
   int nc;             // chunks per sequence
   size_t off_flags, off_recs, off_maps, off_states, bytes;
   size_t lds;         // dynamic LDS per workgroup
+  int kernel;         // M3_KERNEL_PER_CHUNK or M3_KERNEL_STREAM
 };
 
 // Fills `plan` for a validated shape and entry point (gated readout,
@@ -106,6 +107,13 @@ bool prefill_variant_spills(const PrefillVariant& v);
 constexpr int kFusedAngleCap = 8192;
 size_t fused_lds_bytes(int Q, int R, int N, int P, int esize, int pro = 0);
 hipError_t launch_fused_prefill(const FusedParams& p, size_t lds, int dtype, hipStream_t stream);
+// The persistent streaming prefill (m3_stream.hip): the shapes it takes, its
+// LDS per workgroup, and its launch (one workgroup per compute unit; same
+// workspace layout and slot size as the per-chunk kernel, plus an exit
+// counter in the workspace's third 8-byte word).
+bool stream_supported(int dtype, int N, int P, int R, int Q, int gated, int pro);
+size_t stream_lds_bytes(int Q, int R, int N, int P);
+hipError_t launch_stream_prefill(const FusedParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Decode: one workgroup per (sequence, head).

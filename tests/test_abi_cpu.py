@@ -359,3 +359,47 @@ def test_backward_validation_codes(lib):
     assert call(ok, dx=FAR[0]) == 6                        # dx aliases x
     assert call(ok, dC=FAR[9] + 64) == 6                   # two outputs overlap
     assert call(m3.make_shape(2, 64, 3, 64, 128, 3, 0, 1)) == 2   # R = 3
+
+
+def test_prefill_kernel_choice(lib):
+    """m3_prefill_kernel_used: the streaming kernel for bf16, P = 64, N = 128
+    at R <= 4 with 128 or 256 (token, rank) rows per chunk that fit its LDS (at
+    N = 64 only when asked for); the per-chunk kernel for every other shape it
+    takes; 0 for refused shapes.  The debug selector restricts the choice and
+    rejects unknown values."""
+    S, C = m3.M3_KERNEL_STREAM, m3.M3_KERNEL_PER_CHUNK
+    k = lambda N, R, chunk, P=64, code=m3.M3_BF16: m3.prefill_kernel_used(
+        m3.make_shape(2, 1000, 4, P, N, R, chunk, code))
+    assert k(128, 4, 0) == S and k(128, 4, 64) == S and k(128, 4, 32) == S    # MIMO: 256 / 128 rows
+    assert k(128, 2, 64) == S and k(128, 1, 128) == S
+    assert k(64, 1, 0) == C and k(64, 1, 256) == C and k(64, 4, 32) == C     # N = 64: per-chunk by default
+    assert k(128, 4, 16) == C and k(128, 2, 32) == C                         # 64 rows
+    assert k(128, 2, 128) == 0                                               # its LDS fits neither kernel
+    assert k(128, 8, 32) == C and k(128, 4, 64, P=32) == C and k(32, 4, 64) == C
+    assert k(64, 1, 64, code=m3.M3_FP32) == C and k(128, 4, 64, code=m3.M3_FP32) == 0   # (fp32 N = 128: refused)
+    assert k(128, 4, 128) == 0 and k(256, 4, 0) == 0                         # refused shapes
+    try:
+        m3.debug_set_prefill_kernel(C)
+        assert k(128, 4, 0) == C and k(64, 1, 0) == C
+        m3.debug_set_prefill_kernel(S)
+        assert k(128, 4, 0) == S and k(64, 1, 0) == S and k(64, 1, 256) == S and k(64, 2, 64) == S
+        assert k(64, 1, 64) == C and k(64, 4, 64, P=32) == C
+        with pytest.raises(m3.M3Error):
+            m3.debug_set_prefill_kernel(7)
+        assert k(128, 4, 0) == S                                             # unchanged by the bad value
+    finally:
+        m3.debug_set_prefill_kernel(0)
+    assert k(128, 4, 0) == S
+
+
+def test_stream_kernels_use_no_scratch(lib):
+    """Every streaming prefill variant of this build is free of scratch memory
+    (the compiler report), so none is refused on that account."""
+    import json
+    path = os.path.join(os.path.dirname(m3.LIB_PATH), "..", "_build", "kernel_usage.json")
+    if not os.path.exists(path):
+        pytest.skip("no kernel usage report (build the library first)")
+    usage = json.load(open(path))
+    stream = {n: u for n, u in usage.items() if "stream_kernel" in n}
+    assert len(stream) == 20, sorted(stream)
+    assert all(u.get("scratch", 0) == 0 for u in stream.values()), {n: u for n, u in stream.items() if u.get("scratch")}
