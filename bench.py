@@ -213,14 +213,23 @@ def _timed(step, steps, warmup, reps=1):
     return out
 
 
-def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None, reps=1):
+def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None, reps=1, kernel=0):
     """One step = one m3_scan_prefill over the whole layer (all heads), with the
     final state exported; `nsets` input sets alternate so a step cannot be served
     from the last-level cache left warm by the previous one.  gate="fused": one
     m3_scan_prefill_gated (z, w_y, w_z) per step; gate="torch": m3_scan_prefill
     then the same readout in torch ops.  prologue="fused": one
     m3_scan_prefill_prologue (raw angles, B/C biases) per step; "torch": the
-    prologue in torch ops, then m3_scan_prefill."""
+    prologue in torch ops, then m3_scan_prefill.  kernel: 0 the library's choice,
+    or m3.M3_KERNEL_PER_CHUNK / M3_KERNEL_STREAM (m3_debug_set_prefill_kernel)."""
+    m3.debug_set_prefill_kernel(kernel)
+    try:
+        return _bench_prefill(w, steps, warmup, chunk, nsets, gate, prologue, reps)
+    finally:
+        m3.debug_set_prefill_kernel(0)
+
+
+def _bench_prefill(w, steps, warmup, chunk, nsets, gate, prologue, reps):
     dev = torch.device("cuda")
     sets = [inputs.make_prefill_inputs(w, seed=s, device=dev) for s in range(nsets)]
     if prologue:
@@ -245,6 +254,8 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None, 
     q_used = m3.prefill_chunk_used(shape, "gated" if gate == "fused" else "prologue" if prologue == "fused" else "plain")
     if q_used == 0:
         raise m3.M3Error(2, f"the library takes no chunk {chunk} for {w.name}")
+    kern = "stream_kernel" if (not gate and prologue != "fused" and
+                               m3.prefill_kernel_used(shape) == m3.M3_KERNEL_STREAM) else "prefill_kernel"
     ys = [torch.empty_like(s["x"]) for s in sets]
     hs = [torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
           for _ in sets]
@@ -281,7 +292,7 @@ def bench_prefill(w, steps, warmup, chunk=0, nsets=2, gate=None, prologue=None, 
     flops = tok * w.nheads * prefill_flops_per_token_head(w, q_used)
     del sets, ys, hs, ws
     msl = r["ms_launch"]
-    return dict(r, tokens_per_s=tok / (ms * 1e-3), chunk=q_used, bytes=nbytes, flops=flops,
+    return dict(r, tokens_per_s=tok / (ms * 1e-3), chunk=q_used, bytes=nbytes, flops=flops, kernel=kern,
                 gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
                 gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
@@ -417,7 +428,8 @@ def cpu_baseline(w, target_s=10.0):
                 value_1thread=(L1 / w.nheads) / el1)
 
 
-PREFILL_SOURCES = ["m3_fused_kernel.h", "m3_device.h", "m3_internal.h"]
+PREFILL_SOURCES = {"prefill_kernel": ["m3_fused_kernel.h", "m3_device.h", "m3_internal.h"],
+                   "stream_kernel": ["m3_stream.hip", "m3_fused_kernel.h", "m3_device.h", "m3_internal.h"]}
 DECODE_SOURCES = ["m3_decode.hip", "m3_device.h", "m3_internal.h"]
 
 
@@ -434,7 +446,7 @@ def prefill_chunk_for(w, requested):
 
 def prefill_line(w, rr):
     return dict(tokens_per_s_layer=rr["tokens_per_s"], us=round(rr["ms"] * 1e3, 1),
-                us_median=round(rr["ms_median"] * 1e3, 1), chunk=rr["chunk"],
+                us_median=round(rr["ms_median"] * 1e3, 1), chunk=rr["chunk"], kernel=rr["kernel"],
                 us_per_launch=round(rr["ms_launch"] * 1e3, 1),
                 hbm_frac=round(rr["gbs_launch"] / HBM_PEAK_GBS, 4),
                 mfma_frac=round(rr["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4))
@@ -488,10 +500,10 @@ def main():
         chunk = prefill_chunk_for(w, requested)
         r = bench_prefill(w, args.steps, args.warmup, chunk=chunk, reps=args.reps)
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
-        traffic = measured_traffic(f"prefill_kernel_{w.name}_q{r['chunk']}")
+        traffic = measured_traffic(f"{r['kernel']}_{w.name}_q{r['chunk']}")
         roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(r["gbs_launch"] / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="prefill_kernel",
+                    kernel=r["kernel"],
                     algorithmic_bytes_per_launch=r["bytes"],
                     us_per_launch=round(r["ms_launch"] * 1e3, 2),
                     mfma_tflops=round(r["tflops_launch"], 2),
@@ -521,6 +533,14 @@ def main():
             key = f"{name}_prefill" + ("_default_chunk" if q == 0 else "")
             sec[key] = prefill_line(wl, bench_prefill(wl, steps, max(2, args.warmup // 5),
                                                       chunk=prefill_chunk_for(wl, q)))
+        # the N = 128 workloads on the per-chunk kernel, beside the streaming
+        # kernel the library takes for them
+        for name in ("long", "mimo"):
+            wl = inputs.WORKLOADS[name]
+            steps = args.steps if name != "long" else max(3, args.steps // 4)
+            sec[f"{name}_prefill_per_chunk_kernel"] = prefill_line(
+                wl, bench_prefill(wl, steps, max(2, args.warmup // 5), chunk=prefill_chunk_for(wl, wl.chunk),
+                                  kernel=m3.M3_KERNEL_PER_CHUNK))
         wd = inputs.WORKLOADS["decode"]
         if args.workload != "decode":
             rd = bench_decode(wd, 200, 30)

@@ -418,6 +418,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
         const Ck nk = chunk_of(nticket);
         ntok0 = nk.tok0;
         nnt = nk.nt;
+        small_load(nk);   // the next chunk's scalars and angles, in flight from here
       }
       // stage block j + 1 (loaded PRE blocks ago) into the other slot, and
       // reuse its prefetch slot for block j + 1 + PRE of this chunk, or past
@@ -771,9 +772,8 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
         for (int e = 0; e < 4; ++e) yacc[pn][e] += e4[e] * ia[e];
       }
     }
-    // the next chunk's scalars, angles and C rows (cf is dead): in flight
-    // during the y stores and the next chunk's start
-    small_load(nck);
+    // the next chunk's C rows (cf is dead): in flight during the y stores and
+    // the next chunk's start (its scalars and angles went out at block kXStep)
     c_load(nck);
     if (vk) {
       T* Yg = static_cast<T*>(p->y) + tok0 * R * P;
