@@ -313,6 +313,7 @@ m3_status prefill_common(const m3_shape* s,
   f.batch = b; f.L = L; f.H = H; f.N = N; f.P = P; f.R = R; f.logR = ilog2(R);
   f.Q = plan.Q; f.nc = plan.nc;
   f.use_maps = 1;   // (the launch decides from the device's resident workgroups)
+  f.late_flag = 0;  // (likewise, for the streaming kernel)
   const hipError_t e = plan.kernel == M3_KERNEL_STREAM ? launch_stream_prefill(f, hs)
                                                        : launch_fused_prefill(f, lds, s->dtype, hs);
   if (e == hipErrorNotSupported) return M3_ERR_SHAPE;   // the loaded kernel uses scratch

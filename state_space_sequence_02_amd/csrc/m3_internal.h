@@ -70,6 +70,7 @@ struct FusedParams {
   unsigned spin_limit;       // polls a look-back wait makes before it gives up
   int batch, L, H, N, P, R, logR, Q, nc;
   int use_maps;          // publish chunk maps when the predecessor's state is late
+  int late_flag;         // streaming kernel: raise the state flag after the readout, not before
   int pro; float eps;    // prologue: B/C/B_prev column RMS norm (+ eps), angle = dt x theta
   const float* biasB; const float* biasC;             // prologue biases [H][R][N] (each may be NULL)
 };

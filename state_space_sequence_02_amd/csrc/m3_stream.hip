@@ -50,6 +50,10 @@ using namespace fused;
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+#ifndef M3_STREAM_MAP_GROUP
+#define M3_STREAM_MAP_GROUP 3
+#endif
+constexpr int kMapGroup = M3_STREAM_MAP_GROUP;   // maps loaded at once in the look-back
 
 // LDS: per-row data, cos/sin of Phi (then U while the look-back runs), the
 // two-slot ring (then S_in^T for the readout), every lane's C~ fragments
@@ -85,6 +89,23 @@ __device__ __forceinline__ KParams reload_params() {
   KParams kp = (KParams)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+s"(kp));
   return kp;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 inside each 16-lane row (lanes before the shift read 0), then
+// lane 15 of each row added into rows 1 and 3, then lane 31 into rows 2 and 3.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_mv(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, BOUND));
+}
+__device__ __forceinline__ float wave_scan_add(float v) {
+  v += dpp_mv<0x111, 0xF, true>(v);    // row_shr:1
+  v += dpp_mv<0x112, 0xF, true>(v);    // row_shr:2
+  v += dpp_mv<0x114, 0xF, true>(v);    // row_shr:4
+  v += dpp_mv<0x118, 0xF, true>(v);    // row_shr:8
+  v += dpp_mv<0x142, 0xA, false>(v);   // row_bcast:15, into rows 1 and 3
+  v += dpp_mv<0x143, 0xC, false>(v);   // row_bcast:31, into rows 2 and 3
+  return v;
 }
 
 // NBK: 32-row source blocks per chunk (Q * R = 32 NBK); PRE: blocks in flight;
@@ -156,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 
 
   Raw8<T> pre[PRE];
-  float dv, lmv, dnv, lmnv_raw;
+  float dv, lmv, dnv, lmnv_raw, av;
   float4 th4[ALEN];
   Raw8<T> craw[NK];
   struct Ck { int c, bh, h, nt; size_t tok0; };
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
     }
     raw_load_buf(r, ldB ? rB : rX, off);
   };
-  // the chunk's per-token scalars, angles and this wave's C rows
+  // the chunk's per-token scalars, its head's A, and its angles
   auto small_load = [&](const Ck& k) {
     const int nt = k.nt;
     const Rsrc rD = buf_rsrc(p->dt + k.tok0, nt > 0 ? (nt - 1) * tsb + 4 : 0);
@@ -240,6 +261,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
     lmv = buf_load_f32(rL, toff);
     dnv = buf_load_f32(rDn, toff);
     lmnv_raw = buf_load_f32(rLn, toff);
+    av = buf_load_f32(buf_rsrc(p->A, (uint32_t)p->H * 4), nt > 0 ? (uint32_t)k.h * 4 : kOff);   // A of the head
     const Rsrc rT = buf_rsrc(p->theta ? p->theta + k.tok0 * NH : nullptr, (p->theta && nt > 0) ? (nt - 1) * tsb * NH + NH * 4 : 0);
 #pragma unroll
     for (int j = 0; j < ALEN; ++j)
@@ -281,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       for (int u = 0; u < PRE; ++u) blk_load(pre[u], ck.tok0, ck.nt, u);
     }
     if (ticket >= total) break;
-    const int c = ck.c, bh = ck.bh, h = ck.h, nt = ck.nt;
+    const int c = ck.c, bh = ck.bh, nt = ck.nt;
     const int rows = nt * R;
     const int NB = (rows + 31) / 32;          // source blocks with valid rows
     const size_t tok0 = ck.tok0;
@@ -294,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       s_misc[4] = 0;   // wave counter: state published
       nextw = atomicAdd(p->ctl, 1ull);
     }
-    const float A = p->A[h];
+    const float A = av;   // (loaded with the scalars, one chunk ahead)
     const float lmnv = (c * Q + tid + 1 < p->L && tid < nt) ? lmnv_raw : 1.f;   // (only multiplies dnv = 0 otherwise)
 
     // ---- chunk-local cumulative log decay (token tid) and phases ----
@@ -304,11 +326,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       wv = gv + (1.f - lmnv) * dnv;
       lsc = dv * A;
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float u = __shfl_up(lsc, off);
-      if (lane >= off) lsc += u;
-    }
+    lsc = wave_scan_add(lsc);
 #pragma unroll
     for (int j = 1; j < ALEN; ++j) th4[j] = add4(th4[j], th4[j - 1]);
     const float4 atot = th4[ALEN - 1];
@@ -329,7 +347,11 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       l_end += t;
     }
     float4 abase = sub4(ainc, atot);
-    for (int w = 0; w < wave; ++w) abase = add4(abase, s_sega[w * NG + cg]);
+#pragma unroll
+    for (int w = 0; w < kWaves - 1; ++w) {   // (every read issued at once)
+      const float4 t = s_sega[w * NG + cg];
+      if (w < wave) abase = add4(abase, t);
+    }
     __syncthreads();   // scan scratch (in the ring) is dead after this
     if (tid < Q) {
       const float lv = lsc + lbase;
@@ -682,26 +704,42 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 #pragma unroll
           for (int jj = 0; jj < PTW; ++jj)
             if (pslot + WPN * jj < TPt) FU[i][jj] = buf_load_dev4(rS, slot_off(i, jj));
-        for (int j = sidx + 1; j < c; ++j) {
-          const size_t jid = (size_t)bh * p->nc + j;
-          const Rsrc rU = buf_rsrc(p->maps + jid * SLOT, SLOT * 4);
-          // the map's record (a_j, then cos/sin Psi_j per pair) through a
-          // uniform descriptor: 32-bit offsets, no per-lane 64-bit addresses
-          const Rsrc rR = buf_rsrc(p->recs + jid * (2 * NH + 2), (2 * NH + 2) * 4);
-          const float ax = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, 0, 0, kCpolDevice));
+        // kMapGroup maps' loads at once, then applied oldest first (a slot
+        // past c - 1 reloads map c - 1 and is not applied)
+        for (int j0 = sidx + 1; j0 < c; j0 += kMapGroup) {
+          float ax[kMapGroup];
+          f32x4 r4[kMapGroup][NPW], um[kMapGroup][NPW][PTW];
 #pragma unroll
-          for (int i = 0; i < NPW; ++i) {
-            const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
-            const f32x4 r4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, (uint32_t)(2 + n0) * 4, 0, kCpolDevice));
+          for (int g = 0; g < kMapGroup; ++g) {
+            const size_t jid = (size_t)bh * p->nc + min(j0 + g, c - 1);
+            const Rsrc rU = buf_rsrc(p->maps + jid * SLOT, SLOT * 4);
+            // the map's record (a_j, then cos/sin Psi_j per pair) through a
+            // uniform descriptor: 32-bit offsets, no per-lane 64-bit addresses
+            const Rsrc rR = buf_rsrc(p->recs + jid * (2 * NH + 2), (2 * NH + 2) * 4);
+            ax[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, 0, 0, kCpolDevice));
 #pragma unroll
-            for (int jj = 0; jj < PTW; ++jj) {
-              if (pslot + WPN * jj < TPt) {
-                const f32x4 u = buf_load_dev4(rU, slot_off(i, jj));
+            for (int i = 0; i < NPW; ++i) {
+              const int n0 = (nslot + NGRP * i) * 16 + 4 * g4;
+              r4[g][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, (uint32_t)(2 + n0) * 4, 0, kCpolDevice));
+#pragma unroll
+              for (int jj = 0; jj < PTW; ++jj)
+                um[g][i][jj] = pslot + WPN * jj < TPt ? buf_load_dev4(rU, slot_off(i, jj)) : zero4();
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < kMapGroup; ++g) {
+            if (j0 + g >= c) break;
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) {
+              const f32x4 q = r4[g][i];
+#pragma unroll
+              for (int jj = 0; jj < PTW; ++jj) {
+                const f32x4 u = um[g][i][jj];
                 f32x4& x = FU[i][jj];
-                const float x0 = ax * (r4[0] * x[0] - r4[1] * x[1]) + u[0];
-                const float x1 = ax * (r4[1] * x[0] + r4[0] * x[1]) + u[1];
-                const float x2 = ax * (r4[2] * x[2] - r4[3] * x[3]) + u[2];
-                const float x3 = ax * (r4[3] * x[2] + r4[2] * x[3]) + u[3];
+                const float x0 = ax[g] * (q[0] * x[0] - q[1] * x[1]) + u[0];
+                const float x1 = ax[g] * (q[1] * x[0] + q[0] * x[1]) + u[1];
+                const float x2 = ax[g] * (q[2] * x[2] - q[3] * x[3]) + u[2];
+                const float x3 = ax[g] * (q[3] * x[2] + q[2] * x[3]) + u[3];
                 x[0] = x0; x[1] = x1; x[2] = x2; x[3] = x3;
               }
             }
@@ -742,8 +780,11 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
         }
       }
     }
-    // the state flag goes up as soon as the stores are done
-    if (publish) {
+    // the state flag goes up once the stores are done: at once when the
+    // successor is likely waiting for it, else after the readout below, which
+    // runs while the stores complete
+    const bool late = p->late_flag != 0;
+    if (publish && !late) {
       mem_done();
       arrive_and_flag(&s_misc[4], flags + c, tag << 2 | 2u, kWaves, lane == 0);
     }
@@ -771,6 +812,10 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) yacc[pn][e] += e4[e] * ia[e];
       }
+    }
+    if (publish && late) {
+      mem_done();
+      arrive_and_flag(&s_misc[4], flags + c, tag << 2 | 2u, kWaves, lane == 0);
     }
     // the next chunk's C rows (cf is dead): in flight during the y stores and
     // the next chunk's start (its scalars and angles went out at block kXStep)
@@ -808,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 }
 
 template <int N, int P, int R, int NBK, int PRE, bool MAPS>
-hipError_t launch_v(const FusedParams& p, size_t grid, hipStream_t stream) {
+hipError_t launch_v(const FusedParams& p, size_t grid, bool late, hipStream_t stream) {
   constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P).total;
   const void* fn = reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, MAPS>);
   static std::atomic<int> scratch_state{0};   // 0 unknown, 1 none, 2 uses scratch
@@ -830,6 +875,7 @@ hipError_t launch_v(const FusedParams& p, size_t grid, hipStream_t stream) {
   }
   FusedParams q = p;
   q.use_maps = MAPS ? 1 : 0;
+  q.late_flag = late ? 1 : 0;
   hipLaunchKernelGGL((stream_kernel<N, P, R, NBK, PRE, MAPS>), dim3((unsigned)grid), dim3(kThreads), lds, stream, q);
   return hipGetLastError();
 }
@@ -855,10 +901,20 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
   }
   const size_t chunks = (size_t)p.batch * p.H * p.nc;
   const size_t grid = std::min(chunks, (size_t)resident);
-  // maps pay off when many chunks of one sequence are in flight at once (as
-  // for the per-chunk kernel): more resident workgroups than 4 per sequence
-  if ((size_t)resident > 4 * (size_t)p.batch * p.H) return launch_v<N, P, R, NBK, PRE, true>(p, grid, stream);
-  return launch_v<N, P, R, NBK, PRE, false>(p, grid, stream);
+  // maps pay off when many chunks of one sequence are in flight at once: more
+  // than 8 resident workgroups per sequence.  Without maps each chunk of a
+  // sequence waits for its predecessor's state, a hand-off of ~2.2-2.5 us at
+  // N = 128; with maps a chunk publishes its map and composes a run of them,
+  // ~1 us more per chunk.  Measured on 65,536-token sequences (N = 128, R = 4,
+  // 256 resident workgroups): 8 in flight, states only 4% faster; 16 and 32,
+  // maps 1.5 and 2.2 times faster.
+  if ((size_t)resident > 8 * (size_t)p.batch * p.H) return launch_v<N, P, R, NBK, PRE, true>(p, grid, false, stream);
+  // States only.  With at most 4 chunks of a sequence in flight the hand-off
+  // chain (~2.5 us a link) stays well inside the time a workgroup spends on its
+  // chunks, so a chunk's state flag waits for the end of its readout, and the
+  // state stores complete meanwhile instead of holding up the whole workgroup.
+  const bool late = (size_t)resident <= 4 * (size_t)p.batch * p.H;
+  return launch_v<N, P, R, NBK, PRE, false>(p, grid, late, stream);
 }
 
 }  // namespace stream
