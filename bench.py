@@ -468,6 +468,8 @@ def main():
     ap.add_argument("--workload", default="long", choices=["long", "siso", "mimo", "decode", "tiny"])
     ap.add_argument("--chunk", type=int, default=-1,
                     help="prefill tokens per chunk (-1: the configuration's; 0: library default)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "per_chunk", "stream"],
+                    help="prefill kernel of the headline line (auto: the one the library takes)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -498,7 +500,8 @@ def main():
     else:
         requested = w.chunk if args.chunk < 0 else args.chunk
         chunk = prefill_chunk_for(w, requested)
-        r = bench_prefill(w, args.steps, args.warmup, chunk=chunk, reps=args.reps)
+        kernel = {"auto": 0, "per_chunk": m3.M3_KERNEL_PER_CHUNK, "stream": m3.M3_KERNEL_STREAM}[args.kernel]
+        r = bench_prefill(w, args.steps, args.warmup, chunk=chunk, reps=args.reps, kernel=kernel)
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
         traffic = measured_traffic(f"{r['kernel']}_{w.name}_q{r['chunk']}")
         roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",

@@ -309,8 +309,11 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
     const size_t tok0 = ck.tok0;
     unsigned long long* flags = p->flags + (size_t)bh * p->nc;
     __syncthreads();   // the previous chunk's output stage is done with s_row, S_in^T and s_misc
-    // the next ticket: taken now, read by everyone after loop step kXStep - 1
-    unsigned long long nextw = 0;
+    // the next ticket: taken now, read by everyone after loop step kXStep - 1.
+    // Nothing is computed from the atomic's result before then (it goes to LDS
+    // whole, both words, so neither register of it is reused meanwhile;
+    // readers mask it), so no wait for it is placed here.
+    unsigned long long nextw;
     if (tid == 0) {
       s_misc[3] = 0;   // wave counter: map published
       s_misc[4] = 0;   // wave counter: state published
@@ -434,9 +437,9 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 #pragma unroll
      for (int u = 0; u < PRE; ++u) {
       const int j = jb + u;
-      if (j == kXStep - 1 && tid == 0) s_misc[8] = (int)(unsigned)(nextw & kTicketMask);
+      if (j == kXStep - 1 && tid == 0) *reinterpret_cast<unsigned long long*>(s_misc + 8) = nextw;
       if (j == kXStep) {
-        nticket = (unsigned)__builtin_amdgcn_readfirstlane(s_misc[8]);
+        nticket = (unsigned)__builtin_amdgcn_readfirstlane(s_misc[8]) & (unsigned)kTicketMask;
         const Ck nk = chunk_of(nticket);
         ntok0 = nk.tok0;
         nnt = nk.nt;
@@ -817,8 +820,9 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       mem_done();
       arrive_and_flag(&s_misc[4], flags + c, tag << 2 | 2u, kWaves, lane == 0);
     }
-    // the next chunk's C rows (cf is dead): in flight during the y stores and
-    // the next chunk's start (its scalars and angles went out at block kXStep)
+    // the next chunk's C rows (cf is dead), after the state flag (the wait
+    // before a flag covers every load in flight): in flight during the y
+    // stores and the next chunk's start
     c_load(nck);
     if (vk) {
       T* Yg = static_cast<T*>(p->y) + tok0 * R * P;
