@@ -250,12 +250,16 @@ def _bench_prefill(w, steps, warmup, chunk, nsets, gate, prologue, reps):
                 for _ in sets]
     dcode = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
     shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, chunk, dcode)
-    ws = torch.zeros(m3.prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(m3.prefill_prologue_workspace_bytes(shape) if prologue == "fused" else
+                     m3.prefill_workspace_bytes(shape), dtype=torch.uint8, device=dev)
     q_used = m3.prefill_chunk_used(shape, "gated" if gate == "fused" else "prologue" if prologue == "fused" else "plain")
     if q_used == 0:
         raise m3.M3Error(2, f"the library takes no chunk {chunk} for {w.name}")
-    kern = "stream_kernel" if (not gate and prologue != "fused" and
+    staged = prologue == "fused" and m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_STAGED
+    kern = "stream_kernel" if (not gate and (prologue != "fused" or staged) and
                                m3.prefill_kernel_used(shape) == m3.M3_KERNEL_STREAM) else "prefill_kernel"
+    if staged:
+        kern = "prologue stage + " + kern
     ys = [torch.empty_like(s["x"]) for s in sets]
     hs = [torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
           for _ in sets]
@@ -576,14 +580,17 @@ def main():
                                             "could be served from the 256 MB last-level cache")
         rg = bench_decode(wd, 200, 30, gated=True)
         sec["mimo_decode_gated"] = decode_line(wd, rg)
-        # the fused prologue (BCNorm + B/C biases + angle = dt x raw angle), and
-        # the prefill's unfused alternative (the prologue in torch ops first);
-        # on the SISO workload: the library refuses the N = 128 prologue prefill
-        # (its kernel variants keep a few values in scratch memory)
-        ws_ = inputs.WORKLOADS["siso"]
-        pf = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="fused")
-        pt = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="torch")
-        sec["siso_prefill_prologue"] = dict(prefill_line(ws_, pf), us_unfused_torch_prologue=round(pt["ms"] * 1e3, 1))
+        # the prologue (BCNorm + B/C biases + angle = dt x raw angle) through
+        # m3_scan_prefill_prologue, and the unfused alternative (the prologue in
+        # torch ops first): fused into the prefill kernel on the SISO workload;
+        # staged before the (streaming) prefill on the MIMO workload, whose fused
+        # N = 128 variant keeps a few values in scratch memory and is not launched
+        for name in ("siso", "mimo"):
+            ws_ = inputs.WORKLOADS[name]
+            pf = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="fused")
+            pt = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="torch")
+            sec[f"{name}_prefill_prologue"] = dict(prefill_line(ws_, pf),
+                                                   us_unfused_torch_prologue=round(pt["ms"] * 1e3, 1))
         rp = bench_decode(wd, 200, 30, prologue=True)
         sec["mimo_decode_prologue"] = decode_line(wd, rp)
         # the backward of the recurrence (every gradient), at the SISO and MIMO

@@ -74,8 +74,9 @@ typedef struct {
     int32_t dtype;
 } m3_shape;
 
-/* Bytes of device workspace m3_scan_prefill, m3_scan_prefill_gated and
- * m3_scan_prefill_prologue need for this shape (the largest of the three; 0 on an
+/* Bytes of device workspace m3_scan_prefill, m3_scan_prefill_gated and the
+ * fused form of m3_scan_prefill_prologue need for this shape (the largest of
+ * the three; the staged prologue needs more: m3_prefill_prologue_workspace_bytes; 0 on an
  * invalid or unsupported shape, including one of more than 2^26 - 1
  * chunks).  The buffer holds a control word (ticket count and call epoch) at
  * offset 0, a sticky error word at offset 8 (see m3_prefill_status), per-chunk
@@ -110,10 +111,10 @@ int32_t m3_prefill_chunk_used(const m3_shape* s);
  * s->chunk, or 0 when it takes none. */
 int32_t m3_prefill_max_chunk(const m3_shape* s);
 
-/* m3_prefill_chunk_used for m3_scan_prefill_gated and for
- * m3_scan_prefill_prologue (which have kernel variants, and the prologue
- * limits, of their own): the chunk each will use, or 0 when it refuses the
- * shape. */
+/* m3_prefill_chunk_used for m3_scan_prefill_gated (which has kernel variants
+ * of its own) and for m3_scan_prefill_prologue (its fused variant's chunk, or
+ * in the staged form m3_scan_prefill's): the chunk each will use, or 0 when it
+ * refuses the shape. */
 int32_t m3_prefill_gated_chunk_used(const m3_shape* s);
 int32_t m3_prefill_prologue_chunk_used(const m3_shape* s);
 
@@ -317,15 +318,34 @@ typedef struct {
     const float* bias_C;    /* [H, R, N] fp32 added to C after the norm, or NULL */
 } m3_prologue;
 
-/* m3_scan_prefill with the fused prologue applied to B, C, B_prev and theta
- * inside the kernel's load stage.  pro must not be NULL (M3_ERR_NULL).  The
- * bias tables take R x (2N + 4) x 4 bytes of LDS per workgroup beside the chunk's
- * tiles; a shape whose tiles leave too little room gets M3_ERR_SHAPE, and so
- * does a chunk of more than 128 (token, rank) rows for N <= 64 or 256 for
- * N = 128 (the default chunks never are).  fp32 inputs take N <= 64 only
- * (M3_ERR_SHAPE at N = 128); bf16 inputs every N the prefill takes.  The workspace is the one
- * m3_prefill_workspace_bytes gives for the shape.  Everything else as
+/* m3_scan_prefill with the prologue applied to B, C, B_prev and theta.  It
+ * takes every shape m3_scan_prefill takes, in one of two forms
+ * (m3_prefill_prologue_mode):
+ *   M3_PROLOGUE_FUSED   the prologue runs inside the prefill kernel's load
+ *                       stage (one launch; its bias tables take R x (2N + 4) x 4
+ *                       bytes of LDS beside the chunk's tiles).  Used where
+ *                       that kernel variant exists and uses no scratch memory:
+ *                       bf16 or fp32 inputs at N <= 64 and bf16 at N = 128 with
+ *                       P <= 32, at chunks of one 16-row output tile per wave;
+ *   M3_PROLOGUE_STAGED  elsewhere: a prologue kernel writes the normalized B,
+ *                       C, B_prev and the angles dt x theta into the workspace
+ *                       (the inputs' layouts and dtype, bf16 rounded to nearest
+ *                       even; angles fp32), then the plain prefill runs on them
+ *                       with the chunk m3_scan_prefill takes.  The results equal
+ *                       the fused form's up to that rounding.
+ * pro must not be NULL (M3_ERR_NULL).  The workspace must hold
+ * m3_prefill_prologue_workspace_bytes(s) bytes (M3_ERR_WORKSPACE), zero-filled
+ * before its first use as for m3_scan_prefill, and in the staged form it must
+ * not overlap any input, y or h_out (M3_ERR_ALIAS).  Everything else as
  * m3_scan_prefill. */
+enum { M3_PROLOGUE_FUSED = 1, M3_PROLOGUE_STAGED = 2 };
+int32_t m3_prefill_prologue_mode(const m3_shape* s);   /* 0 when the shape is refused */
+/* Bytes of workspace m3_scan_prefill_prologue needs for this shape (never less
+ * than m3_prefill_workspace_bytes, so one buffer serves every prefill entry
+ * point; 0 when the shape is refused).  In the staged form it adds, behind the
+ * plain prefill's part, b x L x H x R x N elements each for B and C,
+ * b x H x R x N for B_prev and b x L x H x N/2 fp32 angles. */
+size_t m3_prefill_prologue_workspace_bytes(const m3_shape* s);
 m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,
                                    const void* x, const void* B, const void* C,
                                    const float* dt, const float* A, const float* lam,

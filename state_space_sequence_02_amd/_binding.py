@@ -25,8 +25,10 @@ EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_prefill_ma
            "m3_scan_prefill_gated", "m3_decode_step", "m3_decode_step_bf16_state",
            "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
            "m3_prefill_kernel_used", "m3_debug_set_prefill_kernel",
+           "m3_prefill_prologue_mode", "m3_prefill_prologue_workspace_bytes",
            "m3_status_str", "m3_version")
 M3_KERNEL_PER_CHUNK, M3_KERNEL_STREAM = 1, 2
+M3_PROLOGUE_FUSED, M3_PROLOGUE_STAGED = 1, 2
 
 
 class M3Shape(ctypes.Structure):
@@ -90,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.m3_scan_prefill_gated.argtypes = [sp] + [vp] * 16 + [sz, vp]
     lib.m3_decode_step_gated.restype = ctypes.c_int
     lib.m3_decode_step_gated.argtypes = [sp] + [vp] * 15
+    lib.m3_prefill_prologue_mode.restype = ctypes.c_int32
+    lib.m3_prefill_prologue_mode.argtypes = [sp]
+    lib.m3_prefill_prologue_workspace_bytes.restype = sz
+    lib.m3_prefill_prologue_workspace_bytes.argtypes = [sp]
     lib.m3_scan_prefill_prologue.restype = ctypes.c_int
     lib.m3_scan_prefill_prologue.argtypes = [sp, ctypes.POINTER(M3Prologue)] + [vp] * 13 + [sz, vp]
     lib.m3_decode_step_prologue.restype = ctypes.c_int
@@ -148,6 +154,16 @@ def prefill_chunk_used(shape: M3Shape, variant: str = "plain") -> int:
     fn = {"plain": "m3_prefill_chunk_used", "gated": "m3_prefill_gated_chunk_used",
           "prologue": "m3_prefill_prologue_chunk_used"}[variant]
     return int(getattr(load_library(), fn)(ctypes.byref(shape)))
+
+
+def prefill_prologue_mode(shape: M3Shape) -> int:
+    """m3_prefill_prologue_mode: M3_PROLOGUE_FUSED (1), M3_PROLOGUE_STAGED (2),
+    or 0 when m3_scan_prefill_prologue refuses the shape."""
+    return int(load_library().m3_prefill_prologue_mode(ctypes.byref(shape)))
+
+
+def prefill_prologue_workspace_bytes(shape: M3Shape) -> int:
+    return int(load_library().m3_prefill_prologue_workspace_bytes(ctypes.byref(shape)))
 
 
 def prefill_max_chunk(shape: M3Shape) -> int:
@@ -277,10 +293,12 @@ def _prologue(eps, bias_B, bias_C, dev):
 def scan_prefill_prologue(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None, x_prev=None,
                           y=None, h_out=None, chunk: int = 0, workspace=None, want_state: bool = True,
                           eps: float = 1e-6, bias_B=None, bias_C=None):
-    """Chunked prefill with the fused prologue (m3_scan_prefill_prologue): B, C
+    """Chunked prefill with the prologue (m3_scan_prefill_prologue; fused into
+    the prefill kernel or staged before it, see prefill_prologue_mode): B, C
     and B_prev RMS-normalised per column over N (+ eps) plus bias_B / bias_C
     [H,R,N] fp32 (or None); theta holds raw angles, the step angle being
-    dt * theta.  Other arguments as scan_prefill.  Returns (y, h_out)."""
+    dt * theta.  Other arguments as scan_prefill; a workspace passed in must
+    hold prefill_prologue_workspace_bytes.  Returns (y, h_out)."""
     lib = load_library()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -290,7 +308,7 @@ def scan_prefill_prologue(x, B, C, dt, A, lam, theta=None, h0=None, B_prev=None,
         y = torch.empty_like(x)
     if h_out is None and want_state:
         h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
-    need = int(lib.m3_prefill_workspace_bytes(ctypes.byref(shape)))
+    need = int(lib.m3_prefill_prologue_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     f32 = torch.float32

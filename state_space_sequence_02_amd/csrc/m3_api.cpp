@@ -155,6 +155,34 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro) {
   return true;
 }
 
+// The prologue prefill in one of two forms: fused into the prefill's load
+// stage (the shape's prologue kernel variant), or, where the library does not
+// launch that variant, staged: a prologue kernel writes the normalized B, C,
+// B_prev and the angles dt x theta into the workspace behind the plain
+// prefill's part, and the plain prefill runs on them.  The staged form takes
+// every shape the plain prefill takes.
+struct StagedLayout { size_t off_B, off_C, off_Bp, off_phi, bytes; };
+
+StagedLayout staged_layout(const m3_shape& s, const PrefillPlan& plain) {
+  const size_t es = esize(s.dtype), tok = (size_t)s.batch * s.seqlen * s.nheads, bh = (size_t)s.batch * s.nheads;
+  const size_t rowsz = (size_t)s.rank * s.dstate * es;
+  StagedLayout o;
+  o.off_B = align256(plain.bytes);
+  o.off_C = align256(o.off_B + tok * rowsz);
+  o.off_Bp = align256(o.off_C + tok * rowsz);
+  o.off_phi = align256(o.off_Bp + bh * rowsz);
+  o.bytes = align256(o.off_phi + tok * (s.dstate / 2) * sizeof(float));
+  return o;
+}
+
+// M3_PROLOGUE_FUSED or M3_PROLOGUE_STAGED with that form's plan, or 0 when
+// the shape is refused.
+int prologue_mode(const m3_shape& s, PrefillPlan* plan) {
+  if (plan_prefill(s, plan, 0, 1)) return M3_PROLOGUE_FUSED;
+  if (plan_prefill(s, plan, 0, 0)) return M3_PROLOGUE_STAGED;
+  return 0;
+}
+
 }  // namespace m3
 
 using namespace m3;
@@ -190,8 +218,23 @@ int32_t m3_prefill_gated_chunk_used(const m3_shape* s) {
 int32_t m3_prefill_prologue_chunk_used(const m3_shape* s) {
   if (check_common(s, true) != M3_OK) return 0;
   PrefillPlan plan;
-  if (!plan_prefill(*s, &plan, 0, 1)) return 0;
+  if (!prologue_mode(*s, &plan)) return 0;
   return plan.Q;
+}
+
+int32_t m3_prefill_prologue_mode(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  return prologue_mode(*s, &plan);
+}
+
+size_t m3_prefill_prologue_workspace_bytes(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  const int mode = prologue_mode(*s, &plan);
+  if (!mode) return 0;
+  const size_t own = mode == M3_PROLOGUE_STAGED ? staged_layout(*s, plan).bytes : plan.bytes;
+  return std::max(own, m3_prefill_workspace_bytes(s));
 }
 
 int32_t m3_prefill_max_chunk(const m3_shape* s) {
@@ -581,8 +624,53 @@ m3_status m3_scan_prefill_prologue(const m3_shape* s, const m3_prologue* pro,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream) {
   if (!pro) return M3_ERR_NULL;
-  return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, Gate{false, nullptr, nullptr, nullptr},
-                        Pro{true, pro->eps, pro->bias_B, pro->bias_C}, y, h_out, workspace, workspace_bytes, stream);
+  const Gate nog{false, nullptr, nullptr, nullptr};
+  m3_status st = check_common(s, true);
+  if (st != M3_OK) return st;
+  PrefillPlan plan;
+  const int mode = prologue_mode(*s, &plan);
+  const size_t bh = (size_t)s->batch * s->nheads;
+  if (mode != M3_PROLOGUE_STAGED || bh == 0 || s->seqlen == 0)   // (no rows to stage: nothing differs)
+    return prefill_common(s, x, B, C, dt, A, lam, theta, h0, B_prev, x_prev, nog,
+                          Pro{true, pro->eps, pro->bias_B, pro->bias_C}, y, h_out, workspace, workspace_bytes, stream);
+  // staged: the prologue kernel, then the plain prefill on its results
+  if (!x || !B || !C || !dt || !A || !lam || !y) return M3_ERR_NULL;
+  if ((B_prev == nullptr) != (x_prev == nullptr)) return M3_ERR_NULL;
+  const StagedLayout lay = staged_layout(*s, plan);
+  if (!workspace || workspace_bytes < lay.bytes) return M3_ERR_WORKSPACE;
+  const int L = s->seqlen, H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
+  const size_t es = esize(s->dtype), tok = (size_t)s->batch * L * H;
+  const size_t ybytes = tok * R * P * es, sbytes = bh * N * P * sizeof(float);
+  // the workspace is written before the prefill reads it: it must not overlap
+  // any input, nor y or h_out (which the prefill checks against the inputs it
+  // is given, the staged ones; the original B, C, B_prev, angles and bias
+  // tables are checked here)
+  struct { const void* p; size_t n; } ins[] = {
+      {x, tok * R * P * es}, {B, tok * R * N * es}, {C, tok * R * N * es},
+      {dt, tok * sizeof(float)}, {A, (size_t)H * sizeof(float)}, {lam, tok * sizeof(float)},
+      {theta, theta ? tok * (N / 2) * sizeof(float) : 0}, {h0, h0 ? sbytes : 0},
+      {B_prev, bh * R * N * es}, {x_prev, bh * R * P * es},
+      {pro->bias_B, pro->bias_B ? (size_t)H * R * N * sizeof(float) : 0},
+      {pro->bias_C, pro->bias_C ? (size_t)H * R * N * sizeof(float) : 0}};
+  for (const auto& in : ins) {
+    if (overlaps(workspace, lay.bytes, in.p, in.n)) return M3_ERR_ALIAS;
+    if (overlaps(y, ybytes, in.p, in.n)) return M3_ERR_ALIAS;
+    if (h_out && in.p != h0 && overlaps(h_out, sbytes, in.p, in.n)) return M3_ERR_ALIAS;
+  }
+  if (overlaps(workspace, lay.bytes, y, ybytes) || (h_out && overlaps(workspace, lay.bytes, h_out, sbytes)))
+    return M3_ERR_ALIAS;
+  char* ws = static_cast<char*>(workspace);
+  PrologueStage ps;
+  ps.dtype = s->dtype; ps.N = N; ps.H = H; ps.R = R;
+  ps.tokens = tok; ps.pairs = bh; ps.eps = pro->eps;
+  ps.B = B; ps.C = C; ps.Bp = B_prev; ps.dt = dt; ps.theta = theta;
+  ps.biasB = pro->bias_B; ps.biasC = pro->bias_C;
+  ps.Bn = ws + lay.off_B; ps.Cn = ws + lay.off_C;
+  ps.Bpn = B_prev ? ws + lay.off_Bp : nullptr;
+  ps.phi = theta ? reinterpret_cast<float*>(ws + lay.off_phi) : nullptr;
+  if (launch_prologue_stage(ps, static_cast<hipStream_t>(stream)) != hipSuccess) return M3_ERR_DEVICE;
+  return prefill_common(s, x, ps.Bn, ps.Cn, dt, A, lam, ps.phi, h0, ps.Bpn, x_prev, nog, kNoPro, y, h_out,
+                        workspace, plan.bytes, stream);
 }
 
 const char* m3_status_str(m3_status st) {

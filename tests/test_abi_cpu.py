@@ -178,17 +178,35 @@ def test_prologue_validation_codes(lib):
     assert prefill(ok, y=FAR[11] + 8) == 6       # y overlaps the B bias table
     assert prefill(ok, ws=None) == 4
     assert prefill(m3.make_shape(2, 128, 3, 64, 256, 4, 64, 1)) == 2      # N = 256: decode only
-    # more than one 16-row output tile per wave (chunk above the default): rejected
-    assert prefill(m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1)) == 2
-    assert prefill(m3.make_shape(2, 512, 3, 64, 64, 2, 128, 1)) == 2
-    assert prefill(m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1)) == 2
-    assert prefill(m3.make_shape(2, 128, 3, 64, 64, 4, 64, 1)) == 2   # 256 rows: two tiles per wave
-    for R, q in ((1, 256), (2, 128), (4, 64)):   # the chunk query agrees with the call
-        assert m3.prefill_chunk_used(m3.make_shape(2, 512, 3, 64, 64, R, q, 1), "prologue") == 0
-        assert m3.prefill_chunk_used(m3.make_shape(2, 512, 3, 64, 64, R, q, 1)) == q
-    # fp32 inputs at N = 128: rejected
-    assert prefill(m3.make_shape(2, 128, 3, 32, 128, 1, 0, m3.M3_FP32)) == 2
-    assert prefill(m3.make_shape(2, 128, 3, 64, 128, 4, 0, m3.M3_FP32)) == 2
+    assert m3.prefill_prologue_mode(ok) == m3.M3_PROLOGUE_FUSED
+    # more than one 16-row output tile per wave (chunk above the default), and
+    # the bf16 MIMO shape at N = 128: no fused variant is launched there, so
+    # the prologue is staged before the plain prefill, at the plain chunk
+    for shape in (m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1), m3.make_shape(2, 512, 3, 64, 64, 2, 128, 1),
+                  m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1), m3.make_shape(2, 128, 3, 64, 64, 4, 64, 1),
+                  m3.make_shape(4, 4096, 32, 64, 128, 4, 0, 1)):
+        assert m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_STAGED
+        q = m3.prefill_chunk_used(shape)
+        assert q > 0 and m3.prefill_chunk_used(shape, "prologue") == q
+        need = m3.prefill_prologue_workspace_bytes(shape)
+        assert need > m3.prefill_workspace_bytes(shape) > 0
+        b, L, H, P, N, R, es = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, shape.rank, 2
+        assert need >= m3.prefill_workspace_bytes(shape) + (2 * b * L * H * R * N + b * H * R * N) * es + b * L * H * N // 2 * 4
+    st = m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1)
+    need = m3.prefill_prologue_workspace_bytes(st)
+    assert prefill(st, p=None) == 1
+    assert prefill(st, ws=None) == 4
+    assert prefill(st, wsb=need - 1) == 4             # the staged rows need the larger workspace
+    assert prefill(st, wsb=need, ws=FAR[1]) == 6      # the workspace overlaps B
+    assert prefill(st, wsb=need, ws=FAR[11] - 64) == 6   # ... or a bias table
+    assert prefill(st, wsb=need, y=FAR[10] + 64) == 6    # y overlaps the workspace
+    assert prefill(st, wsb=need, y=FAR[12]) == 6      # y aliases the C bias table
+    assert prefill(st, wsb=need, Bp=FAR[13]) == 1     # B_prev without x_prev
+    # shapes the plain prefill refuses are refused in both forms
+    for shape in (m3.make_shape(2, 128, 3, 32, 128, 1, 0, m3.M3_FP32), m3.make_shape(2, 128, 3, 64, 256, 4, 0, 1)):
+        if m3.prefill_chunk_used(shape) == 0:
+            assert m3.prefill_prologue_mode(shape) == 0 and m3.prefill_prologue_workspace_bytes(shape) == 0
+            assert prefill(shape) == 2
     dec = m3.make_shape(4, 1, 2, 64, 128, 4, 0, m3.M3_BF16)
     assert decode(dec, p=None) == 1
     assert decode(dec, y=FAR[12]) == 6           # y aliases the C bias table
@@ -273,7 +291,11 @@ def test_prefill_refuses_scratch_variants(lib):
                             s = m3.make_shape(1, 300, 2, P, N, R, chunk, code)
                             q = m3.prefill_chunk_used(s, variant)
                             if q:
-                                assert (code, N, P, R, _row_tiles(q, R, N), g, pro) not in spills
+                                # the staged prologue runs the plain prefill's variant
+                                staged = pro and m3.prefill_prologue_mode(s) == m3.M3_PROLOGUE_STAGED
+                                assert (code, N, P, R, _row_tiles(q, R, N), g, 0 if staged else pro) not in spills
+                                if pro:
+                                    assert q == (m3.prefill_chunk_used(s) if staged else q)
     from state_space_sequence_02_amd import inputs
     for name in ("tiny", "siso", "mimo", "long"):
         w = inputs.WORKLOADS[name]

@@ -44,14 +44,16 @@ NO_PREFILL = {("fp32", 128, 128, 8)}
 # of them (bf16 P=64 R=4) made a GPU memory fault whose cause was not found, so
 # the path was taken out of the library
 N256_SKIP = "N=256 prefill is not built (heavy scratch spills; one unexplained GPU memory fault)"
-# The library refuses (M3_ERR_SHAPE, nothing launched) every prefill kernel
-# variant the build's compiler report gives scratch memory, and the prologue
-# prefill with two or more output tiles per wave or with fp32 inputs at
-# N = 128: all the GPU memory faults met in this kernel's development (one of
-# them a prologue variant with two tiles per wave, bf16 N=64 P=64 R=2, another
-# an fp32 N=128 P=32 R=1 prologue variant) and the one wrong result came from
-# spilling variants, with causes not established.  A refused case checks that
-# the call raises before any launch.
+# The library never launches a prefill kernel variant the build's compiler
+# report gives scratch memory, nor a fused prologue variant with two or more
+# output tiles per wave or with fp32 inputs at N = 128: all the GPU memory
+# faults met in this kernel's development (one of them a prologue variant with
+# two tiles per wave, bf16 N=64 P=64 R=2, another an fp32 N=128 P=32 R=1
+# prologue variant) and the one wrong result came from spilling variants, with
+# causes not established.  Where the plain prefill's variant is refused the
+# shape is refused (M3_ERR_SHAPE, nothing launched; a refused case checks that
+# the call raises); where only the fused prologue's is, the prologue entry
+# point stages the prologue before the plain prefill, and the grid runs it.
 
 
 def _taken(dtype, N, P, R, chunk, variant):

@@ -72,10 +72,16 @@ def test_decode_prologue(shape, biases):
 PREFILL = [
     # (workload, overrides, chunk, biases, carry)
     ("siso", dict(batch=2, seqlen=300, nheads=3), 64, True, True),
-    # two output tiles per wave: refused on the host (the prologue's variants
-    # with more than one tile per wave spilled to scratch and one of them made
-    # a GPU memory fault whose cause was not established)
+    # two output tiles per wave: no fused variant is launched (the prologue's
+    # variants with more than one tile per wave spilled to scratch, and one of
+    # them made a GPU memory fault whose cause was not established), so the
+    # prologue is staged before the plain prefill
     ("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),
+    ("siso", dict(batch=2, seqlen=200, nheads=2, rank=2), 128, True, True),
+    # the bf16 MIMO shape at N = 128 (its fused variant spills): staged, and the
+    # plain prefill it runs is the streaming kernel
+    ("mimo", dict(batch=2, seqlen=300, nheads=3), 0, True, True),
+    ("mimo", dict(batch=1, seqlen=129, nheads=2), 64, False, False),
     ("siso", dict(batch=2, seqlen=200, nheads=2), 128, False, False),
     ("mimo", dict(batch=2, seqlen=130, nheads=2), 64, True, True),
     ("mimo", dict(batch=1, seqlen=97, nheads=2), 32, False, True),
@@ -99,15 +105,18 @@ def test_prefill_prologue(case):
     th, bb, bc = _pro_inputs(w, seed + 2, (w.batch, w.seqlen), biases)
     dg, cg = dev_inputs(d), (dev_inputs(c) if c else {})
     if taken_chunk(w, chunk, "prologue") == 0:
-        # refused on the host: two or more output tiles per wave, or a kernel
-        # variant the build report gives scratch memory (at N = 128 the prologue
-        # variants keep a few values in scratch)
+        # refused on the host: only where the plain prefill refuses the shape
+        # too (the staged form takes every shape the plain prefill takes)
+        assert taken_chunk(w, chunk) == 0
         note(f"prefill prologue {name} {kw} chunk={chunk}: refused on the host")
         with pytest.raises(m3.M3Error, match="M3_ERR_SHAPE"):
             m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
                                      chunk=chunk, eps=eps)
         return
-    note(f"prefill prologue {name} {kw} {w.dtype} chunk={chunk} biases={biases} carry={carry}")
+    code = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+    mode = m3.prefill_prologue_mode(m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank,
+                                                  chunk, code))
+    note(f"prefill prologue {name} {kw} {w.dtype} chunk={chunk} biases={biases} carry={carry} mode={mode}")
     y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
                                     chunk=chunk, eps=eps, bias_B=None if bb is None else bb.cuda(),
                                     bias_C=None if bc is None else bc.cuda())
