@@ -115,3 +115,26 @@ def test_backward_without_dh_and_empty_sequence():
     g0 = m3.scan_backward(**{k: d0[k] for k in KEYS}, **cg, dy=torch.empty_like(d0["x"]), dh_out=dho)
     torch.cuda.synchronize()
     assert torch.equal(g0["h0"], dho) and not g0["A"].any() and not g0["B_prev"].any()
+
+
+@pytest.mark.parametrize("name", ["siso", "mimo"])
+def test_backward_full_size(name):
+    """The benchmarked shapes (4 x 4,096 tokens x 32 heads; SISO N = 64 and
+    MIMO N = 128, R = 4), every head run on the GPU in the launch bench.py
+    times, with an incoming state and previous write; every gradient of two
+    heads (all four sequences, so dA of those heads is complete) compared with
+    the oracle."""
+    w = inputs.workload(name)
+    d, c, dy, dho = _case(w, seed=5100 + w.rank, carry=True, rotation=True)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note(f"backward full size {name}")
+    got = m3.scan_backward(**{k: dg[k] for k in KEYS}, **cg, dy=dy.cuda(), dh_out=dho.cuda())
+    torch.cuda.synchronize()
+    heads = [0, w.nheads - 1]
+    tok = lambda t: t[:, :, heads]           # [b, L, H, ...] arrays
+    seq = lambda t: t[:, heads]              # [b, H, ...] arrays
+    sub_d = {k: (None if v is None else v[heads] if k == "A" else tok(v)) for k, v in d.items()}
+    sub_c = {k: seq(v) for k, v in c.items()}
+    sub_got = {k: (None if v is None else v[heads] if k == "A" else
+                   seq(v) if k in ("h0", "B_prev", "x_prev") else tok(v)) for k, v in got.items()}
+    _check(w, sub_d, sub_c, tok(dy), seq(dho), sub_got)

@@ -185,3 +185,30 @@ def test_fused_entry_points_edges():
     torch.cuda.synchronize()
     assert out0.numel() == 0 and y0.numel() == 0
     assert torch.equal(h0, cg["h0"]) and torch.equal(h1, cg["h0"])
+
+
+def test_prefill_prologue_full_size_staged():
+    """The MIMO workload at full size (4 x 4,096 tokens x 32 heads, N = 128,
+    R = 4) through m3_scan_prefill_prologue: the staged form (its fused
+    variant is not launched) followed by the streaming prefill, every head run;
+    y and the final state of two heads compared with the oracle."""
+    w = inputs.workload("mimo")
+    code = m3.M3_BF16
+    assert m3.prefill_prologue_mode(m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0,
+                                                  code)) == m3.M3_PROLOGUE_STAGED
+    d = inputs.make_prefill_inputs(w, seed=811)
+    c = inputs.random_carry(w, seed=812)
+    th, bb, bc = _pro_inputs(w, 813, (w.batch, w.seqlen), True)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note("prefill prologue full size mimo (staged)")
+    y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
+                                    eps=1e-5, bias_B=bb.cuda(), bias_C=bc.cuda())
+    torch.cuda.synchronize()
+    heads = [0, w.nheads - 1]
+    tk = lambda t: _np(t[:, :, heads])
+    sq = lambda t: _np(t[:, heads])
+    yr, hr = oracle.scan_prologue(tk(d["x"]), tk(d["B"]), tk(d["C"]), tk(d["dt"]), _np(d["A"][heads]),
+                                  tk(d["lam"]), tk(th), h0=sq(c["h0"]), B_prev=sq(c["B_prev"]),
+                                  x_prev=sq(c["x_prev"]), eps=1e-5, bias_B=_np(bb[heads]), bias_C=_np(bc[heads]))
+    check_blocks(to64(y[:, :, heads]), yr, TOL["bf16"], (1, 3, 4), "prologue y", elem_axes=(3, 4))
+    check_blocks(to64(h[:, heads]), hr, TOL["bf16"], (2, 3), "prologue h_out")
