@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "m3_internal.h"
+#include "m3_prologue.h"
 
 namespace m3 {
 namespace {

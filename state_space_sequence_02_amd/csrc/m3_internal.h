@@ -205,21 +205,6 @@ __host__ __device__ constexpr int backward_segment(int R, int N, int P) {
 }
 hipError_t launch_backward(const BackwardParams& p, int dtype, int N, int P, int R, hipStream_t stream);
 
-// The prologue as a stage of its own (m3_prologue.hip): B, C and B_prev
-// normalized with their biases added, and the angles dt x theta, written to
-// Bn, Cn, Bpn and phi (the inputs' layouts and dtype; phi fp32).  tokens =
-// b x L x H, pairs = b x H.
-struct PrologueStage {
-  int dtype, N, H, R;
-  size_t tokens, pairs;
-  float eps;
-  const void* B; const void* C; const void* Bp;
-  const float* dt; const float* theta;
-  const float* biasB; const float* biasC;
-  void* Bn; void* Cn; void* Bpn; float* phi;
-};
-hipError_t launch_prologue_stage(const PrologueStage& p, hipStream_t stream);
-
 // The device-resident prefill scratch of m3_scan_prefill_noalloc: its size
 // (M3_NOALLOC_SCRATCH_BYTES in m3.h) and its device address on the current
 // device (looked up once per device).

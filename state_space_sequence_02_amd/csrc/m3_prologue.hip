@@ -12,6 +12,7 @@
 // prefill then runs on them.  Both kernels are HBM streams: each input element
 // is read once and each result written once.
 #include "m3_device.h"
+#include "m3_prologue.h"
 
 namespace m3 {
 namespace {
