@@ -474,6 +474,8 @@ def main():
                     help="prefill tokens per chunk (-1: the configuration's; 0: library default)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "per_chunk", "stream"],
                     help="prefill kernel of the headline line (auto: the one the library takes)")
+    ap.add_argument("--prologue", action="store_true",
+                    help="headline prefill through m3_scan_prefill_prologue (raw angles, B/C biases)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -505,7 +507,8 @@ def main():
         requested = w.chunk if args.chunk < 0 else args.chunk
         chunk = prefill_chunk_for(w, requested)
         kernel = {"auto": 0, "per_chunk": m3.M3_KERNEL_PER_CHUNK, "stream": m3.M3_KERNEL_STREAM}[args.kernel]
-        r = bench_prefill(w, args.steps, args.warmup, chunk=chunk, reps=args.reps, kernel=kernel)
+        r = bench_prefill(w, args.steps, args.warmup, chunk=chunk, reps=args.reps, kernel=kernel,
+                          prologue="fused" if args.prologue else None)
         value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
         traffic = measured_traffic(f"{r['kernel']}_{w.name}_q{r['chunk']}")
         roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -516,7 +519,7 @@ def main():
                     mfma_tflops=round(r["tflops_launch"], 2),
                     mfma_frac=round(r["tflops_launch"] / MFMA_BF16_PEAK_TFS, 4),
                     algorithmic_flops_per_launch=r["flops"])
-        config = dict(workload=f"{w.name} prefill: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
+        config = dict(workload=f"{w.name} prefill{' with the prologue' if args.prologue else ''}: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
                                f"N={w.dstate}, R={w.rank}, {w.dtype} in, fp32 state",
                       batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, dstate=w.dstate,
                       headdim=w.headdim, rank=w.rank, chunk=r["chunk"], chunk_requested=requested)
