@@ -476,6 +476,8 @@ def main():
                     help="prefill kernel of the headline line (auto: the one the library takes)")
     ap.add_argument("--prologue", action="store_true",
                     help="headline prefill through m3_scan_prefill_prologue (raw angles, B/C biases)")
+    ap.add_argument("--backward", action="store_true",
+                    help="headline: the backward (m3_scan_backward, every gradient) at the prefill workload's shape")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -503,6 +505,18 @@ def main():
                       batch=w.batch, nheads=w.nheads, dstate=w.dstate, headdim=w.headdim, rank=w.rank,
                       state_buffers=3)
         steps_done = args.steps * 10
+    elif args.backward:
+        r = bench_backward(w, args.steps, args.warmup, reps=args.reps)
+        value, unit, ms = r["tokens_per_s"], "tokens/s/layer", r["ms"]
+        roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(r["gbs_launch"] / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="m3_scan_backward (five launches)", algorithmic_bytes_per_launch=r["bytes"],
+                    us_per_launch=round(r["ms_launch"] * 1e3, 2))
+        config = dict(workload=f"{w.name} backward: b={w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
+                               f"N={w.dstate}, R={w.rank}, {w.dtype} in, fp32 gradients",
+                      batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, dstate=w.dstate,
+                      headdim=w.headdim, rank=w.rank, workspace_bytes=r["workspace_bytes"])
+        steps_done = args.steps
     else:
         requested = w.chunk if args.chunk < 0 else args.chunk
         chunk = prefill_chunk_for(w, requested)
