@@ -256,8 +256,8 @@ def _bench_prefill(w, steps, warmup, chunk, nsets, gate, prologue, reps):
     if q_used == 0:
         raise m3.M3Error(2, f"the library takes no chunk {chunk} for {w.name}")
     staged = prologue == "fused" and m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_STAGED
-    kern = "stream_kernel" if (not gate and (prologue != "fused" or staged) and
-                               m3.prefill_kernel_used(shape) == m3.M3_KERNEL_STREAM) else "prefill_kernel"
+    used = m3.prefill_prologue_kernel_used(shape) if prologue == "fused" else m3.prefill_kernel_used(shape)
+    kern = "stream_kernel" if (not gate and used == m3.M3_KERNEL_STREAM) else "prefill_kernel"
     if staged:
         kern = "prologue stage + " + kern
     ys = [torch.empty_like(s["x"]) for s in sets]
@@ -599,9 +599,8 @@ def main():
         sec["mimo_decode_gated"] = decode_line(wd, rg)
         # the prologue (BCNorm + B/C biases + angle = dt x raw angle) through
         # m3_scan_prefill_prologue, and the unfused alternative (the prologue in
-        # torch ops first): fused into the prefill kernel on the SISO workload;
-        # staged before the (streaming) prefill on the MIMO workload, whose fused
-        # N = 128 variant keeps a few values in scratch memory and is not launched
+        # torch ops first): fused into the per-chunk kernel on the SISO
+        # workload and into the streaming kernel on the MIMO workload
         for name in ("siso", "mimo"):
             ws_ = inputs.WORKLOADS[name]
             pf = bench_prefill(ws_, args.steps, max(2, args.warmup // 5), chunk=64, prologue="fused")

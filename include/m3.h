@@ -322,11 +322,16 @@ typedef struct {
  * takes every shape m3_scan_prefill takes, in one of two forms
  * (m3_prefill_prologue_mode):
  *   M3_PROLOGUE_FUSED   the prologue runs inside the prefill kernel's load
- *                       stage (one launch; its bias tables take R x (2N + 4) x 4
- *                       bytes of LDS beside the chunk's tiles).  Used where
- *                       that kernel variant exists and uses no scratch memory:
- *                       bf16 or fp32 inputs at N <= 64 and bf16 at N = 128 with
- *                       P <= 32, at chunks of one 16-row output tile per wave;
+ *                       stage (one launch; its bias tables take about
+ *                       R x 2N x 4 bytes of LDS beside the chunk's tiles).
+ *                       Used where such a kernel variant exists and uses no
+ *                       scratch memory: in the streaming kernel wherever the
+ *                       plain prefill streams (bf16, P = 64, R = 2 or 4 at
+ *                       N = 128, among them the MIMO and long shapes), else in
+ *                       the per-chunk kernel: bf16 or fp32 inputs at N <= 64 and
+ *                       bf16 at N = 128 with P <= 32, at chunks of one 16-row
+ *                       output tile per wave (m3_prefill_prologue_kernel_used
+ *                       says which kernel);
  *   M3_PROLOGUE_STAGED  elsewhere: a prologue kernel writes the normalized B,
  *                       C, B_prev and the angles dt x theta into the workspace
  *                       (the inputs' layouts and dtype, bf16 rounded to nearest
@@ -340,6 +345,10 @@ typedef struct {
  * m3_scan_prefill. */
 enum { M3_PROLOGUE_FUSED = 1, M3_PROLOGUE_STAGED = 2 };
 int32_t m3_prefill_prologue_mode(const m3_shape* s);   /* 0 when the shape is refused */
+/* The prefill kernel a m3_scan_prefill_prologue call runs (M3_KERNEL_STREAM or
+ * M3_KERNEL_PER_CHUNK, as m3_prefill_kernel_used; in the staged form the plain
+ * prefill's), or 0 when the shape is refused. */
+int32_t m3_prefill_prologue_kernel_used(const m3_shape* s);
 /* Bytes of workspace m3_scan_prefill_prologue needs for this shape (never less
  * than m3_prefill_workspace_bytes, so one buffer serves every prefill entry
  * point; 0 when the shape is refused).  In the staged form it adds, behind the

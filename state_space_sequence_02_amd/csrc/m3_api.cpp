@@ -79,15 +79,15 @@ int choose_chunk(const m3_shape& s, int gated, int pro) {
   return 0;
 }
 
-// The streaming prefill variants {N, P, R, 32-row blocks} that use scratch
-// (build report): those shapes take the per-chunk kernel.
-const int kStreamScratch[][4] = {
+// The streaming prefill variants {N, P, R, 32-row blocks, prologue} that use
+// scratch (build report): those shapes take the per-chunk kernel.
+const int kStreamScratch[][5] = {
 #include "m3_scratch_table_stream.inc"
-    {-1, 0, 0, 0}};
+    {-1, 0, 0, 0, 0}};
 
-bool stream_spills(int N, int P, int R, int Q) {
+bool stream_spills(int N, int P, int R, int Q, int pro = 0) {
   for (const auto& k : kStreamScratch)
-    if (k[0] == N && k[1] == P && k[2] == R && k[3] * 32 == Q * R) return true;
+    if (k[0] == N && k[1] == P && k[2] == R && k[3] * 32 == Q * R && k[4] == (pro ? 1 : 0)) return true;
   return false;
 }
 
@@ -126,7 +126,26 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro) {
   // scratch, and a memory fault was seen in one of them whose cause is not
   // established, so that path is not built.
   if (s.dstate > 128) return false;
-  const int q = choose_chunk(s, gated, pro);
+  const int mode = g_prefill_kernel.load(std::memory_order_relaxed);
+  // whether the streaming kernel runs a shape at chunk q (the library's choice
+  // at N = 128; at N = 64 only when asked for)
+  auto streams = [&](int q, int with_pro) {
+    return q > 0 && mode != M3_KERNEL_PER_CHUNK && (mode == M3_KERNEL_STREAM || s.dstate == 128) &&
+           stream_supported(s.dtype, s.dstate, s.headdim, s.rank, q, gated, with_pro) &&
+           !stream_spills(s.dstate, s.headdim, s.rank, q, with_pro);
+  };
+  int q = 0;
+  bool stream_pro = false;
+  if (pro && !gated) {
+    // the prologue fused into the streaming kernel, at the plain prefill's
+    // chunk, wherever the plain prefill would stream
+    const int qs = choose_chunk(s, 0, 0);
+    if (streams(qs, 0) && streams(qs, 1)) {
+      q = qs;
+      stream_pro = true;
+    }
+  }
+  if (!stream_pro) q = choose_chunk(s, gated, pro);
   if (q == 0) return false;
   plan->Q = q;
   plan->nc = s.seqlen > 0 ? (s.seqlen + q - 1) / q : 0;
@@ -146,12 +165,9 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro) {
   // kernel runs two workgroups per compute unit and measured faster (SISO,
   // 4 x 4096 tokens x 32 heads, chunk 128: 134 us against 196 us); the
   // streaming kernel runs there only when asked for (m3_debug_set_prefill_kernel).
-  const int mode = g_prefill_kernel.load(std::memory_order_relaxed);
-  if (mode != M3_KERNEL_PER_CHUNK && (mode == M3_KERNEL_STREAM || s.dstate == 128) &&
-      stream_supported(s.dtype, s.dstate, s.headdim, s.rank, q, gated, pro) &&
-      !stream_spills(s.dstate, s.headdim, s.rank, q)) {
+  if (stream_pro || (!pro && streams(q, 0))) {
     plan->kernel = M3_KERNEL_STREAM;
-    plan->lds = stream_lds_bytes(q, s.rank, s.dstate, s.headdim);
+    plan->lds = pro ? stream_lds_bytes_pro(q, s.rank, s.dstate, s.headdim) : stream_lds_bytes(q, s.rank, s.dstate, s.headdim);
   }
   return true;
 }
@@ -221,6 +237,13 @@ int32_t m3_prefill_prologue_chunk_used(const m3_shape* s) {
   PrefillPlan plan;
   if (!prologue_mode(*s, &plan)) return 0;
   return plan.Q;
+}
+
+int32_t m3_prefill_prologue_kernel_used(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!prologue_mode(*s, &plan)) return 0;
+  return plan.kernel;
 }
 
 int32_t m3_prefill_prologue_mode(const m3_shape* s) {

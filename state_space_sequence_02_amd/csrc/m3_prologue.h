@@ -21,4 +21,8 @@ struct PrologueStage {
 };
 hipError_t launch_prologue_stage(const PrologueStage& p, hipStream_t stream);
 
+// Dynamic LDS of the streaming prefill with the prologue fused (its bias
+// tables beside the chunk's tiles; m3_stream.hip).
+size_t stream_lds_bytes_pro(int Q, int R, int N, int P);
+
 }  // namespace m3

@@ -29,6 +29,15 @@
 //    the inter-chunk term exp(l_t) C~_t^T S_in added to the accumulated intra
 //    term, and y stored.
 //
+// With PRO (m3_scan_prefill_prologue) the prologue is applied where the
+// operands are staged: each B row is RMS-normalised over its N values (the
+// row's N/8 items sit in consecutive lanes: DPP row rotations at N = 128, xor
+// shuffles at N = 64) and gets the head's B bias, each C row likewise when its
+// MFMA fragments are formed (4 lane groups), a sequence's first chunk scales
+// B_prev by column norms wave 0 takes into LDS, and the angle threads multiply
+// the raw angles by their tokens' dt before the phase scan.  The head's bias
+// tables ([R][N] each) are loaded one chunk ahead with the scalars.
+//
 // Termination and the control words: a workgroup whose ticket is past the
 // call's last one stops; it then counts itself in the exit counter (the
 // workspace's third 8-byte word), and the last of the grid to stop resets the
@@ -59,10 +68,12 @@ constexpr int kMapGroup = M3_STREAM_MAP_GROUP;   // maps loaded at once in the l
 // two-slot ring (then S_in^T for the readout), every lane's C~ fragments
 // (its wave's output rows; read back only by that lane), scalars.
 struct SLds {
-  size_t row, rw, W, cs, ring, blk, cfr, misc, total;
+  size_t row, rw, W, cs, ring, blk, cfr, misc, pb, total;
   size_t segl, sega;   // scan scratch, inside the ring (before a chunk's first block is staged)
 };
-__host__ __device__ constexpr SLds lds_of(int Q, int R, int N, int P) {
+// pro: the fused prologue's tables behind the rest: the head's B and C biases
+// [R][N] each, then B_prev's column norm factors [R] (a sequence's first chunk)
+__host__ __device__ constexpr SLds lds_of(int Q, int R, int N, int P, bool pro = false) {
   SLds o{};
   const int QR = Q * R;
   o.row = 0;
@@ -73,7 +84,8 @@ __host__ __device__ constexpr SLds lds_of(int Q, int R, int N, int P) {
   o.blk = round_up_i(2 * 32 * (N + 8) + 2 * 32 * x_stride(P, 2), 16);   // B~ [32][N+8], X [32][XS] (bf16)
   o.cfr = o.ring + 2 * o.blk;     // [N/32][kThreads] 16-byte fragments
   o.misc = o.cfr + 16 * (size_t)kThreads * (N / 32);
-  o.total = o.misc + 64;
+  o.pb = o.misc + 64;
+  o.total = o.pb + (pro ? sizeof(float) * (size_t)R * (2 * N + 4) : 0);
   o.segl = o.ring;
   o.sega = o.ring + sizeof(float) * kWaves;
   return o;
@@ -112,7 +124,10 @@ __device__ __forceinline__ float wave_scan_add(float v) {
 // MAPS: chunk maps in use (many chunks of one sequence in flight at once: a
 // chunk whose predecessor's state is late publishes its map, and the look-back
 // composes maps); without, a chunk waits for its predecessor's state.
-template <int N, int P, int R, int NBK, int PRE, bool MAPS>
+// PRO: the fused prologue (BCNorm of B, C and B_prev with the head's B/C
+// biases, the step angle dt x theta) applied where B and C are staged and the
+// angles scanned.
+template <int N, int P, int R, int NBK, int PRE, bool MAPS, bool PRO>
 __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   typedef bf16 T;
   constexpr int NH = N / 2;
@@ -140,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   static_assert(NBK % PRE == 0 && kXStep >= 1, "a chunk's block 0 lands in prefetch slot 0");
   static_assert(ALEN >= 1 && ALEN <= 4 && NSEG * ALEN == Q, "angle threads");
   static_assert(kThreads % (N / 8) == 0 && NK >= 1 && TPt >= 1, "tiles");
-  constexpr SLds lay = lds_of(Q, R, N, P);
+  constexpr SLds lay = lds_of(Q, R, N, P, PRO);
   constexpr uint32_t kOff = 0x80000000u;      // an offset past every extent
   constexpr uint32_t SLOT = fused_slot_floats(N, P);
   static_assert(SLOT == (uint32_t)NPW * PTW * kThreads * 4, "slot layout");
@@ -156,6 +171,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   T* s_H = reinterpret_cast<T*>(smem + lay.ring);          // S_in^T [P][N + 8] (after the blocks)
   bf16x8* s_cf = reinterpret_cast<bf16x8*>(smem + lay.cfr);   // C~ fragments [NK][kThreads]
   int* s_misc = reinterpret_cast<int*>(smem + lay.misc);
+  float* s_pb = reinterpret_cast<float*>(smem + lay.pb);   // PRO: bias tables, B_prev norms
   auto ringB = [&](int slot) { return reinterpret_cast<T*>(smem + lay.ring + slot * lay.blk); };
   auto ringX = [&](int slot) { return reinterpret_cast<T*>(smem + lay.ring + slot * lay.blk) + 32 * NS; };
 
@@ -179,6 +195,8 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   Raw8<T> pre[PRE];
   float dv, lmv, dnv, lmnv_raw, av;
   float4 th4[ALEN];
+  float dth[ALEN];   // PRO: dt of the angle thread's tokens
+  float4 pbv;        // PRO: 4 of the head's bias values (B's [R][N] then C's)
   Raw8<T> craw[NK];
   struct Ck { int c, bh, h, nt; size_t tok0; };
   Ck ck{0, 0, 0, 0, 0};
@@ -266,6 +284,18 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 #pragma unroll
     for (int j = 0; j < ALEN; ++j)
       th4[j] = buf_load_f32x4(rT, sg < NSEG ? (uint32_t)(sg * ALEN + j) * tsb * NH + 16 * cg : kOff);
+    if constexpr (PRO) {
+      // theta holds raw angles: each angle thread also takes its tokens' dt
+#pragma unroll
+      for (int j = 0; j < ALEN; ++j) dth[j] = buf_load_f32(rD, sg < NSEG ? (uint32_t)(sg * ALEN + j) * tsb : kOff);
+      // the head's biases, one float4 per thread: B's [R][N] (threads below
+      // R N / 4), then C's (the next R N / 4); a missing table reads as zeros
+      constexpr int kPb4 = R * N / 4;
+      const Rsrc rBb = buf_rsrc(p->biasB ? p->biasB + (size_t)k.h * R * N : nullptr, (p->biasB && nt > 0) ? R * N * 4 : 0);
+      const Rsrc rCb = buf_rsrc(p->biasC ? p->biasC + (size_t)k.h * R * N : nullptr, (p->biasC && nt > 0) ? R * N * 4 : 0);
+      pbv = add4(buf_load_f32x4(rBb, tid < kPb4 ? (uint32_t)tid * 16 : kOff),
+                 buf_load_f32x4(rCb, tid >= kPb4 && tid < 2 * kPb4 ? (uint32_t)(tid - kPb4) * 16 : kOff));
+    }
   };
   auto c_load = [&](const Ck& k) {
     const Rsrc rC = buf_rsrc(static_cast<const T*>(p->C) + k.tok0 * R * N, k.nt > 0 ? (uint32_t)(k.nt - 1) * rsB + R * N * 2 : 0);
@@ -284,6 +314,26 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       const int grow = 32 * j + row;
       float v[8];
       raw_unpack(r, v);
+      if constexpr (PRO) {   // the row's N / 8 items sit in consecutive lanes
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        if constexpr (N / 8 == 16) {   // one 16-lane DPP row: rotate-and-add
+          ss += dpp_row_ror<8>(ss);
+          ss += dpp_row_ror<4>(ss);
+          ss += dpp_row_ror<2>(ss);
+          ss += dpp_row_ror<1>(ss);
+        } else {
+#pragma unroll
+          for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off);
+        }
+        if (grow < rows) {   // (rows past the chunk's end stay zero)
+          const float sc = rsqrtf(ss / (float)N + p->eps);
+          const float* bb = s_pb + (grow & (R - 1)) * N + ng * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * sc + bb[e];
+        }
+      }
       // (rows past the chunk's end hold zeros: any angle will do)
       rotate_neg(v, s_cs + (min(grow, rows - 1) >> LOGR) * CSS + ng, NG);
       store8<T>(ringB(slot) + row * NS + ng * 8, v);
@@ -319,6 +369,25 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       s_misc[4] = 0;   // wave counter: state published
       nextw = atomicAdd(p->ctl, 1ull);
     }
+    if constexpr (PRO) {
+      if (tid < R * N / 2) *reinterpret_cast<float4*>(s_pb + 4 * tid) = pbv;
+      // a sequence's first chunk: wave 0 reduces B_prev's column norms into
+      // LDS (read when S_in is set up)
+      if (c == 0 && p->Bp && wave == 0) {
+        const T* Bp0 = static_cast<const T*>(p->Bp) + (size_t)bh * R * N;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float ss = 0.f;
+          for (int n = lane; n < N; n += 64) {
+            const float t = to_f(Bp0[r * N + n]);
+            ss += t * t;
+          }
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+          if (lane == 0) s_pb[2 * R * N + r] = rsqrtf(ss / (float)N + p->eps);
+        }
+      }
+    }
     const float A = av;   // (loaded with the scalars, one chunk ahead)
     const float lmnv = (c * Q + tid + 1 < p->L && tid < nt) ? lmnv_raw : 1.f;   // (only multiplies dnv = 0 otherwise)
 
@@ -330,6 +399,11 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       lsc = dv * A;
     }
     lsc = wave_scan_add(lsc);
+    if constexpr (PRO) {   // the step angle: dt x the raw angle
+#pragma unroll
+      for (int j = 0; j < ALEN; ++j)
+        th4[j] = make_float4(th4[j].x * dth[j], th4[j].y * dth[j], th4[j].z * dth[j], th4[j].w * dth[j]);
+    }
 #pragma unroll
     for (int j = 1; j < ALEN; ++j) th4[j] = add4(th4[j], th4[j - 1]);
     const float4 atot = th4[ALEN - 1];
@@ -398,11 +472,32 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
     const int row_a = tile * 16 + l16;
     {
       const int ta = row_a < rows ? row_a >> LOGR : 0;
+      float csc = 1.f;
+      if constexpr (PRO) {   // a C row: NK slices in this lane, 4 lane groups
+        float ss = 0.f;
+#pragma unroll
+        for (int kn = 0; kn < NK; ++kn) {
+          float v[8];
+          raw_unpack(craw[kn], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        csc = rsqrtf(ss / (float)N + p->eps);
+      }
 #pragma unroll
       for (int kn = 0; kn < NK; ++kn) {
         const int n0 = kn * 32 + 8 * g4;
         float v[8];
         raw_unpack(craw[kn], v);
+        if constexpr (PRO) {
+          if (row_a < rows) {
+            const float* bc = s_pb + R * N + (row_a & (R - 1)) * N + n0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * csc + bc[e];
+          }
+        }
         rotate_neg(v, s_cs + ta * CSS + n0 / 8, NG);
         Frag<T> cfk;
 #pragma unroll
@@ -623,6 +718,12 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
           bpv[r][1] = __uint_as_float(w.x & 0xffff0000u);
           bpv[r][2] = __uint_as_float(w.y << 16);
           bpv[r][3] = __uint_as_float(w.y & 0xffff0000u);
+          if constexpr (PRO) {
+            if (Bp) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bpv[r][e] = bpv[r][e] * s_pb[2 * R * N + r] + s_pb[r * N + n0 + e];
+            }
+          }
         }
 #pragma unroll
         for (int jj = 0; jj < PTW; ++jj) {
@@ -856,10 +957,10 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   }
 }
 
-template <int N, int P, int R, int NBK, int PRE, bool MAPS>
+template <int N, int P, int R, int NBK, int PRE, bool MAPS, bool PRO>
 hipError_t launch_v(const FusedParams& p, size_t grid, bool late, hipStream_t stream) {
-  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P).total;
-  const void* fn = reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, MAPS>);
+  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P, PRO).total;
+  const void* fn = reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, MAPS, PRO>);
   static std::atomic<int> scratch_state{0};   // 0 unknown, 1 none, 2 uses scratch
   int st = scratch_state.load(std::memory_order_relaxed);
   if (st == 0) {
@@ -880,13 +981,13 @@ hipError_t launch_v(const FusedParams& p, size_t grid, bool late, hipStream_t st
   FusedParams q = p;
   q.use_maps = MAPS ? 1 : 0;
   q.late_flag = late ? 1 : 0;
-  hipLaunchKernelGGL((stream_kernel<N, P, R, NBK, PRE, MAPS>), dim3((unsigned)grid), dim3(kThreads), lds, stream, q);
+  hipLaunchKernelGGL((stream_kernel<N, P, R, NBK, PRE, MAPS, PRO>), dim3((unsigned)grid), dim3(kThreads), lds, stream, q);
   return hipGetLastError();
 }
 
-template <int N, int P, int R, int NBK, int PRE>
+template <int N, int P, int R, int NBK, int PRE, bool PRO>
 hipError_t launch(const FusedParams& p, hipStream_t stream) {
-  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P).total;
+  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P, PRO).total;
   // resident workgroups per device (cached): the persistent grid (both map
   // modes have the same launch bounds and LDS)
   int dev = 0;
@@ -897,7 +998,7 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, true>), kThreads, lds) != hipSuccess)
+            &per, reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, true, PRO>), kThreads, lds) != hipSuccess)
       return hipErrorInvalidValue;
     resident = cus * per;
     if (resident <= 0) return hipErrorInvalidValue;
@@ -912,13 +1013,13 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
   // ~1 us more per chunk.  Measured on 65,536-token sequences (N = 128, R = 4,
   // 256 resident workgroups): 8 in flight, states only 4% faster; 16 and 32,
   // maps 1.5 and 2.2 times faster.
-  if ((size_t)resident > 8 * (size_t)p.batch * p.H) return launch_v<N, P, R, NBK, PRE, true>(p, grid, false, stream);
+  if ((size_t)resident > 8 * (size_t)p.batch * p.H) return launch_v<N, P, R, NBK, PRE, true, PRO>(p, grid, false, stream);
   // States only.  With at most 4 chunks of a sequence in flight the hand-off
   // chain (~2.5 us a link) stays well inside the time a workgroup spends on its
   // chunks, so a chunk's state flag waits for the end of its readout, and the
   // state stores complete meanwhile instead of holding up the whole workgroup.
   const bool late = (size_t)resident <= 4 * (size_t)p.batch * p.H;
-  return launch_v<N, P, R, NBK, PRE, false>(p, grid, late, stream);
+  return launch_v<N, P, R, NBK, PRE, false, PRO>(p, grid, late, stream);
 }
 
 }  // namespace stream
@@ -927,31 +1028,33 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
 // N = 64 with R = 1, 2 or 4 at 128 or 256 (token, rank) rows per chunk; N = 128
 // at 128 rows (R = 1, 2, 4) or 256 rows (R = 4): the chunks whose LDS fits.
 bool stream_supported(int dtype, int N, int P, int R, int Q, int gated, int pro) {
-  if (dtype != M3_BF16 || P != 64 || (N != 64 && N != 128) || gated || pro) return false;
+  if (dtype != M3_BF16 || P != 64 || (N != 64 && N != 128) || gated) return false;
   if (R != 1 && R != 2 && R != 4) return false;
   if (Q * R != 128 && Q * R != 256) return false;
-  return Q * (N / 2) <= kFusedAngleCap && stream::lds_of(Q, R, N, P).total <= (size_t)kLdsBudget;
+  return Q * (N / 2) <= kFusedAngleCap && stream::lds_of(Q, R, N, P, pro != 0).total <= (size_t)kLdsBudget;
 }
 
 size_t stream_lds_bytes(int Q, int R, int N, int P) { return stream::lds_of(Q, R, N, P).total; }
+size_t stream_lds_bytes_pro(int Q, int R, int N, int P) { return stream::lds_of(Q, R, N, P, true).total; }
 
-hipError_t launch_stream_prefill(const FusedParams& p, hipStream_t s) {
+template <bool PRO>
+hipError_t launch_stream_pro(const FusedParams& p, hipStream_t s) {
   const int rows = p.Q * p.R;
 #define M3_STREAM_R(NN, NBK, PRE)                                        \
   switch (p.R) {                                                         \
-    case 1: return stream::launch<NN, 64, 1, NBK, PRE>(p, s);            \
-    case 2: return stream::launch<NN, 64, 2, NBK, PRE>(p, s);            \
-    case 4: return stream::launch<NN, 64, 4, NBK, PRE>(p, s);            \
+    case 1: return stream::launch<NN, 64, 1, NBK, PRE, PRO>(p, s);       \
+    case 2: return stream::launch<NN, 64, 2, NBK, PRE, PRO>(p, s);       \
+    case 4: return stream::launch<NN, 64, 4, NBK, PRE, PRO>(p, s);       \
     default: return hipErrorInvalidValue;                                \
   }
   if (p.P != 64) return hipErrorInvalidValue;
   if (p.N == 128) {
     // (128 tokens at R = 2, 256 rows, do not fit: the cos/sin table of 128
     // tokens, the ring and the C~ fragments of 256 rows need ~164 KB of LDS)
-    if (rows == 256 && p.R == 4) return stream::launch<128, 64, 4, 8, 4>(p, s);
-    if (rows == 128 && p.R == 1) return stream::launch<128, 64, 1, 4, 2>(p, s);
-    if (rows == 128 && p.R == 2) return stream::launch<128, 64, 2, 4, 2>(p, s);
-    if (rows == 128 && p.R == 4) return stream::launch<128, 64, 4, 4, 2>(p, s);
+    if (rows == 256 && p.R == 4) return stream::launch<128, 64, 4, 8, 4, PRO>(p, s);
+    if (rows == 128 && p.R == 1) return stream::launch<128, 64, 1, 4, 2, PRO>(p, s);
+    if (rows == 128 && p.R == 2) return stream::launch<128, 64, 2, 4, 2, PRO>(p, s);
+    if (rows == 128 && p.R == 4) return stream::launch<128, 64, 4, 4, 2, PRO>(p, s);
     return hipErrorInvalidValue;
   } else if (p.N == 64) {
     if (rows == 256) { M3_STREAM_R(64, 8, 4) }
@@ -959,6 +1062,10 @@ hipError_t launch_stream_prefill(const FusedParams& p, hipStream_t s) {
   }
 #undef M3_STREAM_R
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_prefill(const FusedParams& p, hipStream_t s) {
+  return p.pro ? launch_stream_pro<true>(p, s) : launch_stream_pro<false>(p, s);
 }
 
 }  // namespace m3

@@ -179,12 +179,19 @@ def test_prologue_validation_codes(lib):
     assert prefill(ok, ws=None) == 4
     assert prefill(m3.make_shape(2, 128, 3, 64, 256, 4, 64, 1)) == 2      # N = 256: decode only
     assert m3.prefill_prologue_mode(ok) == m3.M3_PROLOGUE_FUSED
-    # more than one 16-row output tile per wave (chunk above the default), and
-    # the bf16 MIMO shape at N = 128: no fused variant is launched there, so
-    # the prologue is staged before the plain prefill, at the plain chunk
+    # the bf16 MIMO and long shapes at N = 128: fused into the streaming
+    # kernel (the per-chunk kernel's prologue variant there uses scratch), at
+    # the plain prefill's chunk
+    for shape in (m3.make_shape(4, 4096, 32, 64, 128, 4, 0, 1), m3.make_shape(1, 65536, 32, 64, 128, 4, 64, 1)):
+        assert m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_FUSED
+        assert m3.prefill_kernel_used(shape) == m3.prefill_prologue_kernel_used(shape) == m3.M3_KERNEL_STREAM
+        assert m3.prefill_chunk_used(shape, "prologue") == m3.prefill_chunk_used(shape) == 64
+        assert m3.prefill_prologue_workspace_bytes(shape) == m3.prefill_workspace_bytes(shape)
+    # more than one 16-row output tile per wave (chunk above the default): no
+    # fused variant is launched there, so the prologue is staged before the
+    # plain prefill, at the plain chunk
     for shape in (m3.make_shape(2, 512, 3, 64, 64, 1, 256, 1), m3.make_shape(2, 512, 3, 64, 64, 2, 128, 1),
-                  m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1), m3.make_shape(2, 128, 3, 64, 64, 4, 64, 1),
-                  m3.make_shape(4, 4096, 32, 64, 128, 4, 0, 1)):
+                  m3.make_shape(2, 512, 3, 32, 32, 1, 256, 1), m3.make_shape(2, 128, 3, 64, 64, 4, 64, 1)):
         assert m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_STAGED
         q = m3.prefill_chunk_used(shape)
         assert q > 0 and m3.prefill_chunk_used(shape, "prologue") == q
@@ -270,6 +277,24 @@ def _scratch_variants():
     return out
 
 
+def _stream_scratch_variants():
+    """Streaming prefill variants (N, P, R, 32-row blocks, prologue) the build's
+    compiler report gives scratch memory (either map mode)."""
+    import json
+    import re
+    path = os.path.join(os.path.dirname(m3.LIB_PATH), "..", "_build", "kernel_usage.json")
+    if not os.path.exists(path):
+        pytest.skip("no kernel usage report (build the library first)")
+    pat = re.compile(r"stream_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E")
+    out = set()
+    for name, u in json.load(open(path)).items():
+        m = pat.search(name)
+        if m and u.get("scratch", 0) > 0:
+            n, p, r, nbk, _pre, _maps, pro = map(int, m.groups())
+            out.add((n, p, r, nbk, pro))
+    return out
+
+
 def _row_tiles(q, R, N):
     rows = -(-q * R // 32) * 32
     waves = (1024 if N >= 128 else 512) // 64
@@ -282,6 +307,7 @@ def test_prefill_refuses_scratch_variants(lib):
     (from the compiler report of this build), for each entry point; and the
     configurations' kernels use none."""
     spills = _scratch_variants()
+    stream_spills = _stream_scratch_variants()
     for variant, (g, pro) in {"plain": (0, 0), "gated": (1, 0), "prologue": (0, 1)}.items():
         for code in (m3.M3_BF16, m3.M3_FP32):
             for N in (16, 32, 64, 128):
@@ -291,9 +317,18 @@ def test_prefill_refuses_scratch_variants(lib):
                             s = m3.make_shape(1, 300, 2, P, N, R, chunk, code)
                             q = m3.prefill_chunk_used(s, variant)
                             if q:
-                                # the staged prologue runs the plain prefill's variant
+                                # the staged prologue runs the plain prefill's variant; where
+                                # the plain prefill streams, the prologue is fused into the
+                                # streaming kernel (its own spill-free variants, checked below)
                                 staged = pro and m3.prefill_prologue_mode(s) == m3.M3_PROLOGUE_STAGED
-                                assert (code, N, P, R, _row_tiles(q, R, N), g, 0 if staged else pro) not in spills
+                                streamed = (pro and not staged and m3.prefill_kernel_used(s) == m3.M3_KERNEL_STREAM
+                                            and q == m3.prefill_chunk_used(s))
+                                if streamed:
+                                    assert (N, P, R, q * R // 32, 1) not in stream_spills
+                                elif not g and not pro and m3.prefill_kernel_used(s) == m3.M3_KERNEL_STREAM:
+                                    assert (N, P, R, q * R // 32, 0) not in stream_spills
+                                else:
+                                    assert (code, N, P, R, _row_tiles(q, R, N), g, 0 if staged else pro) not in spills
                                 if pro:
                                     assert q == (m3.prefill_chunk_used(s) if staged else q)
     from state_space_sequence_02_amd import inputs
@@ -421,7 +456,19 @@ def test_stream_kernels_use_no_scratch(lib):
     path = os.path.join(os.path.dirname(m3.LIB_PATH), "..", "_build", "kernel_usage.json")
     if not os.path.exists(path):
         pytest.skip("no kernel usage report (build the library first)")
+    import re
     usage = json.load(open(path))
-    stream = {n: u for n, u in usage.items() if "stream_kernel" in n}
-    assert len(stream) == 20, sorted(stream)
-    assert all(u.get("scratch", 0) == 0 for u in stream.values()), {n: u for n, u in stream.items() if u.get("scratch")}
+    pat = re.compile(r"stream_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E")
+    stream = {tuple(map(int, m.groups())): u for n, u in usage.items() for m in [pat.search(n)] if m}
+    assert len(stream) == 40, sorted(stream)   # 10 shapes x 2 map modes x with and without the prologue
+    plain = {k: u for k, u in stream.items() if k[6] == 0}
+    assert all(u.get("scratch", 0) == 0 for u in plain.values()), {k: u for k, u in plain.items() if u.get("scratch")}
+    # with the prologue fused: the MIMO / long variant (N = 128, R = 4, 8 blocks) is scratch-free; any variant
+    # that is not is refused on the host (its shapes take the per-chunk kernel's prologue or the staged one)
+    assert all(stream[(128, 64, 4, 8, 4, maps, 1)].get("scratch", 0) == 0 for maps in (0, 1))
+    for (n, p, r, nbk, _pre, _maps, pro), u in stream.items():
+        if pro and u.get("scratch", 0) > 0:
+            q = nbk * 32 // r
+            shape = m3.make_shape(1, 4 * q, 2, p, n, r, q, m3.M3_BF16)
+            assert not (m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_FUSED and
+                        m3.prefill_kernel_used(shape) == m3.M3_KERNEL_STREAM and n == 128)

@@ -78,10 +78,12 @@ PREFILL = [
     # prologue is staged before the plain prefill
     ("siso", dict(batch=1, seqlen=333, nheads=2), 256, True, True),
     ("siso", dict(batch=2, seqlen=200, nheads=2, rank=2), 128, True, True),
-    # the bf16 MIMO shape at N = 128 (its fused variant spills): staged, and the
-    # plain prefill it runs is the streaming kernel
+    # the bf16 MIMO shape at N = 128: fused into the streaming kernel (the
+    # per-chunk kernel's variant there uses scratch)
     ("mimo", dict(batch=2, seqlen=300, nheads=3), 0, True, True),
     ("mimo", dict(batch=1, seqlen=129, nheads=2), 64, False, False),
+    ("mimo", dict(batch=1, seqlen=700, nheads=2, rank=2), 64, True, True),
+    ("mimo", dict(batch=1, seqlen=400, nheads=2, dstate=64), 64, True, True),
     ("siso", dict(batch=2, seqlen=200, nheads=2), 128, False, False),
     ("mimo", dict(batch=2, seqlen=130, nheads=2), 64, True, True),
     ("mimo", dict(batch=1, seqlen=97, nheads=2), 32, False, True),
@@ -187,23 +189,32 @@ def test_fused_entry_points_edges():
     assert torch.equal(h0, cg["h0"]) and torch.equal(h1, cg["h0"])
 
 
-def test_prefill_prologue_full_size_staged():
+@pytest.mark.parametrize("kernel", ["stream", "per_chunk"])
+def test_prefill_prologue_full_size(kernel):
     """The MIMO workload at full size (4 x 4,096 tokens x 32 heads, N = 128,
-    R = 4) through m3_scan_prefill_prologue: the staged form (its fused
-    variant is not launched) followed by the streaming prefill, every head run;
-    y and the final state of two heads compared with the oracle."""
+    R = 4) through m3_scan_prefill_prologue, every head run: fused into the
+    streaming kernel (the library's choice), and with the per-chunk kernel
+    forced, whose prologue variant there is not launched, so the prologue is
+    staged before it; y and the final state of two heads compared with the
+    oracle."""
     w = inputs.workload("mimo")
-    code = m3.M3_BF16
-    assert m3.prefill_prologue_mode(m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0,
-                                                  code)) == m3.M3_PROLOGUE_STAGED
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16)
     d = inputs.make_prefill_inputs(w, seed=811)
     c = inputs.random_carry(w, seed=812)
     th, bb, bc = _pro_inputs(w, 813, (w.batch, w.seqlen), True)
     dg, cg = dev_inputs(d), dev_inputs(c)
-    note("prefill prologue full size mimo (staged)")
-    y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
-                                    eps=1e-5, bias_B=bb.cuda(), bias_C=bc.cuda())
-    torch.cuda.synchronize()
+    m3.debug_set_prefill_kernel(m3.M3_KERNEL_STREAM if kernel == "stream" else m3.M3_KERNEL_PER_CHUNK)
+    try:
+        mode = m3.prefill_prologue_mode(shape)
+        assert mode == (m3.M3_PROLOGUE_FUSED if kernel == "stream" else m3.M3_PROLOGUE_STAGED)
+        assert m3.prefill_prologue_kernel_used(shape) == (m3.M3_KERNEL_STREAM if kernel == "stream"
+                                                          else m3.M3_KERNEL_PER_CHUNK)
+        note(f"prefill prologue full size mimo ({kernel}, mode {mode})")
+        y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
+                                        eps=1e-5, bias_B=bb.cuda(), bias_C=bc.cuda())
+        torch.cuda.synchronize()
+    finally:
+        m3.debug_set_prefill_kernel(0)
     heads = [0, w.nheads - 1]
     tk = lambda t: _np(t[:, :, heads])
     sq = lambda t: _np(t[:, heads])
@@ -212,3 +223,24 @@ def test_prefill_prologue_full_size_staged():
                                   x_prev=sq(c["x_prev"]), eps=1e-5, bias_B=_np(bb[heads]), bias_C=_np(bc[heads]))
     check_blocks(to64(y[:, :, heads]), yr, TOL["bf16"], (1, 3, 4), "prologue y", elem_axes=(3, 4))
     check_blocks(to64(h[:, heads]), hr, TOL["bf16"], (2, 3), "prologue h_out")
+
+
+def test_prefill_prologue_stream_long_chain():
+    """The streaming kernel's fused prologue with many chunks of a sequence in
+    flight (maps in use): 8,192 tokens of two heads at the long shape."""
+    w = inputs.workload("long", seqlen=8192, nheads=2)
+    d = inputs.make_prefill_inputs(w, seed=821)
+    c = inputs.random_carry(w, seed=822)
+    th, bb, bc = _pro_inputs(w, 823, (w.batch, w.seqlen), True)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 64, m3.M3_BF16)
+    assert m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_FUSED
+    note("prefill prologue long chain (stream, maps)")
+    y, h = m3.scan_prefill_prologue(dg["x"], dg["B"], dg["C"], dg["dt"], dg["A"], dg["lam"], th.cuda(), **cg,
+                                    chunk=64, eps=1e-5, bias_B=bb.cuda(), bias_C=bc.cuda())
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_prologue(_np(d["x"]), _np(d["B"]), _np(d["C"]), _np(d["dt"]), _np(d["A"]), _np(d["lam"]),
+                                  _np(th), h0=_np(c["h0"]), B_prev=_np(c["B_prev"]), x_prev=_np(c["x_prev"]),
+                                  eps=1e-5, bias_B=_np(bb), bias_C=_np(bc))
+    check_blocks(to64(y), yr, TOL["bf16"], (1, 3, 4), "prologue y", elem_axes=(3, 4))
+    check_blocks(to64(h), hr, TOL["bf16"], (2, 3), "prologue h_out")
