@@ -256,8 +256,9 @@ def _bench_prefill(w, steps, warmup, chunk, nsets, gate, prologue, reps):
     if q_used == 0:
         raise m3.M3Error(2, f"the library takes no chunk {chunk} for {w.name}")
     staged = prologue == "fused" and m3.prefill_prologue_mode(shape) == m3.M3_PROLOGUE_STAGED
-    used = m3.prefill_prologue_kernel_used(shape) if prologue == "fused" else m3.prefill_kernel_used(shape)
-    kern = "stream_kernel" if (not gate and used == m3.M3_KERNEL_STREAM) else "prefill_kernel"
+    used = (m3.prefill_prologue_kernel_used(shape) if prologue == "fused" else
+            m3.prefill_gated_kernel_used(shape) if gate == "fused" else m3.prefill_kernel_used(shape))
+    kern = "stream_kernel" if used == m3.M3_KERNEL_STREAM else "prefill_kernel"
     if staged:
         kern = "prologue stage + " + kern
     ys = [torch.empty_like(s["x"]) for s in sets]

@@ -349,6 +349,10 @@ int32_t m3_prefill_prologue_mode(const m3_shape* s);   /* 0 when the shape is re
  * M3_KERNEL_PER_CHUNK, as m3_prefill_kernel_used; in the staged form the plain
  * prefill's), or 0 when the shape is refused. */
 int32_t m3_prefill_prologue_kernel_used(const m3_shape* s);
+/* Likewise for m3_scan_prefill_gated: the streaming kernel, with the gated
+ * readout in its output stage, wherever the plain prefill streams and that
+ * variant uses no scratch; else the per-chunk kernel's gated variant. */
+int32_t m3_prefill_gated_kernel_used(const m3_shape* s);
 /* Bytes of workspace m3_scan_prefill_prologue needs for this shape (never less
  * than m3_prefill_workspace_bytes, so one buffer serves every prefill entry
  * point; 0 when the shape is refused).  In the staged form it adds, behind the

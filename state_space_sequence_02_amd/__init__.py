@@ -8,5 +8,5 @@ from ._binding import (  # noqa: F401
     make_shape, prefill_chunk_used, prefill_workspace_bytes, scan_prefill, scan_prefill_gated, scan_prefill_prologue,
     prefill_max_chunk, prefill_status, debug_set_spin_limit, STATUS, scan_backward, backward_workspace_bytes,
     prefill_kernel_used, debug_set_prefill_kernel, M3_KERNEL_PER_CHUNK, M3_KERNEL_STREAM,
-    prefill_prologue_mode, prefill_prologue_workspace_bytes, prefill_prologue_kernel_used, M3_PROLOGUE_FUSED, M3_PROLOGUE_STAGED,
+    prefill_prologue_mode, prefill_prologue_workspace_bytes, prefill_prologue_kernel_used, prefill_gated_kernel_used, M3_PROLOGUE_FUSED, M3_PROLOGUE_STAGED,
 )

@@ -26,6 +26,7 @@ EXPORTS = ("m3_prefill_workspace_bytes", "m3_prefill_chunk_used", "m3_prefill_ma
            "m3_decode_step_gated", "m3_decode_step_prologue", "m3_scan_prefill_prologue",
            "m3_prefill_kernel_used", "m3_debug_set_prefill_kernel",
            "m3_prefill_prologue_mode", "m3_prefill_prologue_workspace_bytes", "m3_prefill_prologue_kernel_used",
+           "m3_prefill_gated_kernel_used",
            "m3_status_str", "m3_version")
 M3_KERNEL_PER_CHUNK, M3_KERNEL_STREAM = 1, 2
 M3_PROLOGUE_FUSED, M3_PROLOGUE_STAGED = 1, 2
@@ -96,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.m3_prefill_prologue_mode.argtypes = [sp]
     lib.m3_prefill_prologue_kernel_used.restype = ctypes.c_int32
     lib.m3_prefill_prologue_kernel_used.argtypes = [sp]
+    lib.m3_prefill_gated_kernel_used.restype = ctypes.c_int32
+    lib.m3_prefill_gated_kernel_used.argtypes = [sp]
     lib.m3_prefill_prologue_workspace_bytes.restype = sz
     lib.m3_prefill_prologue_workspace_bytes.argtypes = [sp]
     lib.m3_scan_prefill_prologue.restype = ctypes.c_int
@@ -167,6 +170,11 @@ def prefill_prologue_mode(shape: M3Shape) -> int:
 def prefill_prologue_kernel_used(shape: M3Shape) -> int:
     """m3_prefill_prologue_kernel_used: the prefill kernel a prologue call runs."""
     return int(load_library().m3_prefill_prologue_kernel_used(ctypes.byref(shape)))
+
+
+def prefill_gated_kernel_used(shape: M3Shape) -> int:
+    """m3_prefill_gated_kernel_used: the prefill kernel a gated call runs."""
+    return int(load_library().m3_prefill_gated_kernel_used(ctypes.byref(shape)))
 
 
 def prefill_prologue_workspace_bytes(shape: M3Shape) -> int:

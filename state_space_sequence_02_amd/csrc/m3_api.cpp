@@ -79,15 +79,17 @@ int choose_chunk(const m3_shape& s, int gated, int pro) {
   return 0;
 }
 
-// The streaming prefill variants {N, P, R, 32-row blocks, prologue} that use
-// scratch (build report): those shapes take the per-chunk kernel.
-const int kStreamScratch[][5] = {
+// The streaming prefill variants {N, P, R, 32-row blocks, prologue, gated}
+// that use scratch (build report): those shapes take the per-chunk kernel.
+const int kStreamScratch[][6] = {
 #include "m3_scratch_table_stream.inc"
-    {-1, 0, 0, 0, 0}};
+    {-1, 0, 0, 0, 0, 0}};
 
-bool stream_spills(int N, int P, int R, int Q, int pro = 0) {
+bool stream_spills(int N, int P, int R, int Q, int pro, int gated) {
   for (const auto& k : kStreamScratch)
-    if (k[0] == N && k[1] == P && k[2] == R && k[3] * 32 == Q * R && k[4] == (pro ? 1 : 0)) return true;
+    if (k[0] == N && k[1] == P && k[2] == R && k[3] * 32 == Q * R && k[4] == (pro ? 1 : 0) &&
+        k[5] == (gated ? 1 : 0))
+      return true;
   return false;
 }
 
@@ -132,7 +134,7 @@ bool plan_prefill(const m3_shape& s, PrefillPlan* plan, int gated, int pro) {
   auto streams = [&](int q, int with_pro) {
     return q > 0 && mode != M3_KERNEL_PER_CHUNK && (mode == M3_KERNEL_STREAM || s.dstate == 128) &&
            stream_supported(s.dtype, s.dstate, s.headdim, s.rank, q, gated, with_pro) &&
-           !stream_spills(s.dstate, s.headdim, s.rank, q, with_pro);
+           !stream_spills(s.dstate, s.headdim, s.rank, q, with_pro, gated);
   };
   int q = 0;
   bool stream_pro = false;
@@ -237,6 +239,13 @@ int32_t m3_prefill_prologue_chunk_used(const m3_shape* s) {
   PrefillPlan plan;
   if (!prologue_mode(*s, &plan)) return 0;
   return plan.Q;
+}
+
+int32_t m3_prefill_gated_kernel_used(const m3_shape* s) {
+  if (check_common(s, true) != M3_OK) return 0;
+  PrefillPlan plan;
+  if (!plan_prefill(*s, &plan, 1, 0)) return 0;
+  return plan.kernel;
 }
 
 int32_t m3_prefill_prologue_kernel_used(const m3_shape* s) {

@@ -73,7 +73,7 @@ struct SLds {
 };
 // pro: the fused prologue's tables behind the rest: the head's B and C biases
 // [R][N] each, then B_prev's column norm factors [R] (a sequence's first chunk)
-__host__ __device__ constexpr SLds lds_of(int Q, int R, int N, int P, bool pro = false) {
+__host__ __device__ constexpr SLds lds_of(int Q, int R, int N, int P, bool pro = false, bool gate = false) {
   SLds o{};
   const int QR = Q * R;
   o.row = 0;
@@ -85,7 +85,8 @@ __host__ __device__ constexpr SLds lds_of(int Q, int R, int N, int P, bool pro =
   o.cfr = o.ring + 2 * o.blk;     // [N/32][kThreads] 16-byte fragments
   o.misc = o.cfr + 16 * (size_t)kThreads * (N / 32);
   o.pb = o.misc + 64;
-  o.total = o.pb + (pro ? sizeof(float) * (size_t)R * (2 * N + 4) : 0);
+  // (gate: the head's w_y and w_z [R][P] each in the same place)
+  o.total = o.pb + (pro ? sizeof(float) * (size_t)R * (2 * N + 4) : gate ? sizeof(float) * (size_t)R * 2 * P : 0);
   o.segl = o.ring;
   o.sega = o.ring + sizeof(float) * kWaves;
   return o;
@@ -127,7 +128,10 @@ __device__ __forceinline__ float wave_scan_add(float v) {
 // PRO: the fused prologue (BCNorm of B, C and B_prev with the head's B/C
 // biases, the step angle dt x theta) applied where B and C are staged and the
 // angles scanned.
-template <int N, int P, int R, int NBK, int PRE, bool MAPS, bool PRO>
+// GATE: the gated rank-contracted readout fused into the output stage
+// (m3_scan_prefill_gated): out[t][c] = sum_r w_y[r][c] y[(t, r)][c]
+// silu(w_z[r][c] z[t][c]) replaces y.
+template <int N, int P, int R, int NBK, int PRE, bool MAPS, bool PRO, bool GATE>
 __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   typedef bf16 T;
   constexpr int NH = N / 2;
@@ -151,11 +155,13 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   constexpr int ALEN = Q / NSEG;              // tokens per angle thread
   constexpr int kXStep = NBK - 1 - PRE;       // first loop step that loads the next chunk's blocks
   static_assert(R == 1 || R == 2 || R == 4, "rank");
+  static_assert(!(PRO && GATE), "one fused stage per variant");
+  static_assert(!GATE || P == 64, "the gated output stage reads 4 columns of z per lane");
   static_assert(MT <= kWaves && kBI + kXI <= kThreads && kBI % 64 == 0 && kXI % 64 == 0, "geometry");
   static_assert(NBK % PRE == 0 && kXStep >= 1, "a chunk's block 0 lands in prefetch slot 0");
   static_assert(ALEN >= 1 && ALEN <= 4 && NSEG * ALEN == Q, "angle threads");
   static_assert(kThreads % (N / 8) == 0 && NK >= 1 && TPt >= 1, "tiles");
-  constexpr SLds lay = lds_of(Q, R, N, P, PRO);
+  constexpr SLds lay = lds_of(Q, R, N, P, PRO, GATE);
   constexpr uint32_t kOff = 0x80000000u;      // an offset past every extent
   constexpr uint32_t SLOT = fused_slot_floats(N, P);
   static_assert(SLOT == (uint32_t)NPW * PTW * kThreads * 4, "slot layout");
@@ -196,7 +202,8 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   float dv, lmv, dnv, lmnv_raw, av;
   float4 th4[ALEN];
   float dth[ALEN];   // PRO: dt of the angle thread's tokens
-  float4 pbv;        // PRO: 4 of the head's bias values (B's [R][N] then C's)
+  float4 pbv;        // PRO: 4 of the head's bias values (B's [R][N] then C's);
+                     // GATE: 4 of the head's gate weights (w_y's [R][P] then w_z's)
   Raw8<T> craw[NK];
   struct Ck { int c, bh, h, nt; size_t tok0; };
   Ck ck{0, 0, 0, 0, 0};
@@ -296,6 +303,13 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       pbv = add4(buf_load_f32x4(rBb, tid < kPb4 ? (uint32_t)tid * 16 : kOff),
                  buf_load_f32x4(rCb, tid >= kPb4 && tid < 2 * kPb4 ? (uint32_t)(tid - kPb4) * 16 : kOff));
     }
+    if constexpr (GATE) {   // the head's w_y then w_z [R][P], one float4 per thread
+      constexpr int kGw4 = R * P / 4;
+      const Rsrc rWy = buf_rsrc(p->wy ? p->wy + (size_t)k.h * R * P : nullptr, (p->wy && nt > 0) ? R * P * 4 : 0);
+      const Rsrc rWz = buf_rsrc(p->wz ? p->wz + (size_t)k.h * R * P : nullptr, (p->wz && nt > 0) ? R * P * 4 : 0);
+      pbv = add4(buf_load_f32x4(rWy, tid < kGw4 ? (uint32_t)tid * 16 : kOff),
+                 buf_load_f32x4(rWz, tid >= kGw4 && tid < 2 * kGw4 ? (uint32_t)(tid - kGw4) * 16 : kOff));
+    }
   };
   auto c_load = [&](const Ck& k) {
     const Rsrc rC = buf_rsrc(static_cast<const T*>(p->C) + k.tok0 * R * N, k.nt > 0 ? (uint32_t)(k.nt - 1) * rsB + R * N * 2 : 0);
@@ -368,6 +382,9 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
       s_misc[3] = 0;   // wave counter: map published
       s_misc[4] = 0;   // wave counter: state published
       nextw = atomicAdd(p->ctl, 1ull);
+    }
+    if constexpr (GATE) {
+      if (tid < R * P / 2) *reinterpret_cast<float4*>(s_pb + 4 * tid) = pbv;
     }
     if constexpr (PRO) {
       if (tid < R * N / 2) *reinterpret_cast<float4*>(s_pb + 4 * tid) = pbv;
@@ -894,6 +911,19 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
     }
     __syncthreads();   // S_in^T complete in LDS
 
+    // GATE: the gate input of this lane's tokens (TPt columns each), in flight
+    // through the inter-chunk readout
+    constexpr int kRG = R < 4 ? R : 4;   // a lane's 4 output rows: 4 / kRG tokens
+    uint2 zr[4 / kRG];
+    if constexpr (GATE) {
+#pragma unroll
+      for (int q = 0; q < 4 / kRG; ++q) {
+        const int row0 = tile * 16 + 4 * g4 + q * kRG;
+        zr[q] = make_uint2(0u, 0u);
+        if (vk && p->z && row0 < rows)
+          zr[q] = *reinterpret_cast<const uint2*>(static_cast<const T*>(p->z) + (tok0 + (size_t)(row0 >> LOGR) * tstride) * P + TPt * l16);
+      }
+    }
     // ---- inter-chunk term exp(l_t) C~_t^T S_in, added to the intra term; y ----
     if (vk) {
       float e4[4];
@@ -925,7 +955,7 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
     // before a flag covers every load in flight): in flight during the y
     // stores and the next chunk's start
     c_load(nck);
-    if (vk) {
+    if (vk && !GATE) {
       T* Yg = static_cast<T*>(p->y) + tok0 * R * P;
       const size_t rowstepX = tstride * R * P;
 #pragma unroll
@@ -936,6 +966,51 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
 #pragma unroll
           for (int pn = 0; pn < TPt; ++pn) v[pn] = chain_ok ? yacc[pn][e] : nanv;
           store_row<T, TPt>(Yg + (row >> LOGR) * rowstepX + (row & (R - 1)) * P + TPt * l16, v);
+        }
+      }
+    } else if (vk) {
+      // gated readout: a lane's 4 rows are whole tokens' ranks (RG rows per
+      // token, R <= 4); it holds head columns TPt*l16 .. TPt*l16+TPt-1 (P = 64:
+      // 4 columns, one 8-byte run of the token's gate input, loaded after the
+      // block loop).  The head's w_y and w_z wait in LDS (loaded one chunk
+      // ahead)
+      const size_t rowstepO = tstride * P;
+      T* Og = static_cast<T*>(p->out) + tok0 * P;
+      const T* Zg = p->z ? static_cast<const T*>(p->z) + tok0 * P : nullptr;
+      const float* wyh = p->wy ? s_pb + TPt * l16 : nullptr;           // the head's w_y, w_z in LDS
+      const float* wzh = p->wz ? s_pb + R * P + TPt * l16 : nullptr;
+      constexpr int RG = R < 4 ? R : 4;
+#pragma unroll
+      for (int q = 0; q < 4; q += RG) {
+        const int row0 = tile * 16 + 4 * g4 + q;
+        const bool valid = row0 < rows;
+        const int tk = row0 >> LOGR;
+        float zv[TPt], o[TPt];
+        const uint2 zw = zr[q / RG];
+        zv[0] = __uint_as_float(zw.x << 16);
+        zv[1] = __uint_as_float(zw.x & 0xffff0000u);
+        zv[2] = __uint_as_float(zw.y << 16);
+        zv[3] = __uint_as_float(zw.y & 0xffff0000u);
+#pragma unroll
+        for (int pn = 0; pn < TPt; ++pn) o[pn] = 0.f;
+#pragma unroll
+        for (int j = q; j < q + RG; ++j) {
+          const int r = (row0 + j - q) & (R - 1);
+#pragma unroll
+          for (int pn = 0; pn < TPt; ++pn) {
+            float v = yacc[pn][j];
+            if (wyh) v *= wyh[r * P + pn];
+            if (Zg) {
+              const float gz = (wzh ? wzh[r * P + pn] : 1.f) * zv[pn];
+              v *= gz * __builtin_amdgcn_rcpf(1.f + __expf(-gz));   // silu (1-ulp reciprocal)
+            }
+            o[pn] += v;
+          }
+        }
+        if (valid) {
+#pragma unroll
+          for (int pn = 0; pn < TPt; ++pn) o[pn] = chain_ok ? o[pn] : nanv;
+          store_row<T, TPt>(Og + tk * rowstepO + TPt * l16, o);
         }
       }
     }
@@ -957,10 +1032,10 @@ __global__ __launch_bounds__(kThreads, 4) void stream_kernel(FusedParams p_in) {
   }
 }
 
-template <int N, int P, int R, int NBK, int PRE, bool MAPS, bool PRO>
+template <int N, int P, int R, int NBK, int PRE, bool MAPS, bool PRO, bool GATE>
 hipError_t launch_v(const FusedParams& p, size_t grid, bool late, hipStream_t stream) {
-  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P, PRO).total;
-  const void* fn = reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, MAPS, PRO>);
+  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P, PRO, GATE).total;
+  const void* fn = reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, MAPS, PRO, GATE>);
   static std::atomic<int> scratch_state{0};   // 0 unknown, 1 none, 2 uses scratch
   int st = scratch_state.load(std::memory_order_relaxed);
   if (st == 0) {
@@ -981,13 +1056,13 @@ hipError_t launch_v(const FusedParams& p, size_t grid, bool late, hipStream_t st
   FusedParams q = p;
   q.use_maps = MAPS ? 1 : 0;
   q.late_flag = late ? 1 : 0;
-  hipLaunchKernelGGL((stream_kernel<N, P, R, NBK, PRE, MAPS, PRO>), dim3((unsigned)grid), dim3(kThreads), lds, stream, q);
+  hipLaunchKernelGGL((stream_kernel<N, P, R, NBK, PRE, MAPS, PRO, GATE>), dim3((unsigned)grid), dim3(kThreads), lds, stream, q);
   return hipGetLastError();
 }
 
-template <int N, int P, int R, int NBK, int PRE, bool PRO>
+template <int N, int P, int R, int NBK, int PRE, bool PRO, bool GATE>
 hipError_t launch(const FusedParams& p, hipStream_t stream) {
-  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P, PRO).total;
+  constexpr size_t lds = lds_of(NBK * 32 / R, R, N, P, PRO, GATE).total;
   // resident workgroups per device (cached): the persistent grid (both map
   // modes have the same launch bounds and LDS)
   int dev = 0;
@@ -998,7 +1073,7 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, true, PRO>), kThreads, lds) != hipSuccess)
+            &per, reinterpret_cast<const void*>(stream_kernel<N, P, R, NBK, PRE, true, PRO, GATE>), kThreads, lds) != hipSuccess)
       return hipErrorInvalidValue;
     resident = cus * per;
     if (resident <= 0) return hipErrorInvalidValue;
@@ -1013,13 +1088,13 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
   // ~1 us more per chunk.  Measured on 65,536-token sequences (N = 128, R = 4,
   // 256 resident workgroups): 8 in flight, states only 4% faster; 16 and 32,
   // maps 1.5 and 2.2 times faster.
-  if ((size_t)resident > 8 * (size_t)p.batch * p.H) return launch_v<N, P, R, NBK, PRE, true, PRO>(p, grid, false, stream);
+  if ((size_t)resident > 8 * (size_t)p.batch * p.H) return launch_v<N, P, R, NBK, PRE, true, PRO, GATE>(p, grid, false, stream);
   // States only.  With at most 4 chunks of a sequence in flight the hand-off
   // chain (~2.5 us a link) stays well inside the time a workgroup spends on its
   // chunks, so a chunk's state flag waits for the end of its readout, and the
   // state stores complete meanwhile instead of holding up the whole workgroup.
   const bool late = (size_t)resident <= 4 * (size_t)p.batch * p.H;
-  return launch_v<N, P, R, NBK, PRE, false, PRO>(p, grid, late, stream);
+  return launch_v<N, P, R, NBK, PRE, false, PRO, GATE>(p, grid, late, stream);
 }
 
 }  // namespace stream
@@ -1028,7 +1103,7 @@ hipError_t launch(const FusedParams& p, hipStream_t stream) {
 // N = 64 with R = 1, 2 or 4 at 128 or 256 (token, rank) rows per chunk; N = 128
 // at 128 rows (R = 1, 2, 4) or 256 rows (R = 4): the chunks whose LDS fits.
 bool stream_supported(int dtype, int N, int P, int R, int Q, int gated, int pro) {
-  if (dtype != M3_BF16 || P != 64 || (N != 64 && N != 128) || gated) return false;
+  if (dtype != M3_BF16 || P != 64 || (N != 64 && N != 128) || (gated && pro)) return false;
   if (R != 1 && R != 2 && R != 4) return false;
   if (Q * R != 128 && Q * R != 256) return false;
   return Q * (N / 2) <= kFusedAngleCap && stream::lds_of(Q, R, N, P, pro != 0).total <= (size_t)kLdsBudget;
@@ -1037,24 +1112,24 @@ bool stream_supported(int dtype, int N, int P, int R, int Q, int gated, int pro)
 size_t stream_lds_bytes(int Q, int R, int N, int P) { return stream::lds_of(Q, R, N, P).total; }
 size_t stream_lds_bytes_pro(int Q, int R, int N, int P) { return stream::lds_of(Q, R, N, P, true).total; }
 
-template <bool PRO>
+template <bool PRO, bool GATE>
 hipError_t launch_stream_pro(const FusedParams& p, hipStream_t s) {
   const int rows = p.Q * p.R;
 #define M3_STREAM_R(NN, NBK, PRE)                                        \
   switch (p.R) {                                                         \
-    case 1: return stream::launch<NN, 64, 1, NBK, PRE, PRO>(p, s);       \
-    case 2: return stream::launch<NN, 64, 2, NBK, PRE, PRO>(p, s);       \
-    case 4: return stream::launch<NN, 64, 4, NBK, PRE, PRO>(p, s);       \
+    case 1: return stream::launch<NN, 64, 1, NBK, PRE, PRO, GATE>(p, s); \
+    case 2: return stream::launch<NN, 64, 2, NBK, PRE, PRO, GATE>(p, s); \
+    case 4: return stream::launch<NN, 64, 4, NBK, PRE, PRO, GATE>(p, s); \
     default: return hipErrorInvalidValue;                                \
   }
   if (p.P != 64) return hipErrorInvalidValue;
   if (p.N == 128) {
     // (128 tokens at R = 2, 256 rows, do not fit: the cos/sin table of 128
     // tokens, the ring and the C~ fragments of 256 rows need ~164 KB of LDS)
-    if (rows == 256 && p.R == 4) return stream::launch<128, 64, 4, 8, 4, PRO>(p, s);
-    if (rows == 128 && p.R == 1) return stream::launch<128, 64, 1, 4, 2, PRO>(p, s);
-    if (rows == 128 && p.R == 2) return stream::launch<128, 64, 2, 4, 2, PRO>(p, s);
-    if (rows == 128 && p.R == 4) return stream::launch<128, 64, 4, 4, 2, PRO>(p, s);
+    if (rows == 256 && p.R == 4) return stream::launch<128, 64, 4, 8, 4, PRO, GATE>(p, s);
+    if (rows == 128 && p.R == 1) return stream::launch<128, 64, 1, 4, 2, PRO, GATE>(p, s);
+    if (rows == 128 && p.R == 2) return stream::launch<128, 64, 2, 4, 2, PRO, GATE>(p, s);
+    if (rows == 128 && p.R == 4) return stream::launch<128, 64, 4, 4, 2, PRO, GATE>(p, s);
     return hipErrorInvalidValue;
   } else if (p.N == 64) {
     if (rows == 256) { M3_STREAM_R(64, 8, 4) }
@@ -1065,7 +1140,9 @@ hipError_t launch_stream_pro(const FusedParams& p, hipStream_t s) {
 }
 
 hipError_t launch_stream_prefill(const FusedParams& p, hipStream_t s) {
-  return p.pro ? launch_stream_pro<true>(p, s) : launch_stream_pro<false>(p, s);
+  if (p.pro && p.out) return hipErrorInvalidValue;   // (no entry point fuses both)
+  if (p.out) return launch_stream_pro<false, true>(p, s);
+  return p.pro ? launch_stream_pro<true, false>(p, s) : launch_stream_pro<false, false>(p, s);
 }
 
 }  // namespace m3

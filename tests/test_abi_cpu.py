@@ -278,20 +278,20 @@ def _scratch_variants():
 
 
 def _stream_scratch_variants():
-    """Streaming prefill variants (N, P, R, 32-row blocks, prologue) the build's
-    compiler report gives scratch memory (either map mode)."""
+    """Streaming prefill variants (N, P, R, 32-row blocks, prologue, gated) the
+    build's compiler report gives scratch memory (either map mode)."""
     import json
     import re
     path = os.path.join(os.path.dirname(m3.LIB_PATH), "..", "_build", "kernel_usage.json")
     if not os.path.exists(path):
         pytest.skip("no kernel usage report (build the library first)")
-    pat = re.compile(r"stream_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E")
+    pat = re.compile(r"stream_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])ELb([01])E")
     out = set()
     for name, u in json.load(open(path)).items():
         m = pat.search(name)
         if m and u.get("scratch", 0) > 0:
-            n, p, r, nbk, _pre, _maps, pro = map(int, m.groups())
-            out.add((n, p, r, nbk, pro))
+            n, p, r, nbk, _pre, _maps, pro, gate = map(int, m.groups())
+            out.add((n, p, r, nbk, pro, gate))
     return out
 
 
@@ -321,12 +321,12 @@ def test_prefill_refuses_scratch_variants(lib):
                                 # the plain prefill streams, the prologue is fused into the
                                 # streaming kernel (its own spill-free variants, checked below)
                                 staged = pro and m3.prefill_prologue_mode(s) == m3.M3_PROLOGUE_STAGED
-                                streamed = (pro and not staged and m3.prefill_kernel_used(s) == m3.M3_KERNEL_STREAM
-                                            and q == m3.prefill_chunk_used(s))
-                                if streamed:
-                                    assert (N, P, R, q * R // 32, 1) not in stream_spills
-                                elif not g and not pro and m3.prefill_kernel_used(s) == m3.M3_KERNEL_STREAM:
-                                    assert (N, P, R, q * R // 32, 0) not in stream_spills
+                                kern = (m3.prefill_prologue_kernel_used(s) if pro else
+                                        m3.prefill_gated_kernel_used(s) if g else m3.prefill_kernel_used(s))
+                                if kern == m3.M3_KERNEL_STREAM and not staged:
+                                    assert (N, P, R, q * R // 32, pro, g) not in stream_spills
+                                elif kern == m3.M3_KERNEL_STREAM:   # staged: the plain streaming variant
+                                    assert (N, P, R, q * R // 32, 0, 0) not in stream_spills
                                 else:
                                     assert (code, N, P, R, _row_tiles(q, R, N), g, 0 if staged else pro) not in spills
                                 if pro:
@@ -458,15 +458,15 @@ def test_stream_kernels_use_no_scratch(lib):
         pytest.skip("no kernel usage report (build the library first)")
     import re
     usage = json.load(open(path))
-    pat = re.compile(r"stream_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E")
+    pat = re.compile(r"stream_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])ELb([01])E")
     stream = {tuple(map(int, m.groups())): u for n, u in usage.items() for m in [pat.search(n)] if m}
-    assert len(stream) == 40, sorted(stream)   # 10 shapes x 2 map modes x with and without the prologue
-    plain = {k: u for k, u in stream.items() if k[6] == 0}
+    assert len(stream) == 60, sorted(stream)   # 10 shapes x 2 map modes x plain / prologue / gated
+    plain = {k: u for k, u in stream.items() if k[6] == 0}   # plain and gated
     assert all(u.get("scratch", 0) == 0 for u in plain.values()), {k: u for k, u in plain.items() if u.get("scratch")}
     # with the prologue fused: the MIMO / long variant (N = 128, R = 4, 8 blocks) is scratch-free; any variant
     # that is not is refused on the host (its shapes take the per-chunk kernel's prologue or the staged one)
-    assert all(stream[(128, 64, 4, 8, 4, maps, 1)].get("scratch", 0) == 0 for maps in (0, 1))
-    for (n, p, r, nbk, _pre, _maps, pro), u in stream.items():
+    assert all(stream[(128, 64, 4, 8, 4, maps, 1, 0)].get("scratch", 0) == 0 for maps in (0, 1))
+    for (n, p, r, nbk, _pre, _maps, pro, _gate), u in stream.items():
         if pro and u.get("scratch", 0) > 0:
             q = nbk * 32 // r
             shape = m3.make_shape(1, 4 * q, 2, p, n, r, q, m3.M3_BF16)

@@ -46,6 +46,10 @@ CASES = [
     ("mimo", dict(batch=1, seqlen=150, nheads=2), 32, False, True),          # rank contraction only
     ("mimo", dict(batch=1, seqlen=97, nheads=2), 64, True, False),           # gate, unit weights
     ("mimo", dict(batch=1, seqlen=70, nheads=2, rank=2, dstate=64), 64, True, True),
+    # N = 128: the streaming kernel with the gated output stage (R = 4, 2, 1)
+    ("mimo", dict(batch=2, seqlen=300, nheads=3), 64, True, True),
+    ("mimo", dict(batch=1, seqlen=300, nheads=2, rank=2), 64, True, True),
+    ("mimo", dict(batch=1, seqlen=260, nheads=2, rank=1), 128, True, False),
     ("mimo", dict(batch=1, seqlen=90, nheads=2, rank=8, dstate=64), 16, True, True),
     ("mimo", dict(batch=1, seqlen=90, nheads=1, rank=8, headdim=128, dstate=64), 16, True, True),
     ("tiny", dict(batch=1, seqlen=100, nheads=2, rank=4, headdim=32, dstate=32), 32, True, True),   # fp32
@@ -75,12 +79,14 @@ def test_prefill_gated(case):
     check_blocks(to64(out), ref, tol, (1, 3), "gated out", elem_axes=(3,),
                  elem_scale=gate_scale(yref, _np(z), _np(wy), _np(wz), block_axes=(1, 3, 4)))
     check_blocks(to64(h), href, tol, (2, 3), "h_out")
-    # the state path is the ungated call's on the same (per-chunk) kernel,
-    # equal up to rounding: with few sequences a chunk may compose its
-    # predecessors' maps, an order of the products that depends on timing.  (The
-    # library's own choice for an ungated call may be the streaming kernel,
-    # whose products run in another order.)
-    m3.debug_set_prefill_kernel(m3.M3_KERNEL_PER_CHUNK)
+    # the state path is the ungated call's on the same kernel (the streaming
+    # or the per-chunk one, whose products run in different orders), equal up
+    # to rounding: with few sequences a chunk may compose its predecessors'
+    # maps, an order of the products that depends on timing
+    code = m3.M3_BF16 if w.dtype == "bf16" else m3.M3_FP32
+    kern = m3.prefill_gated_kernel_used(m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank,
+                                                      chunk, code))
+    m3.debug_set_prefill_kernel(kern)
     try:
         _, h2 = m3.scan_prefill(**{k: dg[k] for k in KEYS}, **cg, chunk=chunk)
         torch.cuda.synchronize()
@@ -145,3 +151,34 @@ def test_gated_prefill_then_decode_continues():
     check_blocks(to64(torch.cat(outs, dim=1)), ref, TOL[w.dtype], (1, 3), "gated out", elem_axes=(3,),
                  elem_scale=gate_scale(yref, _np(z), _np(wy), _np(wz), block_axes=(1, 3, 4)))
     assert np.isfinite(to64(h)).all()
+
+
+@pytest.mark.parametrize("name,kw", [("mimo", {}), ("long", dict(seqlen=8192, nheads=2))],
+                         ids=["mimo-full-size", "long-8192-chain"])
+def test_prefill_gated_stream(name, kw):
+    """The gated readout in the streaming kernel's output stage: the MIMO
+    workload at full size (4 x 4,096 tokens x 32 heads, states only), two heads
+    compared with the oracle; and 8,192 tokens of two heads at the long shape
+    (maps in use), every head compared."""
+    w = inputs.workload(name, **kw)
+    shape = m3.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 64, m3.M3_BF16)
+    assert m3.prefill_gated_kernel_used(shape) == m3.M3_KERNEL_STREAM
+    d = inputs.make_prefill_inputs(w, seed=901)
+    c = inputs.random_carry(w, seed=902)
+    z, wy, wz = _gate_inputs(w, 903, (w.batch, w.seqlen), True, True)
+    dg, cg = dev_inputs(d), dev_inputs(c)
+    note(f"prefill gated stream {name} {kw}")
+    out, h = m3.scan_prefill_gated(**{k: dg[k] for k in KEYS}, **cg, z=z.cuda(), w_y=wy.cuda(), w_z=wz.cuda(),
+                                   chunk=64)
+    torch.cuda.synchronize()
+    heads = [0, w.nheads - 1]
+    sub = lambda t: None if t is None else t[:, :, heads]
+    d2 = {k: (v[heads] if k == "A" else sub(v)) for k, v in d.items()}
+    c2 = {k: v[:, heads] for k, v in c.items()}
+    yref, href = oracle.scan(**oracle_inputs({**d2, **c2}))
+    zn, wyn, wzn = _np(z[:, :, heads]), _np(wy[heads]), _np(wz[heads])
+    ref = oracle.gated_readout(yref, zn, wyn, wzn)
+    tol = TOL[w.dtype]
+    check_blocks(to64(out[:, :, heads]), ref, tol, (1, 3), "gated out", elem_axes=(3,),
+                 elem_scale=gate_scale(yref, zn, wyn, wzn, block_axes=(1, 3, 4)))
+    check_blocks(to64(h[:, heads]), href, tol, (2, 3), "h_out")
