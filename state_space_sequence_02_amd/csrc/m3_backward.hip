@@ -104,6 +104,22 @@ __device__ __forceinline__ Seg segment_of(const BackwardParams& p) {
   return g;
 }
 
+// Copies the rows of tokens s0..s1 of one (sequence, head) -- `width`
+// elements of T per token, at global token index tok0 + t * H -- into LDS
+// [s1 - s0 + 1][width], in 16-byte pieces spread over the block's NT threads.
+// Every load is issued before any is used, so a segment's token loop pays one
+// memory latency instead of one per token.
+template <typename T, int NT>
+__device__ __forceinline__ void stage_rows(T* dst, const T* src, size_t tok0, int H, int s0, int s1, int width) {
+  const int cpr = width * (int)sizeof(T) / 16;   // pieces per row
+  const int n = (s1 - s0 + 1) * cpr;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const int t = i / cpr, c = i - t * cpr;
+    reinterpret_cast<uint4*>(dst + (size_t)t * width)[c] =
+        reinterpret_cast<const uint4*>(src + (tok0 + (size_t)(s0 + t) * H) * width)[c];
+  }
+}
+
 // The write of the token before s0 (B_prev / x_prev, or zeros, before token 0)
 // for the unit's pair k and quad q.
 template <typename T, int N, int P, int R>
@@ -146,10 +162,23 @@ template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(bwd_threads(N, P)) void fwd_maps_kernel(BackwardParams p) {
   constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
   constexpr int UPT = (UNITS + NT - 1) / NT;
+  constexpr int SM = backward_segment(R, N, P);   // tokens per segment (p.S)
+  __shared__ __align__(16) T sB[SM * R * N];
+  __shared__ __align__(16) T sX[SM * R * P];
+  __shared__ __align__(16) float sTh[SM * (N / 2)];
+  __shared__ float sD[SM], sL[SM];
   const Seg g = segment_of(p);
   const int tid = threadIdx.x, q = tid % QP;
   const size_t tok0 = (size_t)g.b * p.L * p.H + g.h;
   const float Ah = p.A[g.h];
+  // the segment's operands, all loads in flight at once
+  stage_rows<T, NT>(sB, static_cast<const T*>(p.B), tok0, p.H, g.s0, g.s1, R * N);
+  stage_rows<T, NT>(sX, static_cast<const T*>(p.x), tok0, p.H, g.s0, g.s1, R * P);
+  if (p.theta) stage_rows<float, NT>(sTh, p.theta, tok0, p.H, g.s0, g.s1, N / 2);
+  if (tid <= g.s1 - g.s0) {
+    sD[tid] = p.dt[tok0 + (size_t)(g.s0 + tid) * p.H];
+    sL[tid] = p.lam[tok0 + (size_t)(g.s0 + tid) * p.H];
+  }
   float4 H0[UPT], H1[UPT], V0[UPT], V1[UPT];
   float zr[UPT], zi[UPT];
 #pragma unroll
@@ -160,12 +189,13 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void fwd_maps_kernel(BackwardPar
     zr[i] = 1.f;
     zi[i] = 0.f;
   }
+  __syncthreads();
   for (int t = g.s0; t <= g.s1; ++t) {
-    const size_t tok = tok0 + (size_t)t * p.H;
-    const float d = p.dt[tok], lm = p.lam[tok];
+    const int lt = t - g.s0;
+    const float d = sD[lt], lm = sL[lt];
     const float al = __expf(d * Ah), be = (1.f - lm) * d * al, ga = lm * d;
-    const T* Bt = static_cast<const T*>(p.B) + tok * R * N;
-    const T* Xt = static_cast<const T*>(p.x) + tok * R * P;
+    const T* Bt = sB + lt * R * N;
+    const T* Xt = sX + lt * R * P;
     float4 xq[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) xq[r] = ld4(Xt + r * P + 4 * q);
@@ -175,7 +205,7 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void fwd_maps_kernel(BackwardPar
       if (u >= UNITS) continue;
       const int k = u / QP;
       float c = 1.f, sn = 0.f;
-      if (p.theta) __sincosf(p.theta[tok * (N / 2) + k], &sn, &c);
+      if (p.theta) __sincosf(sTh[lt * (N / 2) + k], &sn, &c);
       fwd_step<T, N, P, R>(Bt, xq, k, al, be, ga, c, sn, H0[i], H1[i], V0[i], V1[i]);
       const float r0 = zr[i];
       zr[i] = al * (r0 * c - zi[i] * sn);
@@ -197,30 +227,52 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void fwd_maps_kernel(BackwardPar
 
 // 2. The state entering each segment, segment by segment:
 //   S_{-1} = h0 (or 0),  entering_j = S_{j-1},  S_j = z_j S_{j-1} + U_j.
+// One thread per unit (a (b, h)'s units spread over kCombSlices(N, P)
+// workgroups), the next kCombAhead segments' z and U in flight in registers:
+// the chain's only wait is on the arithmetic, not on a load per segment.
+constexpr int kCombAhead = 4;
+template <int N, int P>
+constexpr int comb_slices() { return (bwd_units(N, P) + bwd_threads(N, P) - 1) / bwd_threads(N, P); }
+
 template <int N, int P>
 __global__ __launch_bounds__(bwd_threads(N, P)) void fwd_combine_kernel(BackwardParams p) {
-  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
-  constexpr int UPT = (UNITS + NT - 1) / NT;
-  const int bh = blockIdx.x, tid = threadIdx.x, q = tid % QP;
+  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P), SL = comb_slices<N, P>();
+  constexpr int D = kCombAhead;
+  const int bh = blockIdx.x / SL, u = (blockIdx.x % SL) * NT + threadIdx.x, q = threadIdx.x % QP;
+  if (u >= UNITS) return;
+  const int k = u / QP;
+  const size_t r0 = (size_t)(2 * k) * P + 4 * q;
+  const int ns = p.nseg;
+  auto zof = [&](int j) { return *reinterpret_cast<const float2*>(p.zf + (((size_t)bh * ns + j) * (N / 2) + k) * 2); };
+  auto uof = [&](int j) { return p.sega + ((size_t)bh * ns + j) * N * P + r0; };
+  float2 zq[D];
+  float4 u0[D], u1[D];
 #pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + i * NT;
-    if (u >= UNITS) continue;
-    const int k = u / QP;
-    const size_t r0 = (size_t)(2 * k) * P + 4 * q;
-    float4 S0 = p.h0 ? ld4(p.h0 + (size_t)bh * N * P + r0) : f4(0.f);
-    float4 S1 = p.h0 ? ld4(p.h0 + (size_t)bh * N * P + r0 + P) : f4(0.f);
-    for (int j = 0; j < p.nseg; ++j) {
-      const size_t slot = (size_t)bh * p.nseg + j;
-      float* e = p.segb + slot * N * P + r0;
+  for (int d = 0; d < D; ++d)
+    if (d < ns - 1) {
+      zq[d] = zof(d);
+      u0[d] = ld4(uof(d));
+      u1[d] = ld4(uof(d) + P);
+    }
+  float4 S0 = p.h0 ? ld4(p.h0 + (size_t)bh * N * P + r0) : f4(0.f);
+  float4 S1 = p.h0 ? ld4(p.h0 + (size_t)bh * N * P + r0 + P) : f4(0.f);
+  for (int j0 = 0; j0 < ns; j0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int j = j0 + d;
+      if (j >= ns) break;
+      float* e = p.segb + ((size_t)bh * ns + j) * N * P + r0;
       *reinterpret_cast<float4*>(e) = S0;
       *reinterpret_cast<float4*>(e + P) = S1;
-      if (j + 1 < p.nseg) {
-        const float2 z = *reinterpret_cast<const float2*>(p.zf + (slot * (N / 2) + k) * 2);
-        const float* U = p.sega + slot * N * P + r0;
-        rot(z.x, z.y, S0, S1);
-        S0 = addv(S0, ld4(U));
-        S1 = addv(S1, ld4(U + P));
+      if (j + 1 < ns) {   // segment j's map (in slot d), then slot d takes segment j + D
+        rot(zq[d].x, zq[d].y, S0, S1);
+        S0 = addv(S0, u0[d]);
+        S1 = addv(S1, u1[d]);
+        if (j + D < ns - 1) {
+          zq[d] = zof(j + D);
+          u0[d] = ld4(uof(j + D));
+          u1[d] = ld4(uof(j + D) + P);
+        }
       }
     }
   }
@@ -233,11 +285,21 @@ template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(bwd_threads(N, P)) void bwd_maps_kernel(BackwardParams p) {
   constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
   constexpr int UPT = (UNITS + NT - 1) / NT;
+  constexpr int SM = backward_segment(R, N, P);   // tokens per segment (p.S)
+  __shared__ __align__(16) T sC[SM * R * N];
+  __shared__ __align__(16) T sY[SM * R * P];
+  __shared__ __align__(16) float sTh[SM * (N / 2)];
+  __shared__ float sD[SM];
   const Seg g = segment_of(p);
   const int tid = threadIdx.x, q = tid % QP;
   const size_t tok0 = (size_t)g.b * p.L * p.H + g.h;
   const float Ah = p.A[g.h];
   const bool last = g.j == p.nseg - 1;
+  // the segment's operands, all loads in flight at once
+  stage_rows<T, NT>(sC, static_cast<const T*>(p.C), tok0, p.H, g.s0, g.s1, R * N);
+  stage_rows<T, NT>(sY, static_cast<const T*>(p.dy), tok0, p.H, g.s0, g.s1, R * P);
+  if (p.theta) stage_rows<float, NT>(sTh, p.theta, tok0, p.H, g.s0, g.s1, N / 2);
+  if (tid <= g.s1 - g.s0) sD[tid] = p.dt[tok0 + (size_t)(g.s0 + tid) * p.H];
   float4 G0[UPT], G1[UPT];
   float wr[UPT], wi[UPT];
   // coefficients of the token after the segment (none after the last token)
@@ -260,14 +322,15 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void bwd_maps_kernel(BackwardPar
     wr[i] = 1.f;
     wi[i] = 0.f;
   }
+  __syncthreads();
   for (int t = g.s1; t >= g.s0; --t) {
-    const size_t tok = tok0 + (size_t)t * p.H;
-    const T* Ct = static_cast<const T*>(p.C) + tok * R * N;
-    const T* dYt = static_cast<const T*>(p.dy) + tok * R * P;
+    const int lt = t - g.s0;
+    const T* Ct = sC + lt * R * N;
+    const T* dYt = sY + lt * R * P;
     float4 dyq[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) dyq[r] = ld4(dYt + r * P + 4 * q);
-    const float al = __expf(p.dt[tok] * Ah);
+    const float al = __expf(sD[lt] * Ah);
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
@@ -287,7 +350,7 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void bwd_maps_kernel(BackwardPar
       wr[i] = a_n * (r0 * cn[i] + wi[i] * sn[i]);
       wi[i] = a_n * (wi[i] * cn[i] - r0 * sn[i]);
       float c = 1.f, s = 0.f;
-      if (p.theta) __sincosf(p.theta[tok * (N / 2) + k], &s, &c);
+      if (p.theta) __sincosf(sTh[lt * (N / 2) + k], &s, &c);
       cn[i] = c;
       sn[i] = s;
     }
@@ -307,30 +370,45 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void bwd_maps_kernel(BackwardPar
 }
 
 // 5. The G entering each segment from the right, last segment first:
-//   E_last = 0,  E_{j-1} = G~_j + w_j E_j.
+//   E_last = 0,  E_{j-1} = G~_j + w_j E_j.  (Spread and prefetched as step 2.)
 template <int N, int P>
 __global__ __launch_bounds__(bwd_threads(N, P)) void bwd_combine_kernel(BackwardParams p) {
-  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P);
-  constexpr int UPT = (UNITS + NT - 1) / NT;
-  const int bh = blockIdx.x, tid = threadIdx.x, q = tid % QP;
+  constexpr int NT = bwd_threads(N, P), QP = P / 4, UNITS = bwd_units(N, P), SL = comb_slices<N, P>();
+  constexpr int D = kCombAhead;
+  const int bh = blockIdx.x / SL, u = (blockIdx.x % SL) * NT + threadIdx.x, q = threadIdx.x % QP;
+  if (u >= UNITS) return;
+  const int k = u / QP;
+  const size_t r0 = (size_t)(2 * k) * P + 4 * q;
+  const int ns = p.nseg;
+  auto wof = [&](int j) { return *reinterpret_cast<const float2*>(p.zb + (((size_t)bh * ns + j) * (N / 2) + k) * 2); };
+  auto gof = [&](int j) { return p.sega + ((size_t)bh * ns + j) * N * P + r0; };
+  float2 wq[D];
+  float4 g0[D], g1[D];
 #pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + i * NT;
-    if (u >= UNITS) continue;
-    const int k = u / QP;
-    const size_t r0 = (size_t)(2 * k) * P + 4 * q;
-    float4 E0 = f4(0.f), E1 = f4(0.f);
-    for (int j = p.nseg - 1; j >= 0; --j) {
-      const size_t slot = (size_t)bh * p.nseg + j;
-      float* e = p.segc + slot * N * P + r0;
+  for (int d = 0; d < D; ++d)
+    if (ns - 1 - d > 0) {   // segments ns - 1, ns - 2, ... (segment 0's map is not used)
+      wq[d] = wof(ns - 1 - d);
+      g0[d] = ld4(gof(ns - 1 - d));
+      g1[d] = ld4(gof(ns - 1 - d) + P);
+    }
+  float4 E0 = f4(0.f), E1 = f4(0.f);
+  for (int i0 = 0; i0 < ns; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int j = ns - 1 - (i0 + d);
+      if (j < 0) break;
+      float* e = p.segc + ((size_t)bh * ns + j) * N * P + r0;
       *reinterpret_cast<float4*>(e) = E0;
       *reinterpret_cast<float4*>(e + P) = E1;
-      if (j > 0) {
-        const float2 w = *reinterpret_cast<const float2*>(p.zb + (slot * (N / 2) + k) * 2);
-        const float* Gl = p.sega + slot * N * P + r0;
-        rot(w.x, w.y, E0, E1);
-        E0 = addv(E0, ld4(Gl));
-        E1 = addv(E1, ld4(Gl + P));
+      if (j > 0) {   // segment j's map (in slot d), then slot d takes segment j - D
+        rot(wq[d].x, wq[d].y, E0, E1);
+        E0 = addv(E0, g0[d]);
+        E1 = addv(E1, g1[d]);
+        if (j - D > 0) {
+          wq[d] = wof(j - D);
+          g0[d] = ld4(gof(j - D));
+          g1[d] = ld4(gof(j - D) + P);
+        }
       }
     }
   }
@@ -1056,9 +1134,9 @@ hipError_t run_backward(const BackwardParams& p, hipStream_t s) {
     flag.store(1, std::memory_order_release);
   }
   hipLaunchKernelGGL((fwd_maps_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
-  hipLaunchKernelGGL((fwd_combine_kernel<N, P>), dim3(nbh), blk, 0, s, p);
+  hipLaunchKernelGGL((fwd_combine_kernel<N, P>), dim3(nbh * comb_slices<N, P>()), blk, 0, s, p);
   hipLaunchKernelGGL((bwd_maps_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
-  hipLaunchKernelGGL((bwd_combine_kernel<N, P>), dim3(nbh), blk, 0, s, p);
+  hipLaunchKernelGGL((bwd_combine_kernel<N, P>), dim3(nbh * comb_slices<N, P>()), blk, 0, s, p);
   hipLaunchKernelGGL((chunk_grads_kernel<T, N, P, R>), dim3(nsg), dim3(kBwdThreads), lds, s, p);
   return hipGetLastError();
 }
