@@ -443,7 +443,12 @@ __global__ __launch_bounds__(bwd_threads(N, P)) void bwd_combine_kernel(Backward
 // One workgroup per (segment, sequence, head), everything in LDS as fp32; the
 // row-by-row products (C~ B~^T, dY X^T, and the five products of the gradient
 // formulas above) run as 16x16 fp32 MFMA tiles (v_mfma_f32_16x16x4_f32).
-constexpr int kBwdThreads = 256;
+// Threads of the segment kernel: 512 (two waves per SIMD beside the one
+// workgroup the LDS allows per CU, so one wave's LDS and MFMA waits overlap
+// another's: 12% faster than 256 at the SISO and MIMO shapes), except at
+// N = 128 with R = 1, 2 or 8, whose variants would then exceed the 256
+// registers a lane gets and spill; those keep 256.
+constexpr int grads_threads(int N, int R) { return (N <= 64 || R == 4) ? 512 : 256; }
 constexpr int kTok = 16;   // per-token LDS fields
 
 // 16x16 output tile of A B^T over a contraction of K (a multiple of 32):
@@ -514,8 +519,8 @@ __device__ __forceinline__ void per_token(int m0, const float (&v)[4], F add) {
 }
 
 template <typename T, int N, int P, int R>
-__global__ __launch_bounds__(kBwdThreads) void chunk_grads_kernel(BackwardParams p) {
-  constexpr int NT = kBwdThreads, NH = N / 2;
+__global__ __launch_bounds__(grads_threads(N, R)) void chunk_grads_kernel(BackwardParams p) {
+  constexpr int NT = grads_threads(N, R), NH = N / 2;
   constexpr int NS = N < 32 ? 32 : N, PS = P < 32 ? 32 : P;   // LDS row strides (contractions padded to 32)
   extern __shared__ __align__(16) float sm[];
   const Seg g = segment_of(p);
@@ -1137,7 +1142,7 @@ hipError_t run_backward(const BackwardParams& p, hipStream_t s) {
   hipLaunchKernelGGL((fwd_combine_kernel<N, P>), dim3(nbh * comb_slices<N, P>()), blk, 0, s, p);
   hipLaunchKernelGGL((bwd_maps_kernel<T, N, P, R>), dim3(nsg), blk, 0, s, p);
   hipLaunchKernelGGL((bwd_combine_kernel<N, P>), dim3(nbh * comb_slices<N, P>()), blk, 0, s, p);
-  hipLaunchKernelGGL((chunk_grads_kernel<T, N, P, R>), dim3(nsg), dim3(kBwdThreads), lds, s, p);
+  hipLaunchKernelGGL((chunk_grads_kernel<T, N, P, R>), dim3(nsg), dim3(grads_threads(N, R)), lds, s, p);
   return hipGetLastError();
 }
 
