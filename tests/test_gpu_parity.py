@@ -65,9 +65,6 @@ SMALL = [
     dict(name="mimo", kw=dict(batch=2, seqlen=97, nheads=2), chunk=64),
     dict(name="mimo", kw=dict(batch=1, seqlen=70, nheads=2, headdim=16, dstate=16, rank=8), chunk=16),
     dict(name="mimo", kw=dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=64, rank=2), chunk=32),
-    pytest.param(dict(name="mimo", kw=dict(batch=1, seqlen=64, nheads=1, headdim=64, dstate=256, rank=1), chunk=32),
-                 marks=pytest.mark.skip(reason="N=256 prefill is not built (heavy scratch spills; one unexplained "
-                                                "GPU memory fault)")),
     dict(name="long", kw=dict(seqlen=515, nheads=2), chunk=64),
     # 256 and 512 (token, rank) rows per chunk: two and four 16-row output tiles per wave
     dict(name="siso", kw=dict(batch=1, seqlen=600, nheads=2), chunk=256),
@@ -422,9 +419,11 @@ def test_workload_mimo_full_size():
 
 def test_refused_shapes_raise_before_launch():
     """Shapes the host plan refuses (512-row chunks, kernel variants that would
-    use scratch memory) raise M3_ERR_SHAPE and launch nothing."""
+    use scratch memory, N = 256, which is decode-only) raise M3_ERR_SHAPE and
+    launch nothing."""
     for name, kw, chunk in (("long", dict(seqlen=300, nheads=2), 128),
-                            ("mimo", dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=128, rank=2), 32)):
+                            ("mimo", dict(batch=1, seqlen=90, nheads=1, headdim=128, dstate=128, rank=2), 32),
+                            ("mimo", dict(batch=1, seqlen=64, nheads=1, headdim=64, dstate=256, rank=1), 32)):
         w = inputs.workload(name, **kw)
         assert taken_chunk(w, chunk) == 0
         dg = dev_inputs(inputs.make_prefill_inputs(w, seed=2))
