@@ -302,6 +302,17 @@ def _bench_prefill(w, steps, warmup, chunk, nsets, gate, prologue, reps):
                 gbs_launch=nbytes / (msl * 1e-3) / 1e9, tflops_launch=flops / (msl * 1e-3) / 1e12)
 
 
+# The paper page's Table 6 decode settings (128 sequences x 32 heads, P = 64):
+# name -> (state dtype between steps, overrides of the decode workload).
+DECODE_SETTINGS = {
+    "mimo": (torch.float32, {}),
+    "mimo_bf16_state": (torch.bfloat16, {}),
+    "mimo_n64": (torch.float32, dict(dstate=64)),
+    "siso_n128": (torch.float32, dict(rank=1)),
+    "siso_n64": (torch.float32, dict(rank=1, dstate=64)),
+}
+
+
 def bench_decode(w, steps, warmup, nstate=3, state_dtype=torch.float32, gated=False, prologue=False, reps=1):
     """One step = one m3_decode_step over all (sequence, head) pairs; >= 3 state
     buffers (384 MiB at the 128-sequence shape) rotate so a step cannot be served
@@ -479,6 +490,8 @@ def main():
                     help="headline prefill through m3_scan_prefill_prologue (raw angles, B/C biases)")
     ap.add_argument("--backward", action="store_true",
                     help="headline: the backward (m3_scan_backward, every gradient) at the prefill workload's shape")
+    ap.add_argument("--decode-setting", default="mimo", choices=sorted(DECODE_SETTINGS),
+                    help="decode workload only: which of the Table 6 decode settings is the headline")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -495,14 +508,17 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     if w.steps:
-        r = bench_decode(w, args.steps * 10, args.warmup * 10, reps=args.reps)
+        state_dtype, kw = DECODE_SETTINGS[args.decode_setting]
+        w = inputs.workload("decode", **kw)
+        r = bench_decode(w, args.steps * 10, args.warmup * 10, state_dtype=state_dtype, reps=args.reps)
         value, unit, ms = r["updates_per_s"], "state-updates/s", r["ms"]
-        traffic = measured_traffic("decode_kernel_decode")
+        traffic = measured_traffic("decode_kernel_decode" if args.decode_setting == "mimo"
+                                   else f"decode_kernel_{args.decode_setting}")
         roof = dict(bound="hbm", achieved=round(r["gbs_launch"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(r["gbs_launch"] / HBM_PEAK_GBS, 4), traffic=traffic, kernel="decode_kernel",
                     algorithmic_bytes_per_launch=r["bytes"], us_per_launch=round(r["ms_launch"] * 1e3, 2))
         config = dict(workload=f"decode: {w.batch} seq x {w.nheads} heads, N={w.dstate}, P={w.headdim}, "
-                               f"R={w.rank}, bf16 in, fp32 state",
+                               f"R={w.rank}, bf16 in, {'bf16' if state_dtype == torch.bfloat16 else 'fp32'} state",
                       batch=w.batch, nheads=w.nheads, dstate=w.dstate, headdim=w.headdim, rank=w.rank,
                       state_buffers=3)
         steps_done = args.steps * 10
@@ -573,14 +589,16 @@ def main():
                                       table2_intensity=round(table2_intensity(wd.dstate, wd.headdim, wd.rank), 2))
         # the paper page's Table 6 decode settings: SISO and MIMO, state size 64
         # or 128, fp32 or bf16 state (128 sequences x 32 heads, P=64)
-        def dec(name, state_dtype=torch.float32, **kw):
+        def dec(name, setting):
+            state_dtype, kw = DECODE_SETTINGS[setting]
             wl = inputs.workload("decode", **kw)
             rr = bench_decode(wl, 200, 30, state_dtype=state_dtype)
-            sec[name] = decode_line(wl, rr, "bf16" if state_dtype == torch.bfloat16 else "fp32")
-        dec("mimo_decode_bf16_state", torch.bfloat16)
-        dec("mimo_decode_n64", dstate=64)
-        dec("siso_decode_n128", rank=1)
-        dec("siso_decode_n64", rank=1, dstate=64)
+            sec[name] = dict(decode_line(wl, rr, "bf16" if state_dtype == torch.bfloat16 else "fp32"),
+                             traffic=measured_traffic(f"decode_kernel_{setting}"))
+        dec("mimo_decode_bf16_state", "mimo_bf16_state")
+        dec("mimo_decode_n64", "mimo_n64")
+        dec("siso_decode_n128", "siso_n128")
+        dec("siso_decode_n64", "siso_n64")
         # torch's device copy of the decode states' bytes (N=64 fp32 or N=128
         # bf16: 64 MiB; N=128 fp32: 128 MiB), read once and written once
         sec["device_copy_64MiB"] = bench_copy(64 << 20)
